@@ -1,0 +1,507 @@
+"""Seeded synthetic inputs for single-query (decode) attention over a paged KV cache.
+
+This module draws random numbers and lays them out in the cache format that the library's
+header documents: Gaussian q/K/V rounded to bf16, the FP8-E4M3FN and rotated-codebook
+*encoders* (the cache writer that runs before the decode path), the page-pool permutation,
+block tables, context lengths and window choices.
+
+It holds none of the decode arithmetic -- no gather through block tables, no dequantisation,
+no rotation of the query, no softmax.  The oracle (``oracle/``) and the GPU library each
+implement those on their own; this is the only module both sides share.
+
+Workload shapes follow the attention.rs README (page "guoqingbao/attention.rs", section
+"KV Cache Formats": BF16, FP8 E4M3, Turbo4 = 4-bit K + 4-bit V, Turbo3 = 3-bit K + 4-bit V)
+and the turboquant-rs fused attention wrapper (page "turboquant-rs 0.4.1
+src/cache/cuda/attention.rs": 512-token partitions, sign pattern, codebook, per-token scales).
+"""
+from __future__ import annotations
+
+import dataclasses
+import functools
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_SIZE = 16          # tokens per page
+FORMATS = ("bf16", "fp8", "turbo4", "turbo3")
+FORMAT_CODE = {"bf16": 0, "fp8": 1, "turbo4": 2, "turbo3": 3}
+KV_BITS = {"turbo4": (4, 4), "turbo3": (3, 4)}   # (K bits, V bits)
+
+BF16_POISON = np.uint16(0x7FC0)   # quiet NaN
+FP8_POISON = np.uint8(0x7F)       # E4M3FN NaN (S.1111.111)
+
+
+# --------------------------------------------------------------------------------------------
+# Workload specifications
+# --------------------------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Spec:
+    """Shape and recipe of one synthetic decode-attention batch."""
+    name: str
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    fmt: str
+    context: int | None = None            # every sequence has this length ...
+    ctx_range: tuple[int, int] | None = None   # ... or lengths ~ U{lo..hi} from the seed
+    window: int = 0                       # sliding-window width (0 = none)
+    window_frac: float = 0.0              # fraction of sequences that get the window
+    softcap: float = 0.0                  # tanh logit cap (0 = off)
+    softmax_scale: float | None = None    # default 1/sqrt(head_dim)
+    pool_spare: int = 1024                # spare (poisoned) pages beyond what the batch needs
+    pool_total: int | None = None         # explicit pool size (overrides pool_spare)
+    partition_size: int = 0               # 0 = auto (512, split at >= 1024 tokens)
+    seed: int = 0
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def scale(self) -> np.float32:
+        s = self.softmax_scale if self.softmax_scale is not None else 1.0 / math.sqrt(self.head_dim)
+        return np.float32(s)
+
+    @property
+    def max_context(self) -> int:
+        return self.context if self.context is not None else self.ctx_range[1]
+
+
+SPECS: dict[str, Spec] = {
+    # Tiny parity case: GQA 4:1, D=64, L=300, 19 pages placed by a permutation of a 64-page pool.
+    "c1": Spec("tiny-bf16-L300", 1, 4, 1, 64, "bf16", context=300, softmax_scale=1.0 / 8,
+               pool_total=64),
+    # Llama-3-8B-shaped decode at 4K context.
+    "c2": Spec("llama3-8b-bf16-L4096", 32, 32, 8, 128, "bf16", context=4096),
+    # Ragged long-context batch with sliding window on half the sequences and tanh softcap.
+    "c3": Spec("ragged-bf16-L1..32768-win4096-cap50", 64, 32, 8, 128, "bf16",
+               ctx_range=(1, 32768), window=4096, window_frac=0.5, softcap=50.0),
+    # FP8 E4M3 cache at 32K, GQA 8:1.
+    "c4": Spec("fp8-e4m3-L32768-gqa8", 16, 64, 8, 128, "fp8", context=32768),
+    # Rotated-codebook caches at 64K.
+    "c5-t4": Spec("turbo4-L65536", 8, 32, 8, 128, "turbo4", context=65536),
+    "c5-t3": Spec("turbo3-L65536", 8, 32, 8, 128, "turbo3", context=65536),
+    # 32K-context shapes for the other formats (the headline metric is stated at 32K).
+    "m-bf16": Spec("bf16-L32768-gqa8", 16, 64, 8, 128, "bf16", context=32768),
+    "m-t4": Spec("turbo4-L32768", 8, 32, 8, 128, "turbo4", context=32768),
+    "m-t3": Spec("turbo3-L32768", 8, 32, 8, 128, "turbo3", context=32768),
+}
+
+
+def spec(name: str, **overrides) -> Spec:
+    """A named workload, optionally with fields replaced (smaller batch, other format, ...)."""
+    return dataclasses.replace(SPECS[name], **overrides)
+
+
+# --------------------------------------------------------------------------------------------
+# Byte sizes of the paged layout (documented in include/kvdecode.h)
+# --------------------------------------------------------------------------------------------
+def k_chunk_bytes(fmt: str, d: int) -> int:
+    """Bytes of one (page, KV head) chunk of the K cache."""
+    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 6 * d}[fmt]
+
+
+def v_chunk_bytes(fmt: str, d: int) -> int:
+    """Bytes of one (page, KV head) chunk of the V cache (Turbo V is always 4-bit)."""
+    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 8 * d}[fmt]
+
+
+def kv_bytes_per_token_head(fmt: str, d: int) -> int:
+    """Algorithmic cache bytes the method must read per (token, KV head), K + V (+ norms)."""
+    norms = 8 if fmt.startswith("turbo") else 0
+    return (k_chunk_bytes(fmt, d) + v_chunk_bytes(fmt, d)) // BLOCK_SIZE + norms
+
+
+# --------------------------------------------------------------------------------------------
+# Scalar encoders (cache writer side)
+# --------------------------------------------------------------------------------------------
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_POISON
+    return out
+
+
+def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3FN codes: round to nearest even, saturate to +-448.
+
+    E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; S.1111.111 is NaN, there is no
+    infinity, the largest finite value is 1.75 * 2^8 = 448 and the smallest subnormal 2^-9.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sign = (x.view(np.uint32) >> np.uint32(24)).astype(np.uint8) & np.uint8(0x80)
+    a = np.minimum(np.abs(x), np.float32(448.0))
+    bits = a.view(np.uint32)
+    # normal range: round the 23-bit mantissa to 3 bits (ties to even); a carry bumps the exponent
+    r = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
+    normal = (r.astype(np.int64) - ((127 - 7) << 3))
+    # subnormal range (a < 2^-6): multiples of 2^-9; 8 * 2^-9 is the smallest normal, code 0x08
+    sub = np.rint(a * np.float32(512.0)).astype(np.int64)
+    code = np.where(a < np.float32(2.0 ** -6), sub, normal)
+    code = np.minimum(code, 0x7E).astype(np.uint8)
+    return code | sign
+
+
+def sign_pattern(rng: np.random.Generator, d: int) -> np.ndarray:
+    """A seeded +-1 vector (float32)."""
+    return np.where(rng.integers(0, 2, size=d) == 1, 1.0, -1.0).astype(np.float32)
+
+
+def _wht_rows(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform (Sylvester order) along the last axis, in place."""
+    d = x.shape[-1]
+    h = 1
+    lead = x.shape[:-1]
+    while h < d:
+        y = x.reshape(*lead, d // (2 * h), 2, h)
+        a = y[..., 0, :].copy()
+        b = y[..., 1, :]
+        y[..., 0, :] += b
+        y[..., 1, :] = a - b
+        h *= 2
+    return x
+
+
+@functools.lru_cache(maxsize=None)
+def lloyd_max_normal(levels: int) -> tuple[float, ...]:
+    """Lloyd-Max levels (ascending, fp64) minimising MSE for a standard normal source.
+
+    Fixed point of: boundaries are midpoints of neighbouring levels; each level is the
+    conditional mean of N(0,1) on its cell, E[X | a<X<b] = (phi(a)-phi(b)) / (Phi(b)-Phi(a)).
+    """
+    from scipy.special import ndtr
+
+    def phi(t):
+        return np.exp(-0.5 * t * t) / math.sqrt(2.0 * math.pi)
+
+    c = np.linspace(-2.5, 2.5, levels)
+    for _ in range(100000):
+        b = np.concatenate(([-np.inf], 0.5 * (c[1:] + c[:-1]), [np.inf]))
+        lo, hi = b[:-1], b[1:]
+        new = (phi(lo) - phi(hi)) / (ndtr(hi) - ndtr(lo))
+        new = 0.5 * (new - new[::-1])          # the source is symmetric; keep the levels so
+        done = np.max(np.abs(new - c)) < 4e-15
+        c = new
+        if done:
+            break
+    return tuple(float(v) for v in c)
+
+
+def codebook(levels: int, d: int) -> np.ndarray:
+    """Lloyd-Max codebook for a coordinate of a random unit vector in R^d, i.e. N(0, 1/d),
+    rounded to float32, ascending."""
+    return (np.asarray(lloyd_max_normal(levels)) / math.sqrt(d)).astype(np.float32)
+
+
+def nearest_level(u: np.ndarray, levels_f32: np.ndarray) -> np.ndarray:
+    """Index of the nearest codebook level (ties to the lower index), decided in fp64."""
+    lv = levels_f32.astype(np.float64)
+    mids = 0.5 * (lv[1:] + lv[:-1])
+    return np.searchsorted(mids, u, side="left").astype(np.uint8)
+
+
+def turbo_encode(x: np.ndarray, sign: np.ndarray, levels_f32: np.ndarray):
+    """Rotated-codebook encoder for token vectors x [..., d] (float32).
+
+    y = H_d (s * x) / sqrt(d) (orthonormal Walsh-Hadamard after a +-1 sign flip);
+    norm = ||x||_2 (fp64, rounded to fp32); u = y / norm; idx = nearest level of u.
+    Returns (idx uint8 [..., d], norm float32 [...]).
+    """
+    d = x.shape[-1]
+    xd = x.astype(np.float64)
+    y = _wht_rows(xd * sign.astype(np.float64)) / math.sqrt(d)
+    norm = np.sqrt(np.einsum("...i,...i->...", xd, xd)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = y / norm.astype(np.float64)[..., None]
+    u = np.nan_to_num(u, nan=0.0)
+    return nearest_level(u, levels_f32), norm
+
+
+# --------------------------------------------------------------------------------------------
+# Page packing (layout of one (page, KV head) chunk; see include/kvdecode.h)
+# --------------------------------------------------------------------------------------------
+def _pack_nibbles(idx: np.ndarray) -> np.ndarray:
+    """[..., 2n] 4-bit values -> [..., n] bytes, element 2i in the low nibble of byte i."""
+    idx = idx.astype(np.uint8)
+    return (idx[..., 0::2] & 0xF) | ((idx[..., 1::2] & 0xF) << 4)
+
+
+def _pack_3bit(idx: np.ndarray) -> np.ndarray:
+    """[..., 32] 3-bit values -> [..., 12] bytes; value e occupies bits [3e, 3e+3) of the
+    little-endian 96-bit word formed by the 12 bytes."""
+    v = idx.astype(np.uint64) & np.uint64(7)
+    lo = np.zeros(v.shape[:-1], dtype=np.uint64)      # bits 0..63
+    hi = np.zeros(v.shape[:-1], dtype=np.uint64)      # bits 64..95
+    for e in range(32):
+        bit = 3 * e
+        ve = v[..., e]
+        if bit + 3 <= 64:
+            lo |= ve << np.uint64(bit)
+        elif bit >= 64:
+            hi |= ve << np.uint64(bit - 64)
+        else:   # straddles bit 64
+            lo |= (ve << np.uint64(bit)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+            hi |= ve >> np.uint64(64 - bit)
+    out = np.empty(v.shape[:-1] + (12,), dtype=np.uint8)
+    for i in range(8):
+        out[..., i] = ((lo >> np.uint64(8 * i)) & np.uint64(0xFF)).astype(np.uint8)
+    for i in range(4):
+        out[..., 8 + i] = ((hi >> np.uint64(8 * i)) & np.uint64(0xFF)).astype(np.uint8)
+    return out
+
+
+def pack_k_pages(fmt: str, elems: np.ndarray) -> np.ndarray:
+    """K elements [n_pages, Hkv, 16, D] (bf16 bits / fp8 codes / codebook indices) ->
+    page chunks [n_pages, Hkv, k_chunk_bytes] (uint8)."""
+    n, h, t, d = elems.shape
+    if fmt == "bf16":      # [D/8][16][8] bf16
+        c = elems.astype(np.uint16).reshape(n, h, t, d // 8, 8).transpose(0, 1, 3, 2, 4)
+        return np.ascontiguousarray(c).view(np.uint8).reshape(n, h, -1)
+    if fmt == "fp8":       # [D/16][16][16] bytes
+        c = elems.astype(np.uint8).reshape(n, h, t, d // 16, 16).transpose(0, 1, 3, 2, 4)
+        return np.ascontiguousarray(c).reshape(n, h, -1)
+    groups = elems.reshape(n, h, t, d // 32, 32).transpose(0, 1, 3, 2, 4)   # [D/32][16][32]
+    packed = _pack_nibbles(groups) if fmt == "turbo4" else _pack_3bit(groups)
+    return np.ascontiguousarray(packed).reshape(n, h, -1)
+
+
+def pack_v_pages(fmt: str, elems: np.ndarray) -> np.ndarray:
+    """V elements [n_pages, Hkv, 16, D] -> page chunks [n_pages, Hkv, v_chunk_bytes] (uint8);
+    V is stored transposed, [D][16] per chunk (4-bit for both Turbo formats)."""
+    n, h, t, d = elems.shape
+    c = np.ascontiguousarray(elems.transpose(0, 1, 3, 2))          # [n, h, D, 16]
+    if fmt == "bf16":
+        return c.astype(np.uint16).view(np.uint8).reshape(n, h, -1)
+    if fmt == "fp8":
+        return c.astype(np.uint8).reshape(n, h, -1)
+    return np.ascontiguousarray(_pack_nibbles(c)).reshape(n, h, -1)
+
+
+# --------------------------------------------------------------------------------------------
+# Batch generation
+# --------------------------------------------------------------------------------------------
+@dataclass
+class Inputs:
+    """One synthetic batch, host-side, exactly as the C ABI consumes it."""
+    spec: Spec
+    q: np.ndarray                 # uint16 [B, Hq, D] bf16 bits
+    k_cache: np.ndarray           # uint8 [pool, Hkv, k_chunk_bytes]
+    v_cache: np.ndarray           # uint8 [pool, Hkv, v_chunk_bytes]
+    scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo: f32 [2, pool, Hkv, 16]; bf16: None
+    codebook: np.ndarray | None   # turbo: f32 [2^kbits + 16] (K levels then V levels)
+    sign: np.ndarray | None       # turbo: f32 [D] of +-1
+    block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
+    context_lens: np.ndarray      # int32 [B]
+    window: np.ndarray            # int32 [B]; 0 = no window
+    softmax_scale: np.float32
+    softcap: np.float32
+    max_context_len: int
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_pool_blocks(self) -> int:
+        return self.k_cache.shape[0]
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return self.block_table.shape[1]
+
+    def spans(self) -> np.ndarray:
+        """Attended tokens per sequence: min(L, W) if windowed, else L."""
+        L = self.context_lens.astype(np.int64)
+        W = self.window.astype(np.int64)
+        return np.where(W > 0, np.minimum(L, W), L)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic cache bytes one call must read."""
+        s = self.spec
+        return int(self.spans().sum()) * s.num_kv_heads * kv_bytes_per_token_head(s.fmt, s.head_dim)
+
+
+# Named child streams of one SeedSequence, in a fixed order.
+_STREAMS = ("q", "k", "v", "pool", "lengths", "window", "sign")
+
+
+def _rngs(seed: int) -> dict[str, np.random.Generator]:
+    kids = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    return {name: np.random.default_rng(k) for name, k in zip(_STREAMS, kids)}
+
+
+def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = False,
+                unused_fill: str = "spare", kv_override=None,
+                fp8_scale: np.ndarray | None = None, lengths: np.ndarray | None = None,
+                windows: np.ndarray | None = None) -> Inputs:
+    """Build one batch.
+
+    poison: spare pages and tail slots past each context length hold NaN (bf16 0x7FC0,
+        fp8 0x7F, Turbo norm NaN), so any read that reaches the arithmetic shows up.
+    poison_before_window: also poison pages that lie wholly before a window's start.
+    unused_fill: block-table entries past a sequence's last page -> 'spare' (a poisoned spare
+        page) or -1.
+    kv_override: callable(seq, L) -> (K [Hkv, L, D], V [Hkv, L, D]) float32 logical values,
+        replacing the Gaussian draws (identity tests).
+    fp8_scale: optional f32 [2, Hkv] replacing amax/448.
+    lengths / windows: optional explicit context lengths / window widths per sequence.
+    """
+    assert s.fmt in FORMATS and s.num_q_heads % s.num_kv_heads == 0
+    B, Hkv, D, fmt = s.num_seqs, s.num_kv_heads, s.head_dim, s.fmt
+    r = _rngs(s.seed)
+
+    # lengths and windows
+    if lengths is not None:
+        L = np.asarray(lengths, dtype=np.int32)
+    elif s.context is not None:
+        L = np.full(B, s.context, dtype=np.int32)
+    else:
+        L = r["lengths"].integers(s.ctx_range[0], s.ctx_range[1] + 1, size=B).astype(np.int32)
+    if windows is not None:
+        W = np.asarray(windows, dtype=np.int32)
+    else:
+        W = np.zeros(B, dtype=np.int32)
+        if s.window > 0 and s.window_frac > 0:
+            n_win = int(round(B * s.window_frac))
+            W[r["window"].permutation(B)[:n_win]] = s.window
+    max_ctx = max(int(L.max(initial=0)), 1) if lengths is not None else s.max_context
+    max_blocks = -(-max_ctx // BLOCK_SIZE)
+
+    # pool and block tables
+    n_pages = (-(-L.astype(np.int64) // BLOCK_SIZE))
+    need = int(n_pages.sum())
+    pool = s.pool_total if s.pool_total is not None else need + s.pool_spare
+    assert pool >= need
+    perm = r["pool"].permutation(pool).astype(np.int32)
+    spare = perm[need:]
+    bt = np.empty((B, max_blocks), dtype=np.int32)
+    cur = 0
+    for b in range(B):
+        bt[b, : n_pages[b]] = perm[cur: cur + n_pages[b]]
+        cur += n_pages[b]
+        if unused_fill == "spare" and len(spare):
+            bt[b, n_pages[b]:] = spare[b % len(spare)]
+        else:
+            bt[b, n_pages[b]:] = -1
+
+    # query
+    q = bf16_bits(r["q"].standard_normal((B, s.num_q_heads, D), dtype=np.float32))
+
+    kb, vb = k_chunk_bytes(fmt, D), v_chunk_bytes(fmt, D)
+    k_cache = np.empty((pool, Hkv, kb), dtype=np.uint8)
+    v_cache = np.empty((pool, Hkv, vb), dtype=np.uint8)
+    scales = codebook_arr = sgn = None
+    if fmt.startswith("turbo"):
+        kbits, vbits = KV_BITS[fmt]
+        cb_k, cb_v = codebook(1 << kbits, D), codebook(1 << vbits, D)
+        codebook_arr = np.concatenate([cb_k, cb_v]).astype(np.float32)
+        sgn = sign_pattern(r["sign"], D)
+        scales = np.full((2, pool, Hkv, BLOCK_SIZE), np.nan if poison else 0.0, dtype=np.float32)
+
+    # poison everything first; real pages are overwritten below
+    if poison:
+        if fmt == "bf16":
+            k_cache.view(np.uint16)[...] = BF16_POISON
+            v_cache.view(np.uint16)[...] = BF16_POISON
+        elif fmt == "fp8":
+            k_cache[...] = FP8_POISON
+            v_cache[...] = FP8_POISON
+        else:
+            k_cache[...] = 0x5A
+            v_cache[...] = 0xA5
+    else:
+        k_cache[...] = 0
+        v_cache[...] = 0
+
+    def draw(seq):
+        if kv_override is not None:
+            kk, vv = kv_override(seq, int(L[seq]))
+            return np.asarray(kk, np.float32), np.asarray(vv, np.float32)
+        shape = (Hkv, int(L[seq]), D)
+        return (r["k"].standard_normal(shape, dtype=np.float32),
+                r["v"].standard_normal(shape, dtype=np.float32))
+
+    # fp8 needs amax per KV head over the whole batch first: a first pass over the same streams
+    if fmt == "fp8":
+        if fp8_scale is None:
+            amax = np.zeros((2, Hkv), dtype=np.float32)
+            saved = (r["k"].bit_generator.state, r["v"].bit_generator.state)
+            for b in range(B):
+                kk, vv = draw(b)
+                if kk.size:
+                    amax[0] = np.maximum(amax[0], np.abs(kk).max(axis=(1, 2)))
+                    amax[1] = np.maximum(amax[1], np.abs(vv).max(axis=(1, 2)))
+            r["k"].bit_generator.state, r["v"].bit_generator.state = saved
+            scales = (amax / np.float32(448.0)).astype(np.float32)
+            scales[scales == 0] = np.float32(1.0)
+        else:
+            scales = np.asarray(fp8_scale, dtype=np.float32).reshape(2, Hkv)
+
+    cur = 0
+    for b in range(B):
+        Lb, npg = int(L[b]), int(n_pages[b])
+        phys = perm[cur: cur + npg]
+        cur += npg
+        kk, vv = draw(b)
+        if npg == 0:
+            continue
+        pad = npg * BLOCK_SIZE - Lb
+        if fmt == "bf16":
+            ke, ve = bf16_bits(kk), bf16_bits(vv)
+            fill = BF16_POISON if poison else np.uint16(0)
+        elif fmt == "fp8":
+            ke = e4m3fn_encode(kk / scales[0][:, None, None])
+            ve = e4m3fn_encode(vv / scales[1][:, None, None])
+            fill = FP8_POISON if poison else np.uint8(0)
+        else:
+            ke, kn = turbo_encode(kk, sgn, cb_k)
+            ve, vn = turbo_encode(vv, sgn, cb_v)
+            fill = np.uint8(0)
+            nfill = np.float32(np.nan if poison else 0.0)
+            kn = np.concatenate([kn, np.full((Hkv, pad), nfill, np.float32)], axis=1)
+            vn = np.concatenate([vn, np.full((Hkv, pad), nfill, np.float32)], axis=1)
+            scales[0, phys] = kn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
+            scales[1, phys] = vn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
+        ke = np.concatenate([ke, np.full((Hkv, pad, D), fill, ke.dtype)], axis=1)
+        ve = np.concatenate([ve, np.full((Hkv, pad, D), fill, ve.dtype)], axis=1)
+        ke = ke.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
+        ve = ve.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
+        k_cache[phys] = pack_k_pages(fmt, ke)
+        v_cache[phys] = pack_v_pages(fmt, ve)
+        if poison_before_window and W[b] > 0 and Lb > W[b]:
+            first_live = (Lb - int(W[b])) // BLOCK_SIZE
+            dead = phys[:first_live]
+            if fmt == "bf16":
+                k_cache.view(np.uint16)[dead] = BF16_POISON
+                v_cache.view(np.uint16)[dead] = BF16_POISON
+            elif fmt == "fp8":
+                k_cache[dead] = FP8_POISON
+                v_cache[dead] = FP8_POISON
+            else:
+                scales[:, dead] = np.nan
+
+    return Inputs(spec=s, q=q, k_cache=k_cache, v_cache=v_cache, scales=scales,
+                  codebook=codebook_arr, sign=sgn, block_table=bt, context_lens=L, window=W,
+                  softmax_scale=s.scale, softcap=np.float32(s.softcap), max_context_len=max_ctx)
+
+
+def relayout(inp: Inputs, seed: int) -> Inputs:
+    """The same logical cache placed in a different random set of physical pages."""
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 0xB10C]))
+    pool = inp.num_pool_blocks
+    new_of_old = rng.permutation(pool).astype(np.int32)
+    k = np.empty_like(inp.k_cache)
+    v = np.empty_like(inp.v_cache)
+    k[new_of_old] = inp.k_cache
+    v[new_of_old] = inp.v_cache
+    sc = inp.scales
+    if sc is not None and sc.ndim == 4:
+        sc = np.empty_like(inp.scales)
+        sc[:, new_of_old] = inp.scales
+    bt = inp.block_table.copy()
+    ok = bt >= 0
+    bt[ok] = new_of_old[bt[ok]]
+    return dataclasses.replace(inp, k_cache=k, v_cache=v, scales=sc, block_table=bt)

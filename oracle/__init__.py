@@ -1,0 +1,23 @@
+"""Oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
+
+Plain fp64 CPU definition (``attention``) and a 40-digit ``decimal`` brute force (``brute``).
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package; the GPU library never does, and the two share no code.
+"""
+from .attention import (  # noqa: F401
+    E4M3FN_TABLE,
+    attend,
+    attended_range,
+    bf16_to_f64,
+    decode_attention,
+    dequant_gather,
+    e4m3fn_value,
+    gather_kv,
+    gather_stored,
+    lse_merge,
+    partition_partials,
+    partitions,
+    sylvester_hadamard,
+    unpack_le,
+    unrotate,
+)
