@@ -1,0 +1,197 @@
+"""Benchmark: paged decode attention on one MI355X, effective KV GB/s against HBM peak.
+
+One "step" is one full decode-attention call (partition kernel + LSE reduce) over a synthetic
+batch already resident in HBM.  The default workload is the FP8-E4M3 cache at 32K context
+(16 sequences, 64 query / 8 KV heads, head_dim 128, 512-token partitions).  Every step is
+timed with HIP events on the stream the kernels run on: one event pair around the partition
+kernel, one around the whole call; a 512 MiB buffer is rewritten between steps (outside the
+events) so the 256 MB Infinity Cache holds no KV from the step before.
+
+Prints ONE JSON line.  `value` = algorithmic KV bytes per call / mean call time.
+`roofline` = the partition kernel's algorithmic bytes / its mean duration against 8 TB/s.
+`cpu_baseline` = the fp64 oracle timed on this host's cores over a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: effective KV GB/s (% of HBM peak) at 32K context"
+HBM_PEAK_GBS = 8000.0
+KV_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "turbo4": "turbo4 (K4/V4 rotated codebook)",
+            "turbo3": "turbo3 (K3/V4 rotated codebook)"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4",
+                    help="c1 c2 c3 c4 c5-t4 c5-t3 m-bf16 m-t4 m-t3 (see kvgen.SPECS)")
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per partition-kernel launch")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, seconds):
+    """Time the oracle (unchanged) on a bounded sample of (sequence, KV head) pairs."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    s = inp.spec
+    spans = inp.spans()
+    per_pair = kvgen_bytes_per_token_head(s)
+    done_bytes = 0
+    pairs = 0
+    t0 = time.perf_counter()
+    order = [(b, hk) for b in range(s.num_seqs) for hk in range(s.num_kv_heads)]
+    for b, hk in order:
+        oracle.decode_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table,
+                                inp.context_lens, s.fmt, inp.scales, inp.codebook, inp.sign,
+                                inp.softmax_scale, inp.window, inp.softcap, s.num_kv_heads,
+                                s.head_dim, seqs=[b], kv_heads=[hk])
+        done_bytes += int(spans[b]) * per_pair
+        pairs += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{pairs} of {len(order)} (sequence, KV head) pairs, {done_bytes / 1e6:.1f} MB "
+                      f"of KV in {dt:.1f} s (NumPy fp64 oracle, host cores {os.cpu_count()})"}
+
+
+def kvgen_bytes_per_token_head(s):
+    import kvgen
+    return kvgen.kv_bytes_per_token_head(s.fmt, s.head_dim)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+              "(the per-(sequence, KV head, partition) work would shard by sequence or KV head "
+              "with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import kvgen
+    import quantized_kv_cache_split_amd as kvd
+    from kvgen.torch_io import dims_kwargs, to_torch
+
+    spec = kvgen.SPECS[args.workload]
+    t_gen = time.perf_counter()
+    inp = kvgen.make_inputs(spec)
+    t_gen = time.perf_counter() - t_gen
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t = to_torch(inp, dev)
+    ps = args.partition_size if args.partition_size is not None else spec.partition_size
+    dims = kvd.Dims(**dims_kwargs(inp, ps))
+    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=torch.float32,
+                      device=dev)
+    nws = kvd.workspace_bytes(dims)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) if nws else None
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    call_args = (dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+                 spec.fmt, t["scales"], t["codebook"], t["sign_pattern"],
+                 float(inp.softmax_scale), t["window"], float(inp.softcap), out, ws)
+    kv_bytes = inp.kv_bytes()
+
+    def step(ev=None):
+        if ev is None:
+            kvd.decode_partitions(*call_args)
+            kvd.reduce_partitions(*call_args)
+            return
+        ev[0].record()
+        kvd.decode_partitions(*call_args)
+        ev[1].record()
+        kvd.reduce_partitions(*call_args)
+        ev[2].record()
+
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    t_part = np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3   # seconds
+    t_call = np.array([e[0].elapsed_time(e[2]) for e in events]) * 1e-3
+    assert np.isfinite(out.cpu().numpy()).all(), "non-finite output"
+
+    mean_call = float(t_call.mean())
+    value = kv_bytes / mean_call / 1e9
+    achieved = kv_bytes / float(t_part.mean()) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        rec = json.load(open(args.traffic))
+        if rec.get("workload") == args.workload:
+            traffic = rec.get("hbm_bytes_per_launch")
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_call * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {spec.name}",
+            "num_seqs": spec.num_seqs, "num_q_heads": spec.num_q_heads,
+            "num_kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
+            "context": spec.context if spec.context else list(spec.ctx_range),
+            "window": spec.window, "softcap": spec.softcap,
+            "kv_format": KV_NAMES[spec.fmt], "block_size": 16,
+            "partition_size": ps if ps else 512, "kv_bytes_per_step": kv_bytes,
+            "mfma_operands": "bf16 (bf16/fp8 caches), fp16 (codebook caches); fp32 accumulate",
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "decode_tokens_per_s": round(spec.num_seqs / mean_call, 1),
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(t_call, q)) * 1e3, 4) for q in (10, 50, 90)],
+        "partition_kernel_ms": round(float(t_part.mean()) * 1e3, 4),
+        "reduce_kernel_ms": round(float((t_call - t_part).mean()) * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+        "input_gen_s": round(t_gen, 1),
+        "timed_wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+/*
+ * kvdecode.h -- C ABI of a gfx950 (AMD Instinct MI355X) library for single-query (decode-phase)
+ * attention over a paged KV cache.
+ *
+ * What it computes.  For each sequence b and query head h, with L = context_lens[b] and the
+ * attended key range [lo, L) (lo = max(0, L - window[b]) when window[b] > 0, else 0):
+ *
+ *     z_j   = softmax_scale * <q[b,h], k_j>            j in [lo, L)
+ *     z_j   = softcap * tanh(z_j / softcap)             only when softcap > 0
+ *     out[b,h] = sum_j exp(z_j - max z) v_j / sum_j exp(z_j - max z)
+ *
+ * with k_j, v_j the dequantised key/value vectors of KV head floor(h / (Hq / Hkv)) (GQA/MQA).
+ * Sources: attention.rs README ("KV Cache Formats": BF16, FP8 E4M3, Turbo4 and Turbo3 caches,
+ * each with decode and Split-K decode kernels sharing one float reduce, Split-K from 1024
+ * tokens; "Features": softcapping, sliding window, GQA/MQA, paged block tables, causal mask)
+ * and turboquant-rs 0.4.1 src/cache/cuda/attention.rs (two phases, partitioned attention then
+ * a reduce; 512-token partitions, ceil(kv_len / 512) of them; fp32 per-partition max, sum and
+ * output; the compressed cache is read directly with a sign pattern and a codebook; an empty
+ * context yields an all-zero fp32 output).
+ *
+ * Readings where those pages are silent: the window holds the W most recent keys including
+ * the query's own position; the cap acts on the scaled logit before the max; an empty context
+ * gives zero rows; partitions sit at absolute multiples of the partition size.
+ *
+ * Conventions for every entry point.
+ *   - All array pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronises; it keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null stream).
+ *     Buffers must stay alive until that work has finished.
+ *   - Errors are returned as an int status (kvd_status), never printed.  Arguments are checked
+ *     on the host before anything is launched, so a call that returns an error has launched
+ *     nothing.  After launching, a pending HIP launch error maps to KVD_ERR_HIP.
+ *   - Data-dependent faults the host cannot see are caught on the device, never by reading
+ *     out of bounds: a sequence whose context length is negative or above max_context_len, or
+ *     any of whose block-table entries in the attended range lies outside [0, num_pool_blocks),
+ *     gets NaN in all of its output rows.
+ *
+ * PAGED LAYOUT (block_size is 16 tokens; "chunk" = the bytes of one (page, KV head)).
+ * The K cache is an array [num_pool_blocks][num_kv_heads][k_chunk] of bytes, the V cache
+ * [num_pool_blocks][num_kv_heads][v_chunk]; chunk (p, h) starts at byte (p * Hkv + h) * chunk.
+ * Inside one chunk, with D = head_dim, t the token slot 0..15 and d the element index:
+ *
+ *   BF16  (KVD_BF16)      K: [D/8][16][8] bf16   -- element (t, d) at ((d/8)*16 + t)*8 + d%8
+ *                         V: [D][16]      bf16   -- element (t, d) at d*16 + t (transposed)
+ *                         k_chunk = v_chunk = 32*D bytes
+ *   FP8   (KVD_FP8_E4M3)  K: [D/16][16][16] u8   -- element (t, d) at ((d/16)*16 + t)*16 + d%16
+ *                         V: [D][16] u8          -- element (t, d) at d*16 + t
+ *                         codes are OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN);
+ *                         value = E4M3FN(code) * scale, one fp32 scale per (K|V, KV head).
+ *                         k_chunk = v_chunk = 16*D bytes
+ *   TURBO4 (KVD_TURBO4)   K: [D/32][16][16 B]    -- 32 4-bit indices per 16-byte group
+ *   TURBO3 (KVD_TURBO3)   K: [D/32][16][12 B]    -- 32 3-bit indices per 12-byte group
+ *                         index of (t, d) sits in group ((d/32)*16 + t) at position e = d%32:
+ *                         bits [b*e, b*e + b) of the group's little-endian bitstream (stream
+ *                         bit k = bit k%8 of byte k/8; 4-bit: even e in the low nibble).
+ *                         V (both Turbo formats, 4-bit): [D][16 nibbles = 8 B] -- index of
+ *                         (t, d) is nibble t of row d (even t in the low nibble).
+ *                         k_chunk = 8*D (TURBO4) or 6*D (TURBO3), v_chunk = 8*D bytes.
+ *                         Stored value in the rotated domain: norm[t] * codebook[index];
+ *                         the original vector is  x = diag(s) H x_rot / sqrt(D), H the
+ *                         Sylvester-order D x D Hadamard matrix, s = sign_pattern.
+ *
+ * Query q: bf16 [num_seqs][num_q_heads][D].  Output out: fp32 [num_seqs][num_q_heads][D], in
+ * the original (un-rotated) domain for every format.
+ */
+#ifndef KVDECODE_H
+#define KVDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvd_format {
+    KVD_BF16 = 0,       /* unquantised bfloat16 K and V */
+    KVD_FP8_E4M3 = 1,   /* OCP E4M3FN codes, fp32 scale per KV head */
+    KVD_TURBO4 = 2,     /* rotated codebook: 4-bit K, 4-bit V, fp32 per-token norms */
+    KVD_TURBO3 = 3      /* rotated codebook: 3-bit K, 4-bit V, fp32 per-token norms */
+} kvd_format;
+
+typedef enum kvd_status {
+    KVD_OK = 0,
+    KVD_ERR_NULL = -1,       /* a required pointer is NULL */
+    KVD_ERR_SHAPE = -2,      /* unsupported or inconsistent dimensions */
+    KVD_ERR_FORMAT = -3,     /* unknown kv format */
+    KVD_ERR_ALIGN = -4,      /* a pointer is not 16-byte aligned */
+    KVD_ERR_WORKSPACE = -5,  /* workspace missing or smaller than kvd_workspace_bytes() */
+    KVD_ERR_HIP = -6         /* the HIP runtime reported an error while launching */
+} kvd_status;
+
+/* Shapes.  Supported: block_size == 16; head_dim 64 or 128 for BF16/FP8, 128 for the Turbo
+ * formats; num_q_heads a multiple of num_kv_heads with num_q_heads / num_kv_heads <= 16. */
+typedef struct kvd_dims {
+    int32_t num_seqs;            /* B */
+    int32_t num_q_heads;         /* Hq */
+    int32_t num_kv_heads;        /* Hkv */
+    int32_t head_dim;            /* D */
+    int32_t block_size;          /* tokens per page; must be 16 */
+    int32_t max_blocks_per_seq;  /* row length of block_table */
+    int32_t num_pool_blocks;     /* pages in the K/V pools (device-side bounds check) */
+    int32_t max_context_len;     /* upper bound on context_lens[], >= 1, <= 16 * max_blocks_per_seq */
+    int32_t partition_size;      /* 0: auto -- 512-token partitions when a sequence attends to
+                                    >= 1024 tokens, else a single partition;
+                                    > 0: always split at that many tokens (a multiple of 16);
+                                    -1: never split */
+} kvd_dims;
+
+/* Bytes of device workspace kvd_decode_attn_paged needs: the per-partition fp32 triples
+ * m [B][Hq][P], l [B][Hq][P] and o [B][Hq][P][D], P = ceil(max_context_len / partition size),
+ * each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
+size_t kvd_workspace_bytes(const kvd_dims* dims);
+
+/* Decode attention, both phases (partition kernel, then the reduce kernel when any sequence
+ * is split).
+ *   q            bf16 [B][Hq][D]
+ *   k_cache      K pool in `fmt`'s layout (above);  v_cache  V pool
+ *   block_table  int32 [B][max_blocks_per_seq]; entries for the pages holding the attended
+ *                range [lo, L) must be valid pool indices (others are never read)
+ *   context_lens int32 [B]; 0 gives an all-zero output row
+ *   fmt          a kvd_format
+ *   scales       KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv], K scales then V;
+ *                Turbo: fp32 per-token norms [2][num_pool_blocks][Hkv][16], K then V
+ *   codebook     Turbo: fp32 levels, 2^kbits for K then 16 for V (kbits 4 or 3); else unused
+ *   sign_pattern Turbo: fp32 [D] of +1.0 / -1.0; else unused
+ *   softmax_scale  logit scale (e.g. 1/sqrt(D))
+ *   window       int32 [B] sliding-window widths (0 = none), or NULL for no window at all
+ *   softcap      tanh cap on the scaled logits; 0 = off
+ *   out          fp32 [B][Hq][D]; must not alias any input
+ *   workspace    >= kvd_workspace_bytes(dims) bytes, 256-byte aligned; contents on entry do
+ *                not matter; on return it holds the partials of split sequences
+ *   stream       hipStream_t
+ * All pointers 16-byte aligned. */
+int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* context_lens, int fmt, const float* scales,
+                          const float* codebook, const float* sign_pattern, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Phase 1 alone (same arguments).  One workgroup per (partition, KV head, sequence).  For a
+ * split sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and its triple goes
+ * to the workspace at (b, h, p):  m = max_j z_j * log2(e)  (base-2 units),
+ * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
+ * rotated domain for the Turbo formats.  Empty partitions are not written.  Sequences that are
+ * not split get their final output row written here. */
+int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* context_lens, int fmt, const float* scales,
+                          const float* codebook, const float* sign_pattern, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Phase 2 alone (same arguments; reads the workspace phase 1 filled).  For each split
+ * (b, h): M = max_p m_p, w_p = l_p 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p, then (Turbo)
+ * out <- diag(s) H out / sqrt(D).  Rows of sequences that are not split are left untouched. */
+int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* block_table,
+                          const int32_t* context_lens, int fmt, const float* scales,
+                          const float* codebook, const float* sign_pattern, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Test export: dequantised cache values of tokens [token_begin, token_begin + n_tokens) of
+ * sequence `seq`, KV head `kv_head`, gathered through the block table, written as fp32
+ * [n_tokens][D] in the storage domain: BF16 widened; FP8 E4M3FN(code) * scale rounded to fp32;
+ * Turbo norm * codebook[index] rounded to fp32 (still rotated).  is_v selects V (1) or K (0).
+ * `scales`, `codebook` as for kvd_decode_attn_paged.  Uses the same unpack and decode device
+ * code as the attention kernel.  Tokens must lie in [0, 16 * max_blocks_per_seq). */
+int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cache,
+                       const float* scales, const float* codebook, const int32_t* block_table,
+                       int32_t seq, int32_t kv_head, int32_t token_begin, int32_t n_tokens,
+                       float* out, void* stream);
+
+/* A static, human-readable name for a status code. */
+const char* kvd_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVDECODE_H */

@@ -19,6 +19,8 @@ from __future__ import annotations
 import dataclasses
 import functools
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -134,18 +136,25 @@ def e4m3fn_encode(x: np.ndarray) -> np.ndarray:
     E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits; S.1111.111 is NaN, there is no
     infinity, the largest finite value is 1.75 * 2^8 = 448 and the smallest subnormal 2^-9.
     """
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    sign = (x.view(np.uint32) >> np.uint32(24)).astype(np.uint8) & np.uint8(0x80)
-    a = np.minimum(np.abs(x), np.float32(448.0))
-    bits = a.view(np.uint32)
-    # normal range: round the 23-bit mantissa to 3 bits (ties to even); a carry bumps the exponent
-    r = (bits + np.uint32(0x7FFFF) + ((bits >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)
-    normal = (r.astype(np.int64) - ((127 - 7) << 3))
-    # subnormal range (a < 2^-6): multiples of 2^-9; 8 * 2^-9 is the smallest normal, code 0x08
-    sub = np.rint(a * np.float32(512.0)).astype(np.int64)
-    code = np.where(a < np.float32(2.0 ** -6), sub, normal)
-    code = np.minimum(code, 0x7E).astype(np.uint8)
-    return code | sign
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    sign = ((bits >> np.uint32(24)) & np.uint32(0x80)).astype(np.uint8)
+    # |x| clamped to 448 (0x43E00000); for non-negative floats bit order is value order
+    a = np.minimum(bits & np.uint32(0x7FFFFFFF), np.uint32(0x43E00000))
+    # normal range: round the 23-bit mantissa to 3 bits (ties to even); a carry bumps the
+    # exponent; then rebias 127 -> 7
+    r = a >> np.uint32(20)
+    r &= np.uint32(1)
+    r += a
+    r += np.uint32(0x7FFFF)
+    r >>= np.uint32(20)
+    r -= np.uint32((127 - 7) << 3)
+    # subnormal range (|x| < 2^-6): multiples of 2^-9; 8 * 2^-9 is the smallest normal, 0x08
+    small = a < np.uint32(0x3C800000)
+    if small.any():
+        r[small] = np.rint(a[small].view(np.float32) * np.float32(512.0)).astype(np.uint32)
+    code = r.astype(np.uint8)
+    code |= sign
+    return code
 
 
 def sign_pattern(rng: np.random.Generator, d: int) -> np.ndarray:
@@ -328,9 +337,13 @@ class Inputs:
 _STREAMS = ("q", "k", "v", "pool", "lengths", "window", "sign")
 
 
-def _rngs(seed: int) -> dict[str, np.random.Generator]:
+def _rngs(seed: int) -> dict:
+    """Generators of the named streams, plus the K / V SeedSequences ('k_seq', 'v_seq') whose
+    per-sequence children draw the cache contents."""
     kids = np.random.SeedSequence(seed).spawn(len(_STREAMS))
-    return {name: np.random.default_rng(k) for name, k in zip(_STREAMS, kids)}
+    out = {name: np.random.default_rng(k) for name, k in zip(_STREAMS, kids)}
+    out["k_seq"], out["v_seq"] = kids[1], kids[2]
+    return out
 
 
 def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = False,
@@ -416,38 +429,44 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         k_cache[...] = 0
         v_cache[...] = 0
 
+    # K and V of sequence b come from child b of the K / V stream, so sequences can be drawn and
+    # encoded in parallel threads with a result that does not depend on the thread count.
+    k_kids, v_kids = r["k_seq"].spawn(B), r["v_seq"].spawn(B)
+
     def draw(seq):
         if kv_override is not None:
             kk, vv = kv_override(seq, int(L[seq]))
             return np.asarray(kk, np.float32), np.asarray(vv, np.float32)
         shape = (Hkv, int(L[seq]), D)
-        return (r["k"].standard_normal(shape, dtype=np.float32),
-                r["v"].standard_normal(shape, dtype=np.float32))
+        return (np.random.default_rng(k_kids[seq]).standard_normal(shape, dtype=np.float32),
+                np.random.default_rng(v_kids[seq]).standard_normal(shape, dtype=np.float32))
 
-    # fp8 needs amax per KV head over the whole batch first: a first pass over the same streams
+    starts = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int64)
+    workers = max(1, min(16, os.cpu_count() or 1, B))
+    drawn = {}
     if fmt == "fp8":
+        # one fp32 scale per (K|V, KV head) = amax / 448 over the whole batch: draw first
+        def first(b):
+            kk, vv = draw(b)
+            drawn[b] = (kk, vv)
+            if not kk.size:
+                return np.zeros((2, Hkv), np.float32)
+            return np.stack([np.abs(kk).max(axis=(1, 2)), np.abs(vv).max(axis=(1, 2))])
+        with ThreadPoolExecutor(workers) as ex:
+            amaxes = list(ex.map(first, range(B)))
         if fp8_scale is None:
-            amax = np.zeros((2, Hkv), dtype=np.float32)
-            saved = (r["k"].bit_generator.state, r["v"].bit_generator.state)
-            for b in range(B):
-                kk, vv = draw(b)
-                if kk.size:
-                    amax[0] = np.maximum(amax[0], np.abs(kk).max(axis=(1, 2)))
-                    amax[1] = np.maximum(amax[1], np.abs(vv).max(axis=(1, 2)))
-            r["k"].bit_generator.state, r["v"].bit_generator.state = saved
+            amax = np.max(np.stack(amaxes), axis=0).astype(np.float32)
             scales = (amax / np.float32(448.0)).astype(np.float32)
             scales[scales == 0] = np.float32(1.0)
         else:
             scales = np.asarray(fp8_scale, dtype=np.float32).reshape(2, Hkv)
 
-    cur = 0
-    for b in range(B):
+    def fill_seq(b):
         Lb, npg = int(L[b]), int(n_pages[b])
-        phys = perm[cur: cur + npg]
-        cur += npg
-        kk, vv = draw(b)
+        phys = perm[starts[b]: starts[b] + npg]
+        kk, vv = drawn.pop(b) if b in drawn else draw(b)
         if npg == 0:
-            continue
+            return
         pad = npg * BLOCK_SIZE - Lb
         if fmt == "bf16":
             ke, ve = bf16_bits(kk), bf16_bits(vv)
@@ -465,6 +484,7 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
             vn = np.concatenate([vn, np.full((Hkv, pad), nfill, np.float32)], axis=1)
             scales[0, phys] = kn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
             scales[1, phys] = vn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
+        del kk, vv
         ke = np.concatenate([ke, np.full((Hkv, pad, D), fill, ke.dtype)], axis=1)
         ve = np.concatenate([ve, np.full((Hkv, pad, D), fill, ve.dtype)], axis=1)
         ke = ke.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
@@ -482,6 +502,9 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
                 v_cache[dead] = FP8_POISON
             else:
                 scales[:, dead] = np.nan
+
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(fill_seq, range(B)))
 
     return Inputs(spec=s, q=q, k_cache=k_cache, v_cache=v_cache, scales=scales,
                   codebook=codebook_arr, sign=sgn, block_table=bt, context_lens=L, window=W,

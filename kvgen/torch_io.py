@@ -1,0 +1,31 @@
+"""Move a generated batch into torch tensors (device memory plumbing; no arithmetic)."""
+from __future__ import annotations
+
+import numpy as np
+
+
+def dims_kwargs(inp, partition_size: int | None = None) -> dict:
+    """Field values of the C ABI's kvd_dims for a batch."""
+    s = inp.spec
+    return dict(num_seqs=s.num_seqs, num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads,
+                head_dim=s.head_dim, block_size=16, max_blocks_per_seq=inp.max_blocks_per_seq,
+                num_pool_blocks=inp.num_pool_blocks, max_context_len=inp.max_context_len,
+                partition_size=s.partition_size if partition_size is None else partition_size)
+
+
+def to_torch(inp, device) -> dict:
+    """Tensors for every array argument of the decode call (None where unused)."""
+    import torch
+
+    def t(a, dtype=None):
+        if a is None:
+            return None
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype is not None:
+            x = x.view(dtype)
+        return x.to(device)
+
+    return dict(q=t(inp.q.view(np.int16), torch.bfloat16), k_cache=t(inp.k_cache),
+                v_cache=t(inp.v_cache), block_table=t(inp.block_table),
+                context_lens=t(inp.context_lens), scales=t(inp.scales), codebook=t(inp.codebook),
+                sign_pattern=t(inp.sign), window=t(inp.window))

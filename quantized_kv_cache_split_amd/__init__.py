@@ -1,0 +1,155 @@
+"""Python binding of libkvdecode.so: single-query decode attention over a paged KV cache on
+MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+Functions take torch tensors that already live on the GPU (or None for optional arguments),
+pass their device pointers and the current HIP stream to the C ABI (include/kvdecode.h) and
+raise KvdError on a non-zero status.  Importing this module loads the library and fails loudly
+if it has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "FORMATS",
+           "workspace_bytes", "decode_attn_paged", "decode_partitions", "reduce_partitions",
+           "dequant_gather", "status_str", "library_path", "load"]
+
+BF16, FP8_E4M3, TURBO4, TURBO3 = 0, 1, 2, 3
+FORMATS = {"bf16": BF16, "fp8": FP8_E4M3, "turbo4": TURBO4, "turbo3": TURBO3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
+_lib = None
+
+
+class KvdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+                ("num_pool_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("partition_size", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+_ATTN_ARGS = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+              ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+
+
+def load() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.kvd_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
+        lib.kvd_workspace_bytes.restype = ctypes.c_size_t
+        for name in ("kvd_decode_attn_paged", "kvd_decode_partitions", "kvd_reduce_partitions"):
+            f = getattr(lib, name)
+            f.argtypes = _ATTN_ARGS
+            f.restype = ctypes.c_int
+        lib.kvd_dequant_gather.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        lib.kvd_dequant_gather.restype = ctypes.c_int
+        lib.kvd_status_str.argtypes = [ctypes.c_int]
+        lib.kvd_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load().kvd_status_str(status).decode()
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _fmt(fmt) -> int:
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def workspace_bytes(dims: Dims) -> int:
+    return int(load().kvd_workspace_bytes(ctypes.byref(dims)))
+
+
+def _attn(name, dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
+          sign_pattern, softmax_scale, window, softcap, out, workspace, stream):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(load(), name)(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(block_table), _ptr(context_lens), _fmt(fmt), _ptr(scales),
+                               _ptr(codebook), _ptr(sign_pattern), float(softmax_scale),
+                               _ptr(window), float(softcap), _ptr(out), _ptr(workspace),
+                               ws_bytes, _stream(stream))
+    if st != 0:
+        raise KvdError(st, name)
+    return out
+
+
+def decode_attn_paged(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
+                      codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
+                      stream=None):
+    """Both phases; see kvd_decode_attn_paged in include/kvdecode.h."""
+    return _attn("kvd_decode_attn_paged", dims, q, k_cache, v_cache, block_table, context_lens,
+                 fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
+                 workspace, stream)
+
+
+def decode_partitions(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
+                      codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
+                      stream=None):
+    """Phase 1 (partition kernel) only."""
+    return _attn("kvd_decode_partitions", dims, q, k_cache, v_cache, block_table, context_lens,
+                 fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
+                 workspace, stream)
+
+
+def reduce_partitions(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
+                      codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
+                      stream=None):
+    """Phase 2 (reduce kernel) only."""
+    return _attn("kvd_reduce_partitions", dims, q, k_cache, v_cache, block_table, context_lens,
+                 fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
+                 workspace, stream)
+
+
+def dequant_gather(dims, fmt, is_v, cache, scales, codebook, block_table, seq, kv_head,
+                   token_begin, n_tokens, out, stream=None):
+    """Dequantised values of tokens [token_begin, token_begin + n_tokens) -> out fp32 [n, D]."""
+    st = load().kvd_dequant_gather(ctypes.byref(dims), _fmt(fmt), int(bool(is_v)), _ptr(cache),
+                                   _ptr(scales), _ptr(codebook), _ptr(block_table), int(seq),
+                                   int(kv_head), int(token_begin), int(n_tokens), _ptr(out),
+                                   _stream(stream))
+    if st != 0:
+        raise KvdError(st, "kvd_dequant_gather")
+    return out
+
+
+load()

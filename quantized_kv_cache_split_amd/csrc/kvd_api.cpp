@@ -1,0 +1,244 @@
+// C-ABI host layer: argument checks, workspace sizing and kernel launches (include/kvdecode.h).
+//
+// Mirrors the host side of turboquant-rs 0.4.1 src/cache/cuda/attention.rs: refuse bad
+// arguments before anything runs, size the partitions as ceil(len / partition size), launch
+// the partition kernel and then the reduce, and report a launch failure.  Unlike that wrapper
+// it allocates nothing: the partial buffers live in a caller-provided workspace.
+#include <hip/hip_runtime.h>
+
+#include "kvd_internal.h"
+#include "kvdecode.h"
+
+namespace {
+
+using kvd::LaunchParams;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t k_chunk_bytes(int fmt, int d) {
+    switch (fmt) {
+        case KVD_BF16: return 32LL * d;
+        case KVD_FP8_E4M3: return 16LL * d;
+        case KVD_TURBO4: return 8LL * d;
+        default: return 6LL * d;
+    }
+}
+int64_t v_chunk_bytes(int fmt, int d) {
+    return fmt == KVD_BF16 ? 32LL * d : (fmt == KVD_FP8_E4M3 ? 16LL * d : 8LL * d);
+}
+
+struct Plan {
+    int mode;        // kvd::PartMode
+    int part_size;   // tokens
+    int P;           // partitions per sequence kept in the workspace (0 = no split possible)
+    size_t off_l, off_o, bytes;
+};
+
+// Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
+int check_dims(const kvd_dims* d, int fmt) {
+    if (!d) return KVD_ERR_NULL;
+    if (fmt >= 0 && (fmt < KVD_BF16 || fmt > KVD_TURBO3)) return KVD_ERR_FORMAT;
+    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return KVD_ERR_SHAPE;
+    if (d->num_q_heads % d->num_kv_heads != 0) return KVD_ERR_SHAPE;
+    if (d->num_q_heads / d->num_kv_heads > kvd::kMaxGroup) return KVD_ERR_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return KVD_ERR_SHAPE;
+    if (fmt >= KVD_TURBO4 && d->head_dim != 128) return KVD_ERR_SHAPE;
+    if (d->block_size != kvd::kPageTokens) return KVD_ERR_SHAPE;
+    if (d->max_blocks_per_seq < 1 || d->num_pool_blocks < 1) return KVD_ERR_SHAPE;
+    if (d->max_context_len < 1 ||
+        (int64_t)d->max_context_len > (int64_t)kvd::kPageTokens * d->max_blocks_per_seq)
+        return KVD_ERR_SHAPE;
+    const int ps = d->partition_size;
+    if (!(ps == 0 || ps == -1 || (ps > 0 && ps % kvd::kPageTokens == 0))) return KVD_ERR_SHAPE;
+    if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return KVD_ERR_SHAPE;   // grid limits
+    return KVD_OK;
+}
+
+Plan make_plan(const kvd_dims* d) {
+    Plan pl{};
+    if (d->partition_size == -1) {
+        pl.mode = kvd::kPartNever;
+        pl.part_size = d->max_context_len;
+        pl.P = 0;
+    } else if (d->partition_size == 0) {
+        pl.mode = kvd::kPartAuto;
+        pl.part_size = kvd::kAutoPartition;
+        pl.P = d->max_context_len >= kvd::kAutoSplitMin
+                   ? (d->max_context_len + pl.part_size - 1) / pl.part_size : 0;
+    } else {
+        pl.mode = kvd::kPartFixed;
+        pl.part_size = d->partition_size;
+        pl.P = (d->max_context_len + pl.part_size - 1) / pl.part_size;
+    }
+    const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl.P;
+    const size_t ml = round_up(rows * sizeof(float), 256);
+    pl.off_l = ml;
+    pl.off_o = 2 * ml;
+    pl.bytes = pl.P ? 2 * ml + round_up(rows * d->head_dim * sizeof(float), 256) : 0;
+    return pl;
+}
+
+enum Phases { kPhase1 = 1, kPhase2 = 2 };
+
+int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const void* v_cache,
+        const int32_t* block_table, const int32_t* context_lens, int fmt, const float* scales,
+        const float* codebook, const float* sign_pattern, float softmax_scale,
+        const int32_t* window, float softcap, float* out, void* workspace,
+        size_t workspace_bytes, void* stream) {
+    int st = check_dims(d, fmt);
+    if (st != KVD_OK) return st;
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return KVD_ERR_NULL;
+    if (fmt == KVD_FP8_E4M3 && !scales) return KVD_ERR_NULL;
+    if (fmt >= KVD_TURBO4 && (!scales || !codebook || !sign_pattern)) return KVD_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(block_table, 4) || !aligned(context_lens, 4) || (window && !aligned(window, 4)) ||
+        (scales && !aligned(scales, 16)) || (codebook && !aligned(codebook, 4)) ||
+        (sign_pattern && !aligned(sign_pattern, 4)))
+        return KVD_ERR_ALIGN;
+    if (!(softcap >= 0.0f) || !(softmax_scale == softmax_scale)) return KVD_ERR_SHAPE;
+    const Plan pl = make_plan(d);
+    if (pl.bytes) {
+        if (!workspace) return KVD_ERR_WORKSPACE;
+        if (workspace_bytes < pl.bytes) return KVD_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return KVD_ERR_ALIGN;
+    }
+    if (d->num_seqs == 0) return KVD_OK;
+
+    LaunchParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint8_t*>(k_cache);
+    p.v = static_cast<const uint8_t*>(v_cache);
+    p.bt = block_table;
+    p.ctx = context_lens;
+    p.win = window;
+    p.scales = scales;
+    p.codebook = codebook;
+    p.sign = sign_pattern;
+    p.out = out;
+    char* ws = static_cast<char*>(workspace);
+    p.ws_m = pl.bytes ? reinterpret_cast<float*>(ws) : nullptr;
+    p.ws_l = pl.bytes ? reinterpret_cast<float*>(ws + pl.off_l) : nullptr;
+    p.ws_o = pl.bytes ? reinterpret_cast<float*>(ws + pl.off_o) : nullptr;
+    p.k_chunk = k_chunk_bytes(fmt, d->head_dim);
+    p.v_chunk = v_chunk_bytes(fmt, d->head_dim);
+    p.B = d->num_seqs;
+    p.Hq = d->num_q_heads;
+    p.Hkv = d->num_kv_heads;
+    p.g = d->num_q_heads / d->num_kv_heads;
+    p.D = d->head_dim;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.pool = d->num_pool_blocks;
+    p.max_ctx = d->max_context_len;
+    p.part_mode = pl.P ? pl.mode : kvd::kPartNever;
+    p.part_size = pl.part_size;
+    p.P = pl.P;
+    p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    p.softmax_scale = softmax_scale;
+    p.softcap = softcap;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (phases & kPhase1) {
+        const dim3 grid(pl.P ? pl.P : 1, d->num_kv_heads, d->num_seqs);
+        e = kvd::launch_partitions(fmt, p, grid, s);
+        if (e != hipSuccess) return KVD_ERR_HIP;
+    }
+    if ((phases & kPhase2) && pl.P) {
+        e = kvd::launch_reduce(fmt, p, s);
+        if (e != hipSuccess) return KVD_ERR_HIP;
+    }
+    return KVD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvd_workspace_bytes(const kvd_dims* dims) {
+    if (check_dims(dims, -1) != KVD_OK) return 0;
+    return make_plan(dims).bytes;
+}
+
+int kvd_decode_attn_paged(const kvd_dims* d, const void* q, const void* k, const void* v,
+                          const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
+                          const float* codebook, const float* sign, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    return run(kPhase1 | kPhase2, d, q, k, v, bt, ctx, fmt, scales, codebook, sign,
+               softmax_scale, window, softcap, out, ws, ws_bytes, stream);
+}
+
+int kvd_decode_partitions(const kvd_dims* d, const void* q, const void* k, const void* v,
+                          const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
+                          const float* codebook, const float* sign, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    return run(kPhase1, d, q, k, v, bt, ctx, fmt, scales, codebook, sign, softmax_scale,
+               window, softcap, out, ws, ws_bytes, stream);
+}
+
+int kvd_reduce_partitions(const kvd_dims* d, const void* q, const void* k, const void* v,
+                          const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
+                          const float* codebook, const float* sign, float softmax_scale,
+                          const int32_t* window, float softcap, float* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    return run(kPhase2, d, q, k, v, bt, ctx, fmt, scales, codebook, sign, softmax_scale,
+               window, softcap, out, ws, ws_bytes, stream);
+}
+
+int kvd_dequant_gather(const kvd_dims* d, int fmt, int is_v, const void* cache,
+                       const float* scales, const float* codebook, const int32_t* block_table,
+                       int32_t seq, int32_t kv_head, int32_t token_begin, int32_t n_tokens,
+                       float* out, void* stream) {
+    int st = check_dims(d, fmt);
+    if (st != KVD_OK) return st;
+    if (!cache || !block_table || !out) return KVD_ERR_NULL;
+    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (fmt >= KVD_TURBO4 && !codebook) return KVD_ERR_NULL;
+    if (!aligned(cache, 16) || !aligned(out, 4) || !aligned(block_table, 4) ||
+        (scales && !aligned(scales, 4)))
+        return KVD_ERR_ALIGN;
+    if (seq < 0 || seq >= d->num_seqs || kv_head < 0 || kv_head >= d->num_kv_heads ||
+        token_begin < 0 || n_tokens < 0 ||
+        (int64_t)token_begin + n_tokens > (int64_t)kvd::kPageTokens * d->max_blocks_per_seq)
+        return KVD_ERR_SHAPE;
+    if ((int64_t)n_tokens * d->head_dim > 0x7FFFFFFF) return KVD_ERR_SHAPE;
+    if (n_tokens == 0) return KVD_OK;
+    kvd::GatherParams p{};
+    p.cache = static_cast<const uint8_t*>(cache);
+    p.scales = scales;
+    p.codebook = codebook;
+    p.bt = block_table;
+    p.out = out;
+    p.fmt = fmt;
+    p.is_v = is_v ? 1 : 0;
+    p.chunk = is_v ? v_chunk_bytes(fmt, d->head_dim) : k_chunk_bytes(fmt, d->head_dim);
+    p.Hkv = d->num_kv_heads;
+    p.D = d->head_dim;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.pool = d->num_pool_blocks;
+    p.seq = seq;
+    p.kv_head = kv_head;
+    p.t0 = token_begin;
+    p.n = n_tokens;
+    p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    return kvd::launch_gather(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KVD_OK
+                                                                                 : KVD_ERR_HIP;
+}
+
+const char* kvd_status_str(int status) {
+    switch (status) {
+        case KVD_OK: return "ok";
+        case KVD_ERR_NULL: return "a required pointer is NULL";
+        case KVD_ERR_SHAPE: return "unsupported or inconsistent dimensions";
+        case KVD_ERR_FORMAT: return "unknown kv format";
+        case KVD_ERR_ALIGN: return "a pointer is not aligned as required";
+        case KVD_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVD_ERR_HIP: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI host layer (kvd_api.cpp) and the HIP kernels
+// (kvd_kernels.hip).  Not installed; the public contract is include/kvdecode.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kvd {
+
+constexpr int kPageTokens = 16;     // tokens per page (block_size)
+constexpr int kAutoPartition = 512; // partition size of the automatic split
+constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
+constexpr int kMaxGroup = 16;       // query heads per KV head one workgroup handles
+
+enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };
+
+// Everything a kernel needs, passed by value as the kernel argument.
+struct LaunchParams {
+    const uint16_t* q;        // bf16 [B][Hq][D]
+    const uint8_t* k;         // K pool
+    const uint8_t* v;         // V pool
+    const int32_t* bt;        // [B][max_blocks]
+    const int32_t* ctx;       // [B]
+    const int32_t* win;       // [B] or nullptr
+    const float* scales;      // fp8 [2][Hkv]; turbo norms [2][pool][Hkv][16]
+    const float* codebook;    // turbo levels (K then V)
+    const float* sign;        // turbo [D]
+    float* out;               // [B][Hq][D]
+    float* ws_m;              // [B][Hq][P]
+    float* ws_l;              // [B][Hq][P]
+    float* ws_o;              // [B][Hq][P][D]
+    int64_t k_chunk;          // bytes per (page, KV head), K
+    int64_t v_chunk;          // bytes per (page, KV head), V
+    int32_t B, Hq, Hkv, g, D;
+    int32_t max_blocks, pool, max_ctx;
+    int32_t part_mode;        // PartMode
+    int32_t part_size;        // tokens per partition (split sequences)
+    int32_t P;                // partitions per sequence in the workspace / grid
+    int32_t kbits;            // turbo K index width (4 or 3)
+    float softmax_scale;
+    float softcap;
+};
+
+struct GatherParams {
+    const uint8_t* cache;
+    const float* scales;
+    const float* codebook;
+    const int32_t* bt;
+    float* out;
+    int64_t chunk;
+    int32_t fmt, is_v, Hkv, D, max_blocks, pool, seq, kv_head, t0, n, kbits;
+};
+
+// Launchers (kvd_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s);
+hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+
+}  // namespace kvd

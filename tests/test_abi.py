@@ -1,0 +1,123 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments on the
+host before anything is launched (no GPU needed: these paths make no HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvdecode.h")
+
+kvd = pytest.importorskip("quantized_kv_cache_split_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kvd_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"kvd_decode_attn_paged", "kvd_decode_partitions", "kvd_reduce_partitions",
+            "kvd_workspace_bytes", "kvd_dequant_gather", "kvd_status_str"} <= set(names)
+    lib = ctypes.CDLL(kvd.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def dims(**kw):
+    base = dict(num_seqs=16, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+                max_blocks_per_seq=2048, num_pool_blocks=33792, max_context_len=32768,
+                partition_size=0)
+    base.update(kw)
+    return kvd.Dims(**base)
+
+
+def test_workspace_bytes():
+    d = dims()
+    rows = 16 * 64 * 64
+    assert kvd.workspace_bytes(d) == 2 * rows * 4 + rows * 128 * 4
+    assert kvd.workspace_bytes(dims(max_context_len=1000)) == 0       # auto: never splits
+    assert kvd.workspace_bytes(dims(partition_size=-1)) == 0
+    assert kvd.workspace_bytes(dims(partition_size=128, max_context_len=300, num_seqs=1,
+                                    num_q_heads=4, num_kv_heads=1)) == 256 * 2 + 12 * 128 * 4
+    assert kvd.workspace_bytes(dims(head_dim=96)) == 0
+    assert kvd.workspace_bytes(dims(partition_size=100)) == 0
+
+
+def test_status_strings():
+    assert kvd.status_str(0) == "ok"
+    for s in range(-6, 0):
+        assert kvd.status_str(s) != "unknown status"
+
+
+FAKE = 1 << 20   # a 16-byte aligned, never dereferenced address
+
+
+def call(d=None, fmt=0, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, scales=FAKE, cb=FAKE, sign=FAKE,
+             scale=0.1, win=None, cap=0.0, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(over)
+    lib = kvd.load()
+    return lib.kvd_decode_attn_paged(ctypes.byref(d or dims()), a["q"], a["k"], a["v"], a["bt"],
+                                     a["ctx"], fmt, a["scales"], a["cb"], a["sign"], a["scale"],
+                                     a["win"], a["cap"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("field,value", [("num_q_heads", 60), ("num_kv_heads", 0),
+                                         ("head_dim", 96), ("block_size", 32),
+                                         ("max_context_len", 0), ("max_context_len", 1 << 20),
+                                         ("partition_size", 100), ("num_q_heads", 8 * 17)])
+def test_shape_errors(field, value):
+    assert call(dims(**{field: value})) == -2
+
+
+def test_turbo_needs_d128():
+    assert call(dims(head_dim=64), fmt=2) == -2
+
+
+def test_format_error():
+    assert call(fmt=7) == -3
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "bt", "ctx", "out"])
+def test_null_errors(arg):
+    assert call(**{arg: None}) == -1
+
+
+def test_fp8_and_turbo_need_their_arrays():
+    assert call(fmt=1, scales=None) == -1
+    assert call(fmt=2, cb=None) == -1
+    assert call(fmt=3, sign=None) == -1
+    assert call(fmt=0, scales=None, cb=None, sign=None, ws_bytes=0) == -5
+
+
+def test_alignment_errors():
+    assert call(q=FAKE + 2) == -4
+    assert call(ws=FAKE + 16) == -4
+
+
+def test_workspace_errors():
+    assert call(ws=None) == -5
+    assert call(ws_bytes=100) == -5
+
+
+def test_bad_scalars():
+    assert call(cap=-1.0) == -2
+    assert call(scale=float("nan")) == -2
+
+
+def test_empty_batch_is_ok_without_launching():
+    assert call(dims(num_seqs=0)) == 0
+
+
+def test_gather_arg_errors():
+    lib = kvd.load()
+    d = dims()
+    g = lambda **k: lib.kvd_dequant_gather(ctypes.byref(d), k.get("fmt", 0), 0, FAKE, FAKE, FAKE,
+                                           FAKE, k.get("seq", 0), k.get("head", 0),
+                                           k.get("t0", 0), k.get("n", 4), FAKE, None)
+    assert g(seq=16) == -2 and g(head=8) == -2 and g(t0=-1) == -2 and g(t0=32768, n=1) == -2
+    assert g(fmt=9) == -3
+    assert g(n=0) == 0

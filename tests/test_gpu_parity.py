@@ -1,0 +1,242 @@
+"""GPU parity: the HIP library (through the C ABI) against the fp64 oracle on seeded inputs.
+
+Bar: bit-exact for gathering / dequantised values and for identities that are exact in the
+kernel's arithmetic; max abs error <= 2e-3 and row-normwise relative error <= 1e-2 for the
+fp32-accumulated attention output.  Spare pages and tail slots are NaN-poisoned in every batch,
+so any read outside the attended range that reaches the arithmetic shows up.
+"""
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+from conftest import oracle_args
+from gpu_harness import GpuBatch, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _oracle(inp, window=True):
+    return oracle.decode_attention(*oracle_args(inp, window))
+
+
+def _small(fmt, **kw):
+    base = dict(fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2, pool_total=None)
+    base.update(kw)
+    return kvgen.make_inputs(kvgen.spec("c1", **base))
+
+
+# --------------------------------------------------------------------------------------------
+# gather / dequant: bit-exact
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("which", ["k", "v"])
+def test_dequant_gather_bit_exact(fmt, which):
+    import torch
+    inp = _small(fmt, num_seqs=2, context=None, ctx_range=(40, 77))
+    gb = GpuBatch(inp)
+    s = inp.spec
+    for b in range(s.num_seqs):
+        for hk in range(s.num_kv_heads):
+            L = int(inp.context_lens[b])
+            out = torch.full((L, s.head_dim), float("nan"), device="cuda:0")
+            gb.kvd.dequant_gather(gb.dims, fmt, which == "v",
+                                  gb.t["v_cache" if which == "v" else "k_cache"], gb.t["scales"],
+                                  gb.t["codebook"], gb.t["block_table"], b, hk, 0, L, out)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            want = oracle.dequant_gather(fmt, which, inp.v_cache if which == "v" else inp.k_cache,
+                                         inp.scales, inp.codebook, inp.block_table[b], hk, 0, L,
+                                         s.head_dim)
+            assert got.dtype == want.dtype == np.float32
+            assert (got.view(np.uint32) == want.view(np.uint32)).all(), (b, hk)
+
+
+def test_fp8_all_codes_decode_exactly():
+    """Every E4M3FN code (NaNs included) through the kernel's FP8 decode."""
+    import torch
+    inp = _small("fp8", num_seqs=1, context=16, num_kv_heads=1, num_q_heads=4)
+    phys = int(inp.block_table[0, 0])
+    codes = (np.arange(inp.k_cache.shape[-1]) * 7 % 256).astype(np.uint8)
+    inp.k_cache[phys, 0] = codes
+    inp.v_cache[phys, 0] = codes[::-1]
+    inp.scales[...] = np.float32(0.37)
+    gb = GpuBatch(inp)
+    for which, cache in (("k", inp.k_cache), ("v", inp.v_cache)):
+        out = torch.empty((16, 128), device="cuda:0")
+        gb.kvd.dequant_gather(gb.dims, "fp8", which == "v", gb.t[which + "_cache"], gb.t["scales"],
+                              None, gb.t["block_table"], 0, 0, 0, 16, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = oracle.dequant_gather("fp8", which, cache, inp.scales, None, inp.block_table[0], 0,
+                                     0, 16, 128)
+        assert (np.isnan(got) == np.isnan(want)).all()
+        ok = ~np.isnan(want)
+        assert (got[ok].view(np.uint32) == want[ok].view(np.uint32)).all()
+        assert len(set(cache[phys, 0].tolist())) == 256
+
+
+# --------------------------------------------------------------------------------------------
+# the tiny config: single partition, explicit 3-way split (128), forced single, auto
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("ps", [0, 128, -1, 16])
+def test_c1_tiny(ps):
+    inp = kvgen.make_inputs(kvgen.SPECS["c1"])
+    ref = _oracle(inp)
+    gpu = GpuBatch(inp, partition_size=ps).run()
+    assert_close(gpu, ref, f"c1 ps={ps}")
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("L", [1, 2, 15, 16, 17, 31, 33, 300, 1023, 1024, 1500])
+def test_formats_lengths(fmt, L):
+    inp = _small(fmt, context=L, num_seqs=2, seed=L)
+    ref = _oracle(inp)
+    gpu = GpuBatch(inp).run()
+    assert_close(gpu, ref, f"{fmt} L={L}")
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("hq,hkv", [(1, 1), (2, 1), (16, 1), (12, 4), (32, 4)])
+def test_gqa_groups(fmt, hq, hkv):
+    inp = _small(fmt, num_q_heads=hq, num_kv_heads=hkv, context=700, num_seqs=2)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} g={hq // hkv}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_head_dim_64(fmt):
+    inp = _small(fmt, head_dim=64, context=None, ctx_range=(1, 2500), num_seqs=4)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} D=64")
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_ragged_window_softcap(fmt):
+    """The ragged long-context recipe (lengths U{1..}, window on half, cap 50) at small size."""
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=8, num_q_heads=8, num_kv_heads=2,
+                                       ctx_range=(1, 6000), window=1500),
+                            poison_before_window=True)
+    assert (inp.window > 0).sum() == 4
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} ragged+window+cap")
+
+
+def test_large_logits_softcap():
+    inp = _small("bf16", context=2000, softmax_scale=1.0, softcap=5.0)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), "cap 5, scale 1")
+
+
+@pytest.mark.parametrize("ps", [0, -1, 32, 128, 512, 1024])
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_partition_sizes_agree(fmt, ps):
+    inp = _small(fmt, context=None, ctx_range=(1, 3000), num_seqs=3)
+    assert_close(GpuBatch(inp, partition_size=ps).run(), _oracle(inp), f"{fmt} ps={ps}")
+
+
+# --------------------------------------------------------------------------------------------
+# structure: permutation invariance, poison, identities, partials, error rows
+# --------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_page_permutation_bit_identical(fmt):
+    inp = _small(fmt, context=None, ctx_range=(100, 2600), num_seqs=3)
+    a = GpuBatch(inp).run()
+    b = GpuBatch(kvgen.relayout(inp, 11)).run()
+    assert (a.view(np.uint64) == b.view(np.uint64)).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("L,W", [(300, 0), (300, 37), (3000, 1333), (1500, 0), (77, 100)])
+def test_position_coded_v(fmt, L, W):
+    """K = 0 and V[j][d] = bit d of j: out[d] = #{attended j with bit d set} / span."""
+    D = 128
+
+    def kv(seq, n):
+        j = np.arange(n)
+        return (np.zeros((1, n, D), np.float32),
+                ((j[None, :, None] >> np.arange(D)[None, None, :]) & 1).astype(np.float32))
+
+    inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=D, pool_total=None), lengths=[L],
+                            windows=[W], kv_override=kv, fp8_scale=np.ones((2, 1), np.float32))
+    gpu = GpuBatch(inp).run()[0]
+    lo = max(0, L - W) if W else 0
+    j = np.arange(lo, L)
+    want = np.array([((j >> d) & 1).sum() for d in range(D)]) / (L - lo)
+    assert np.abs(gpu - want[None, :]).max() < 1e-6
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_single_token_exact(fmt):
+    inp = _small(fmt, context=1, num_seqs=3)
+    gpu = GpuBatch(inp).run()
+    s = inp.spec
+    for b in range(3):
+        for h in range(s.num_q_heads):
+            hk = h // s.group
+            v0 = oracle.dequant_gather(fmt, "v", inp.v_cache, inp.scales, None, inp.block_table[b],
+                                       hk, 0, 1, s.head_dim)[0]
+            assert (gpu[b, h].astype(np.float32) == v0).all()
+
+
+def test_uniform_v():
+    D = 128
+    inp = kvgen.make_inputs(kvgen.spec("c1", head_dim=D, pool_total=None, context=5000),
+                            kv_override=lambda s, n: (np.random.default_rng(3).standard_normal((1, n, D)).astype(np.float32),
+                                                      np.full((1, n, D), -1.25, np.float32)))
+    gpu = GpuBatch(inp).run()
+    assert np.abs(gpu + 1.25).max() < 1e-5
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_partials_match_oracle(fmt):
+    inp = _small(fmt, context=None, ctx_range=(200, 700), num_seqs=2)
+    gb = GpuBatch(inp, partition_size=128)
+    gb.run_phase1()
+    m, l, o = gb.partials()
+    s = inp.spec
+    for b in range(s.num_seqs):
+        for hk in range(s.num_kv_heads):
+            parts = oracle.partition_partials(*oracle_args(inp), 128, b, hk, rotated=True)
+            for lo_, hi_, pm, pl, po in parts:
+                p = lo_ // 128
+                rows = slice(hk * s.group, hk * s.group + s.group)
+                m_nat = m[b, rows, p].astype(np.float64) * np.log(2.0)
+                # BF16/FP8 logits are exact bf16 products summed in fp32.  The codebook formats
+                # feed fp16 operands (query and level each rounded to 11 significant bits), so
+                # |dz| <= 2^-10 * scale * |q| * max_t |k_t|  (Cauchy-Schwarz).
+                tol = 1e-4
+                if fmt.startswith("turbo"):
+                    kk = oracle.gather_kv(fmt, "k", inp.k_cache, inp.block_table[b], hk, lo_, hi_,
+                                          s.head_dim, scales=inp.scales, codebook=inp.codebook,
+                                          sign=inp.sign)
+                    qn = np.linalg.norm(oracle.bf16_to_f64(inp.q[b, rows]), axis=1)
+                    tol = 2.0 ** -10 * float(inp.softmax_scale) * qn * np.linalg.norm(kk, axis=1).max()
+                assert (np.abs(m_nat - pm) <= tol).all(), (np.abs(m_nat - pm), tol)
+                lse_gpu = m_nat + np.log(l[b, rows, p].astype(np.float64))
+                assert (np.abs(lse_gpu - (pm + np.log(pl))) <= 2 * tol + 1e-6).all()
+                assert_close(o[b, rows, p].astype(np.float64), po, f"{fmt} partial b{b} h{hk} p{p}")
+
+
+def test_zero_length_and_bad_rows():
+    inp = _small("bf16", num_seqs=4, context=None, ctx_range=(50, 2000))
+    inp.context_lens[1] = 0
+    inp.block_table[2, 1] = inp.num_pool_blocks + 5        # out of the pool
+    inp.block_table[3, 0] = -1
+    gb = GpuBatch(inp)
+    gpu = gb.run()
+    assert (gpu[1] == 0).all()
+    assert np.isnan(gpu[2]).all() and np.isnan(gpu[3]).all()
+    ref = oracle.decode_attention(*oracle_args(inp), seqs=[0])     # the healthy sequence only
+    assert_close(gpu[0:1], ref[0:1], "row next to error rows")
+
+
+def test_context_above_bound_gives_nan():
+    inp = _small("fp8", num_seqs=2, context=64)
+    gb = GpuBatch(inp)
+    gb.t["context_lens"][1] = 10 ** 6
+    gpu = gb.run()
+    assert np.isnan(gpu[1]).all() and np.isfinite(gpu[0]).all()
