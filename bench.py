@@ -4,8 +4,9 @@ One "step" is one full decode-attention call (partition kernel + LSE reduce) ove
 batch already resident in HBM.  The default workload is the FP8-E4M3 cache at 32K context
 (16 sequences, 64 query / 8 KV heads, head_dim 128, 512-token partitions).  Every step is
 timed with HIP events on the stream the kernels run on: one event pair around the partition
-kernel, one around the whole call; a 512 MiB buffer is rewritten between steps (outside the
-events) so the 256 MB Infinity Cache holds no KV from the step before.
+kernel, one around the whole call.  Between steps (outside the events) a 512 MiB buffer is
+read, which evicts the 256 MB Infinity Cache without leaving dirty lines behind: a rewrite
+would leave its write-backs to land inside the next timed call.
 
 Prints ONE JSON line.  `value` = algorithmic KV bytes per call / mean call time.
 `roofline` = the partition kernel's algorithmic bytes / its mean duration against 8 TB/s.
@@ -110,7 +111,12 @@ def main():
                       device=dev)
     nws = kvd.workspace_bytes(dims)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) if nws else None
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    sink = torch.empty(1, dtype=torch.int64, device=dev)
+
+    def evict():   # read 512 MiB (no dirty lines), outside the timed events
+        if flush is not None:
+            torch.sum(flush, dim=0, keepdim=True, out=sink)
     call_args = (dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
                  spec.fmt, t["scales"], t["codebook"], t["sign_pattern"],
                  float(inp.softmax_scale), t["window"], float(inp.softcap), out, ws)
@@ -128,8 +134,7 @@ def main():
         ev[2].record()
 
     for _ in range(args.warmup):
-        if flush is not None:
-            flush.fill_(1)
+        evict()
         step()
     torch.cuda.synchronize()
 
@@ -137,8 +142,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        evict()
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall

@@ -141,7 +141,9 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (phases & kPhase1) {
-        const dim3 grid(pl.P ? pl.P : 1, d->num_kv_heads, d->num_seqs);
+        // one wave per partition, four partitions per workgroup
+        const int px = pl.P ? (pl.P + 3) / 4 : 1;
+        const dim3 grid(px, d->num_kv_heads, d->num_seqs);
         e = kvd::launch_partitions(fmt, p, grid, s);
         if (e != hipSuccess) return KVD_ERR_HIP;
     }

@@ -4,21 +4,25 @@
 // reduce"; 512-token partitions; fp32 per-partition max, sum and output) and the attention.rs
 // README (Split-K decode for every cache format from 1024 tokens on, one shared float reduce):
 //
-//   partition_kernel<FMT, D>  one workgroup (4 waves) per (partition, KV head, sequence).
-//       Each wave walks pairs of 16-token pages.  Per pair it
-//         - loads K and V of both pages with 16-byte (or narrower, for the packed V rows)
-//           coalesced loads straight into MFMA operand registers;
-//         - computes S^T = K Q^T for the 32 tokens x 16 query slots (the GQA group, zero
-//           padded) with v_mfma_f32_16x16x32_{bf16,f16}, dequantising FP8 / codebook indices
-//           in registers on the way (FP8 -> bf16 is exact; codebook levels come from a 16-entry
-//           fp16 table in LDS);
-//         - runs an fp32 online softmax in the base-2 domain (max across the four 16-lane
-//           groups by cross-lane shuffles);
-//         - accumulates O^T += V^T P^T with the same MFMA, P fed as bf16 hi + lo halves (BF16,
-//           FP8: ~2^-16 relative) or as fp16 p * vnorm / running-max(vnorm) (codebook formats).
+//   partition_kernel<FMT, D, CAP>  one workgroup (4 waves) per (partition, KV head, sequence).
+//       Each wave walks pairs of 16-token pages, software-pipelined: while it computes pair k
+//       its loads for pair k+4 (the wave's next pair) are in flight, and the block-table
+//       entries of the pair after that are being fetched with scalar loads.  Per pair it
+//         - loads K and V of both pages straight into MFMA operand registers (16-byte loads
+//           for K; V rows are 32/16/8 bytes per 16-token row depending on the format);
+//         - computes S^T = K Q^T for 32 tokens x 16 query slots (the GQA group, zero padded)
+//           with v_mfma_f32_16x16x32_{bf16,f16}, dequantising in registers on the way: FP8 ->
+//           bf16 is exact; codebook levels come from a 16-entry LDS table;
+//         - runs an fp32 online softmax in the base-2 domain (the per-query max crosses the
+//           four 16-lane groups with two shuffles);
+//         - accumulates O^T += V^T P^T with the same MFMA shape.
+//       Operand precision: BF16 and FP8 caches use exact bf16 K/V/q operands and feed P as a
+//       bf16 hi + lo pair (2^-16 relative).  The codebook caches use fp16 operands split into
+//       hi + lo halves for the levels, the rotated query and P (three MFMAs per product,
+//       about 2^-20 relative), with power-of-two scalings that keep every fp16 value in range.
 //       The MFMA output layout of S^T (lane = query, 4 lane groups x 4 rows = 16 tokens) is
-//       exactly the B-operand layout of P^T for the PV product once the two pages are
-//       interleaved as below, so no data moves between the QK and PV products.
+//       exactly the B-operand layout of P^T for the PV product once the pair's two pages are
+//       interleaved as below, so no data moves between the two products.
 //       The four waves merge their (max, sum, output) through LDS; the workgroup writes its
 //       partition triple to the workspace, or the final row when the sequence is not split.
 //   reduce_kernel<FMT, D>    one workgroup per (query head, sequence): LSE merge of the
@@ -48,10 +52,27 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
+
+template <int FMT>
+constexpr bool is_turbo() { return FMT == KVD_TURBO4 || FMT == KVD_TURBO3; }
+template <int FMT, int D>
+constexpr int k_chunk() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
+template <int FMT, int D>
+constexpr int v_chunk() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : 8 * D; }
+// Vector memory instructions load_pair issues for one page pair.
+template <int FMT, int D>
+constexpr int loads_per_pair() {
+    return FMT == KVD_BF16 ? D / 16 + D / 16 : FMT == KVD_FP8_E4M3 ? D / 32 + D / 16
+         : FMT == KVD_TURBO4 ? 2 + 8 + 4 : 2 + 8 + 4;
+}
+// s_waitcnt immediate that waits until at most n vector memory loads are outstanding (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // ------------------------------------------------------------------------------------------
 // small helpers
@@ -67,9 +88,16 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ float wave_max16x(float v) {   // max over the 4 lane groups
-    v = fmaxf(v, __shfl_xor(v, 16));
-    return fmaxf(v, __shfl_xor(v, 32));
+// Max over the four 16-lane groups (rows) of a wave, returned in every lane.  gfx950's
+// permlane swaps exchange rows 1<->0, 3<->2 (16) and rows 2,3<->0,1 (32) in registers, without
+// LDS traffic.
+__device__ __forceinline__ float max_over_groups(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t w = __float_as_uint(m1);
+    const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 
 // 4 E4M3FN codes (little-endian bytes of w) -> 4 bf16 in two packed pairs.  Exact: every
@@ -80,25 +108,28 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// 8 4-bit indices (index e at bits 4e of w) -> 8 fp16 table values as 4 packed pairs.
-__device__ __forceinline__ u32x4 lut_nib8(const _Float16* lut, uint32_t w) {
-    u32x4 r;
+// Codebook table entries hold the fp16 hi part in bits 0..15 and the fp16 lo part in bits
+// 16..31 of one dword.  8 table entries -> the hi operand and the lo operand (4 pairs each).
+__device__ __forceinline__ void split_pairs(const uint32_t (&r)[8], u32x4& hi, u32x4& lo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f16x2 h = {lut[(w >> (8 * i)) & 15u], lut[(w >> (8 * i + 4)) & 15u]};
-        r[i] = __builtin_bit_cast(uint32_t, h);
+        hi[i] = (r[2 * i] & 0xFFFFu) | (r[2 * i + 1] << 16);
+        lo[i] = (r[2 * i] >> 16) | (r[2 * i + 1] & 0xFFFF0000u);
     }
-    return r;
 }
-// 8 3-bit indices (index e at bits 3e of the low 24 bits of f) -> 8 fp16 table values.
-__device__ __forceinline__ u32x4 lut_tri8(const _Float16* lut, uint32_t f) {
-    u32x4 r;
+// 8 4-bit indices (index e at bits 4e of w) -> hi / lo fp16 operands.
+__device__ __forceinline__ void lut_nib8(const uint32_t* lut, uint32_t w, u32x4& hi, u32x4& lo) {
+    uint32_t r[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f16x2 h = {lut[(f >> (6 * i)) & 7u], lut[(f >> (6 * i + 3)) & 7u]};
-        r[i] = __builtin_bit_cast(uint32_t, h);
-    }
-    return r;
+    for (int e = 0; e < 8; ++e) r[e] = lut[(w >> (4 * e)) & 15u];
+    split_pairs(r, hi, lo);
+}
+// 8 3-bit indices (index e at bits 3e of the low 24 bits of f) -> hi / lo fp16 operands.
+__device__ __forceinline__ void lut_tri8(const uint32_t* lut, uint32_t f, u32x4& hi, u32x4& lo) {
+    uint32_t r[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = lut[(f >> (3 * e)) & 7u];
+    split_pairs(r, hi, lo);
 }
 // The 24-bit field holding indices 8h..8h+7 of a 32-index, 3-bit group (w0..w2 = its 12 bytes).
 __device__ __forceinline__ uint32_t tri_field(uint32_t w0, uint32_t w1, uint32_t w2, int h) {
@@ -108,6 +139,14 @@ __device__ __forceinline__ uint32_t tri_field(uint32_t w0, uint32_t w1, uint32_t
         case 2: return (w1 >> 16) | (w2 << 16);
         default: return w2 >> 8;
     }
+}
+
+// fp32 pair -> (hi, lo) fp16 pairs with x ~= hi + lo.
+__device__ __forceinline__ void f16_hilo(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const f16x2 h = {(_Float16)x0, (_Float16)x1};
+    const f16x2 l = {(_Float16)(x0 - (float)h[0]), (_Float16)(x1 - (float)h[1])};
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 // Power of two 2^-e with max_abs * 2^-e in [0.5, 1) (1 when max_abs is 0 or not finite).
@@ -143,8 +182,9 @@ struct SeqInfo {
 // Attended range [lo, L) of sequence b and whether it is split into partitions.
 __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
     SeqInfo s;
-    int L = p.ctx[b];
-    const int W = p.win ? p.win[b] : 0;
+    // one value per workgroup: keep it in scalar registers so loops over it stay uniform
+    int L = __builtin_amdgcn_readfirstlane(p.ctx[b]);
+    const int W = p.win ? __builtin_amdgcn_readfirstlane(p.win[b]) : 0;
     s.bad = (L < 0) || (L > p.max_ctx) || (W < 0);
     if (s.bad) L = 0;
     s.L = L;
@@ -156,58 +196,157 @@ __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
 }
 
 // ------------------------------------------------------------------------------------------
+// per-format raw registers of one page pair, as loaded from HBM
+// ------------------------------------------------------------------------------------------
+template <int FMT, int D> struct PairRaw;
+template <int D> struct PairRaw<KVD_BF16, D> {      // K [D/8][16][8], V [D][16] bf16
+    u32x4 kx[D / 32], ky[D / 32];
+    u32x4 v[D / 16];
+};
+template <int D> struct PairRaw<KVD_FP8_E4M3, D> {  // K [D/16][16][16], V [D][16] bytes
+    u32x4 kx[D / 64], ky[D / 64];
+    u32x2 v[D / 16];
+};
+template <> struct PairRaw<KVD_TURBO4, 128> {       // K [4][16][16 B], V [128][8 B], norms
+    u32x4 kx, ky;
+    uint32_t v[8];
+    f32x4 kn0, kn1, vn0, vn1;
+};
+template <> struct PairRaw<KVD_TURBO3, 128> {       // K [4][16][12 B], V [128][8 B], norms
+    uint32_t kx[3], ky[3];
+    uint32_t v[8];
+    f32x4 kn0, kn1, vn0, vn1;
+};
+
+// Per-lane placement of the pair's tokens (see the header comment).
+struct LaneMap {
+    int n, j;
+    int a_sel, a_pos;    // QK A row n: page (0 = A, 1 = B) and slot of its tile-X token
+    int v_sel, v_pos0;   // softmax / PV group j: page and first of its eight slots
+};
+
+template <int FMT, int D>
+__device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams& p,
+                                          const LaneMap& ln, size_t headA, size_t headB) {
+    const uint8_t* kch = p.k + (ln.a_sel ? headB : headA) * (size_t)k_chunk<FMT, D>();
+    const uint8_t* vch = p.v + (ln.v_sel ? headB : headA) * (size_t)v_chunk<FMT, D>();
+    if constexpr (FMT == KVD_BF16) {
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {   // x-vector 4s + j of the lane's tokens
+            const uint8_t* base = kch + 1024 * s + 256 * ln.j + 16 * ln.a_pos;
+            r.kx[s] = *reinterpret_cast<const u32x4*>(base);
+            r.ky[s] = *reinterpret_cast<const u32x4*>(base + 64);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+            r.v[i] = *reinterpret_cast<const u32x4*>(vch + (16 * i + ln.n) * 32 + 2 * ln.v_pos0);
+    } else if constexpr (FMT == KVD_FP8_E4M3) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {   // x-vector 4i + j (16 codes)
+            const uint8_t* base = kch + 1024 * i + 256 * ln.j + 16 * ln.a_pos;
+            r.kx[i] = *reinterpret_cast<const u32x4*>(base);
+            r.ky[i] = *reinterpret_cast<const u32x4*>(base + 64);
+        }
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i)
+            r.v[i] = *reinterpret_cast<const u32x2*>(vch + (16 * i + ln.n) * 16 + ln.v_pos0);
+    } else {
+        if constexpr (FMT == KVD_TURBO4) {   // 32-index group j of the lane's tokens
+            const uint8_t* base = kch + 256 * ln.j + 16 * ln.a_pos;
+            r.kx = *reinterpret_cast<const u32x4*>(base);
+            r.ky = *reinterpret_cast<const u32x4*>(base + 64);
+        } else {
+            const uint32_t* bx = reinterpret_cast<const uint32_t*>(kch + 192 * ln.j + 12 * ln.a_pos);
+            const uint32_t* by = reinterpret_cast<const uint32_t*>(kch + 192 * ln.j + 12 * (ln.a_pos + 4));
+#pragma unroll
+            for (int w = 0; w < 3; ++w) { r.kx[w] = bx[w]; r.ky[w] = by[w]; }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r.v[i] = *reinterpret_cast<const uint32_t*>(vch + (16 * i + ln.n) * 8 + ln.v_pos0 / 2);
+        const size_t nb = (ln.v_sel ? headB : headA) * kPageTokens + ln.v_pos0;
+        const size_t voff = (size_t)p.pool * p.Hkv * kPageTokens;
+        r.kn0 = *reinterpret_cast<const f32x4*>(p.scales + nb);
+        r.kn1 = *reinterpret_cast<const f32x4*>(p.scales + nb + 4);
+        r.vn0 = *reinterpret_cast<const f32x4*>(p.scales + voff + nb);
+        r.vn1 = *reinterpret_cast<const f32x4*>(p.scales + voff + nb + 4);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-template <int FMT, int D>
+// Grid (ceil(P / 4), Hkv, B), 4 waves.  For a split sequence wave w of workgroup x owns
+// partition 4x + w on its own and writes that partition's triple straight from registers.
+// For an unsplit sequence (workgroup 0 only) the four waves share the attended range
+// (consecutive quarters of its page pairs) and merge through LDS.
+template <int FMT, int D, bool CAP, int PF>
 __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchParams p) {
-    constexpr bool kTurbo = (FMT == KVD_TURBO4 || FMT == KVD_TURBO3);
+    constexpr bool kTurbo = is_turbo<FMT>();
     constexpr int KS = D / 32;   // QK MFMA steps (k = 32 head elements each)
     constexpr int VT = D / 16;   // PV MFMA tiles (16 head elements each)
     static_assert(!kTurbo || D == 128, "codebook formats are built for head_dim 128");
+    using Raw = PairRaw<FMT, D>;
 
     __shared__ float sm_m[kWaves][kMaxGroup];
     __shared__ float sm_l[kWaves][kMaxGroup];
     __shared__ float sm_o[kWaves][kMaxGroup][D];
     __shared__ float sm_row[kTurbo ? kMaxGroup * D : 1];   // query rotation / output rotation
     __shared__ float sm_rowscale[kMaxGroup];
-    __shared__ _Float16 sm_lut[2][16];
+    __shared__ uint32_t sm_lut[2][16];
     __shared__ float sm_lutscale[2];
 
-    const int part = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, j = lane >> 4;
+    const int xb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = p.g;
     const SeqInfo si = seq_info(p, b);
     float* out_rows = p.out + ((size_t)b * p.Hq + (size_t)hk * g) * D;
 
     if (si.bad || si.L == 0) {
-        if (part == 0) {
+        if (xb == 0) {
             const float v = si.bad ? __builtin_nanf("") : 0.0f;
             for (int i = tid; i < g * D; i += kThreads) out_rows[i] = v;
         }
         return;
     }
-    int lo, hi;
-    if (!si.split) {
-        if (part != 0) return;
-        lo = si.lo;
-        hi = si.L;
-    } else {
+    // token range [lo, hi) of this wave (uniform per workgroup: whether any wave has work)
+    int lo, hi, part = 0;
+    if (si.split) {
+        if (xb * kWaves * p.part_size >= si.L) return;
+        part = xb * kWaves + wave;
         lo = max(si.lo, part * p.part_size);
         hi = min(si.L, (part + 1) * p.part_size);
-        if (lo >= hi) return;
+    } else {
+        if (xb != 0) return;
+        const int pg0 = si.lo / kPageTokens, pg1 = (si.L - 1) / kPageTokens + 1;
+        const int np = (pg1 - pg0 + 1) >> 1;
+        const int per = (np + kWaves - 1) / kWaves;
+        lo = max(si.lo, (pg0 + 2 * per * wave) * kPageTokens);
+        hi = min(si.L, (pg0 + 2 * per * (wave + 1)) * kPageTokens);
     }
+    const bool live = lo < hi;
+
+    LaneMap ln;
+    ln.n = lane & 15;
+    ln.j = lane >> 4;
+    ln.a_sel = ln.n >> 3;
+    ln.a_pos = 8 * ((ln.n >> 2) & 1) + (ln.n & 3);
+    ln.v_sel = ln.j >> 1;
+    ln.v_pos0 = 8 * (ln.j & 1);
+    const int n = ln.n, j = ln.j;
 
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
-    const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)hk * g + qn) * D;
     u32x4 qop[KS];
+    u32x4 qlo[kTurbo ? KS : 1];
     float zscale;           // logit -> base-2 softmax argument (without per-token factors)
     float oscale = 1.0f;    // accumulator -> output units (FP8 V scale / codebook scales)
 
     if constexpr (kTurbo) {
-        // codebook tables (fp16, scaled by a power of two so the largest level is in [0.5, 1))
+        // codebook tables: fp16 hi | lo << 16, levels scaled by a power of two so the largest
+        // magnitude is in [0.5, 1)
         if (wave == 0) {
             const int kl = 1 << p.kbits;
             const int which = lane >> 4, idx = lane & 15;
@@ -220,7 +359,9 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             mx = fmaxf(mx, __shfl_xor(mx, 4));
             mx = fmaxf(mx, __shfl_xor(mx, 8));
             const float sc = pow2_normaliser(mx);
-            if (which < 2) sm_lut[which][idx] = (_Float16)(c * sc);
+            uint32_t h, l;
+            f16_hilo(c * sc, 0.0f, h, l);
+            if (which < 2) sm_lut[which][idx] = (h & 0xFFFFu) | (l << 16);
             if (which < 2 && idx == 0) sm_lutscale[which] = sc;
         }
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
@@ -242,18 +383,18 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = 32 * j + 8 * s;
-            u32x4 w;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f16x2 h = {(_Float16)(sm_row[qn * D + d0 + 2 * i] * qs),
-                           (_Float16)(sm_row[qn * D + d0 + 2 * i + 1] * qs)};
-                w[i] = qlive ? __builtin_bit_cast(uint32_t, h) : 0u;
+                uint32_t h, l;
+                f16_hilo(sm_row[qn * D + d0 + 2 * i] * qs, sm_row[qn * D + d0 + 2 * i + 1] * qs, h, l);
+                qop[s][i] = qlive ? h : 0u;
+                qlo[s][i] = qlive ? l : 0u;
             }
-            qop[s] = w;
         }
         zscale = p.softmax_scale * kLog2e / (qs * sm_lutscale[0] * sqrtf((float)D));
         oscale = 1.0f / sm_lutscale[1];
     } else {
+        const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)hk * g + qn) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = (FMT == KVD_BF16) ? 32 * s + 8 * j : 64 * (s / 2) + 16 * j + 8 * (s % 2);
@@ -266,18 +407,10 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             oscale = p.scales[p.Hkv + hk];
         }
     }
-    const bool capped = p.softcap > 0.0f;
-    const float inv_cap = capped ? 1.0f / p.softcap : 0.0f;
+    const float cap_l2 = CAP ? p.softcap * kLog2e : 0.0f;      // cap in base-2 units
+    const float inv_cap_l2 = CAP ? 1.0f / cap_l2 : 0.0f;
 
-    // ---- main loop over page pairs -------------------------------------------------------
-    const int pg0 = lo / kPageTokens, pg1 = (hi - 1) / kPageTokens + 1;
-    const int npairs = (pg1 - pg0 + 1) >> 1;
-    const int32_t* btrow = p.bt + (size_t)b * p.max_blocks;
-    const int a_sel = n >> 3;                              // QK A row n: page of its token
-    const int a_pos = 8 * ((n >> 2) & 1) + (n & 3);        // slot of its tile-X token
-    const int v_sel = j >> 1;                              // PV / softmax: page of group j
-    const int v_pos0 = 8 * (j & 1);                        // first slot of group j
-
+    // ---- state -------------------------------------------------------------------------
     f32x4 oacc[VT];
 #pragma unroll
     for (int i = 0; i < VT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -285,132 +418,92 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     float sig_run = 1.17549435e-38f;   // running max of V norms (codebook formats)
     bool bad_ids = false;
 
-#pragma unroll 1
-    for (int k = wave; k < npairs; k += kWaves) {
-        const int pgA = pg0 + 2 * k, pgB = pgA + 1;
-        const bool hasB = pgB < pg1;
-        int physA = btrow[pgA];
-        int physB = hasB ? btrow[pgB] : physA;
-        if (physA < 0 || physA >= p.pool) { bad_ids = true; physA = 0; }
-        if (physB < 0 || physB >= p.pool) { bad_ids = true; physB = 0; }
-        const bool full = (pgA * kPageTokens >= lo) && hasB && ((pgB + 1) * kPageTokens <= hi);
+    const int pg0 = live ? lo / kPageTokens : 0, pg1 = live ? (hi - 1) / kPageTokens + 1 : 1;
+    const int npairs = live ? (pg1 - pg0 + 1) >> 1 : 0;
+    const_i32_ptr btrow = (const_i32_ptr)(p.bt + (size_t)b * p.max_blocks);
 
-        const size_t headA = (size_t)physA * p.Hkv + hk, headB = (size_t)physB * p.Hkv + hk;
-        const uint8_t* kch = p.k + (a_sel ? headB : headA) * p.k_chunk;
-        const uint8_t* vch = p.v + (v_sel ? headB : headA) * p.v_chunk;
+    // physical pages of pair k (scalar loads; a missing second page reads the first page's
+    // row, which the mask then hides; ids outside the pool are clamped and flagged)
+    auto fetch_ids = [&](int k, int& pa, int& pb) {
+        const int pgA = pg0 + 2 * k;
+        pa = btrow[pgA];
+        pb = btrow[min(pgA + 1, pg1 - 1)];
+    };
+    auto heads = [&](int pa, int pb, size_t& ha, size_t& hb) {
+        if (pa < 0 || pa >= p.pool) { bad_ids = true; pa = 0; }
+        if (pb < 0 || pb >= p.pool) { bad_ids = true; pb = 0; }
+        ha = (size_t)pa * p.Hkv + hk;
+        hb = (size_t)pb * p.Hkv + hk;
+    };
 
-        // ---- QK: S^T tiles X and Y ----
+    // ---- one pair: logits, online softmax, PV ------------------------------------------
+    // A pair index at or past npairs is a no-op: its token window is empty, so every logit
+    // is -inf, p = 0, alpha = 1 and the V operands are zero.
+    auto compute = [&](const Raw& r, int k) {
+        const int pgA = pg0 + 2 * min(k, npairs - 1);
+        const bool hasB = pgA + 1 < pg1;
+        const int hi_k = k < npairs ? hi : lo;
+        const bool full = (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
+
         f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == KVD_BF16) {
-            u32x4 kx[KS], ky[KS];
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const uint8_t* base = kch + 1024 * s + 256 * j + 16 * a_pos;
-                kx[s] = *reinterpret_cast<const u32x4*>(base);
-                ky[s] = *reinterpret_cast<const u32x4*>(base + 64);
-            }
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                sx = mfma_bf16(kx[s], qop[s], sx);
-                sy = mfma_bf16(ky[s], qop[s], sy);
+                sx = mfma_bf16(r.kx[s], qop[s], sx);
+                sy = mfma_bf16(r.ky[s], qop[s], sy);
             }
         } else if constexpr (FMT == KVD_FP8_E4M3) {
-            u32x4 kx[KS / 2], ky[KS / 2];
-#pragma unroll
-            for (int i = 0; i < KS / 2; ++i) {
-                const uint8_t* base = kch + 1024 * i + 256 * j + 16 * a_pos;
-                kx[i] = *reinterpret_cast<const u32x4*>(base);
-                ky[i] = *reinterpret_cast<const u32x4*>(base + 64);
-            }
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const int i = s / 2, h = s % 2;
-                const u32x2 ax0 = fp8x4_to_bf16(kx[i][2 * h]), ax1 = fp8x4_to_bf16(kx[i][2 * h + 1]);
-                const u32x2 ay0 = fp8x4_to_bf16(ky[i][2 * h]), ay1 = fp8x4_to_bf16(ky[i][2 * h + 1]);
+                const u32x2 ax0 = fp8x4_to_bf16(r.kx[i][2 * h]), ax1 = fp8x4_to_bf16(r.kx[i][2 * h + 1]);
+                const u32x2 ay0 = fp8x4_to_bf16(r.ky[i][2 * h]), ay1 = fp8x4_to_bf16(r.ky[i][2 * h + 1]);
                 sx = mfma_bf16(u32x4{ax0[0], ax0[1], ax1[0], ax1[1]}, qop[s], sx);
                 sy = mfma_bf16(u32x4{ay0[0], ay0[1], ay1[0], ay1[1]}, qop[s], sy);
             }
-        } else if constexpr (FMT == KVD_TURBO4) {
-            const uint8_t* base = kch + 256 * j + 16 * a_pos;
-            const u32x4 kx = *reinterpret_cast<const u32x4*>(base);
-            const u32x4 ky = *reinterpret_cast<const u32x4*>(base + 64);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                sx = mfma_f16(lut_nib8(sm_lut[0], kx[s]), qop[s], sx);
-                sy = mfma_f16(lut_nib8(sm_lut[0], ky[s]), qop[s], sy);
-            }
-        } else {  // KVD_TURBO3
-            const uint32_t* bx = reinterpret_cast<const uint32_t*>(kch + 192 * j + 12 * a_pos);
-            const uint32_t* by = reinterpret_cast<const uint32_t*>(kch + 192 * j + 12 * (a_pos + 4));
-            const uint32_t x0 = bx[0], x1 = bx[1], x2 = bx[2];
-            const uint32_t y0 = by[0], y1 = by[1], y2 = by[2];
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                sx = mfma_f16(lut_tri8(sm_lut[0], tri_field(x0, x1, x2, s)), qop[s], sx);
-                sy = mfma_f16(lut_tri8(sm_lut[0], tri_field(y0, y1, y2, s)), qop[s], sy);
-            }
-        }
-
-        // ---- V operand loads (A of the PV product): tile i, row d = 16 i + n ----
-        u32x4 vop[VT];
-        if constexpr (FMT == KVD_BF16) {
-#pragma unroll
-            for (int i = 0; i < VT; ++i)
-                vop[i] = *reinterpret_cast<const u32x4*>(vch + (16 * i + n) * 32 + 2 * v_pos0);
-        } else if constexpr (FMT == KVD_FP8_E4M3) {
-#pragma unroll
-            for (int i = 0; i < VT; ++i) {
-                const u32x2 w = *reinterpret_cast<const u32x2*>(vch + (16 * i + n) * 16 + v_pos0);
-                const u32x2 a0 = fp8x4_to_bf16(w[0]), a1 = fp8x4_to_bf16(w[1]);
-                vop[i] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-            }
         } else {
 #pragma unroll
-            for (int i = 0; i < VT; ++i) {
-                const uint32_t w = *reinterpret_cast<const uint32_t*>(vch + (16 * i + n) * 8 + v_pos0 / 2);
-                vop[i] = lut_nib8(sm_lut[1], w);
+            for (int s = 0; s < KS; ++s) {
+                u32x4 xh, xl, yh, yl;
+                if constexpr (FMT == KVD_TURBO4) {
+                    lut_nib8(sm_lut[0], r.kx[s], xh, xl);
+                    lut_nib8(sm_lut[0], r.ky[s], yh, yl);
+                } else {
+                    lut_tri8(sm_lut[0], tri_field(r.kx[0], r.kx[1], r.kx[2], s), xh, xl);
+                    lut_tri8(sm_lut[0], tri_field(r.ky[0], r.ky[1], r.ky[2], s), yh, yl);
+                }
+                sx = mfma_f16(xh, qop[s], sx);
+                sx = mfma_f16(xl, qop[s], sx);
+                sx = mfma_f16(xh, qlo[s], sx);
+                sy = mfma_f16(yh, qop[s], sy);
+                sy = mfma_f16(yl, qop[s], sy);
+                sy = mfma_f16(yh, qlo[s], sy);
             }
         }
 
-        // per-token factors (codebook formats): norms of group j's eight tokens
-        float kn[8], vn[8];
-        if constexpr (kTurbo) {
-            const size_t nbase = ((v_sel ? headB : headA) * kPageTokens + v_pos0);
-            const f32x4 k0 = *reinterpret_cast<const f32x4*>(p.scales + nbase);
-            const f32x4 k1 = *reinterpret_cast<const f32x4*>(p.scales + nbase + 4);
-            const size_t voff = (size_t)p.pool * p.Hkv * kPageTokens;
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(p.scales + voff + nbase);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(p.scales + voff + nbase + 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                kn[e] = k0[e]; kn[4 + e] = k1[e];
-                vn[e] = v0[e]; vn[4 + e] = v1[e];
-            }
-        }
-
-        // ---- logits, mask, online softmax ----
         float z[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { z[e] = sx[e]; z[4 + e] = sy[e]; }
+        for (int e = 0; e < 4; ++e) { z[e] = sx[e] * zscale; z[4 + e] = sy[e] * zscale; }
+        if constexpr (kTurbo) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = z[e] * zscale;
-            if constexpr (kTurbo) x *= kn[e];
-            if (capped) {   // cap * tanh(x_nat / cap), in the base-2 domain
-                const float y = x * (1.0f / kLog2e) * inv_cap;
-                const float t = fast_exp2(2.0f * kLog2e * y);
-                x = p.softcap * kLog2e * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
-            }
-            z[e] = x;
+            for (int e = 0; e < 4; ++e) { z[e] *= r.kn0[e]; z[4 + e] *= r.kn1[e]; }
         }
-        uint32_t vmask = 0xFFu;
-        if (!full) {
-            const int tok0 = (pgA + v_sel) * kPageTokens + v_pos0;
-            vmask = 0;
+        if constexpr (CAP) {   // cap * tanh(x / cap), evaluated in base-2 units
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float t = fast_exp2(2.0f * kLog2e * (z[e] * inv_cap_l2));
+                z[e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
+            }
+        }
+        // tokens outside [lo, hi) (and a missing second page) are selected out, never
+        // multiplied: their logits become -inf and their V operands zero
+        uint32_t vmask = 0;
+        {
+            const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = tok0 + e;
-                const bool ok = (t >= lo) && (t < hi) && (v_sel == 0 || hasB);
+                const bool ok = full || ((t >= lo) && (t < hi_k) && (ln.v_sel == 0 || hasB));
                 vmask |= (ok ? 1u : 0u) << e;
                 z[e] = ok ? z[e] : -INFINITY;
             }
@@ -418,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         float mloc = z[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, z[e]);
-        mloc = wave_max16x(mloc);
+        mloc = max_over_groups(mloc);
         const float m_new = fmaxf(m_run, mloc);
         const float alpha = fast_exp2(m_run - m_new);
         float pe[8], psum = 0.0f;
@@ -427,37 +520,46 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         l_run = l_run * alpha + psum;
         m_run = m_new;
 
-        // ---- P operand and PV ----
+        uint32_t mk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mk[i] = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
+                    (((vmask >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
+
         if constexpr (kTurbo) {
+            float vn[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { vn[e] = r.vn0[e]; vn[4 + e] = r.vn1[e]; }
             float vloc = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 vn[e] = ((vmask >> e) & 1u) ? vn[e] : 0.0f;
                 vloc = fmaxf(vloc, vn[e]);
             }
-            vloc = wave_max16x(vloc);
+            vloc = max_over_groups(vloc);
             const float sig_new = fmaxf(sig_run, vloc);
             const float f = alpha * (sig_run / sig_new);
             sig_run = sig_new;
             const float inv_sig = 1.0f / sig_new;
-            u32x4 pop;
+            u32x4 ph, pl;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                f16x2 h = {(_Float16)(pe[2 * i] * vn[2 * i] * inv_sig),
-                           (_Float16)(pe[2 * i + 1] * vn[2 * i + 1] * inv_sig)};
-                pop[i] = __builtin_bit_cast(uint32_t, h);
-            }
-            if (!full) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t mk = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
-                                        (((vmask >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
-#pragma unroll
-                    for (int t = 0; t < VT; ++t) vop[t][i] &= mk;
-                }
+                uint32_t h, l;
+                f16_hilo(pe[2 * i] * vn[2 * i] * inv_sig, pe[2 * i + 1] * vn[2 * i + 1] * inv_sig, h, l);
+                ph[i] = h;
+                pl[i] = l;
             }
 #pragma unroll
-            for (int t = 0; t < VT; ++t) oacc[t] = mfma_f16(vop[t], pop, oacc[t] * f);
+            for (int t = 0; t < VT; ++t) {
+                u32x4 vh, vl;
+                lut_nib8(sm_lut[1], r.v[t], vh, vl);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { vh[i] &= mk[i]; vl[i] &= mk[i]; }
+                f32x4 acc = oacc[t] * f;
+                acc = mfma_f16(vh, ph, acc);
+                acc = mfma_f16(vl, ph, acc);
+                oacc[t] = mfma_f16(vh, pl, acc);
+            }
         } else {
             u32x4 phi, plo;
 #pragma unroll
@@ -469,28 +571,88 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
                             (__bf16)(pe[2 * i + 1] - __uint_as_float(ch))};
                 plo[i] = __builtin_bit_cast(uint32_t, l);
             }
-            if (!full) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t mk = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
-                                        (((vmask >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
-#pragma unroll
-                    for (int t = 0; t < VT; ++t) vop[t][i] &= mk;
-                }
-            }
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
+                u32x4 vop;
+                if constexpr (FMT == KVD_BF16) {
+                    vop = r.v[t];
+                } else {
+                    const u32x2 a0 = fp8x4_to_bf16(r.v[t][0]), a1 = fp8x4_to_bf16(r.v[t][1]);
+                    vop = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vop[i] &= mk[i];
                 f32x4 acc = oacc[t] * alpha;
-                acc = mfma_bf16(vop[t], phi, acc);
-                oacc[t] = mfma_bf16(vop[t], plo, acc);
+                acc = mfma_bf16(vop, phi, acc);
+                oacc[t] = mfma_bf16(vop, plo, acc);
+            }
+        }
+    };
+
+    // ---- streaming walk over the wave's pairs ------------------------------------------
+    // PF pairs are always in flight: buffer i holds pair k + i; after computing it, the same
+    // buffer is refilled with pair k + i + PF.  Pair indices past the end are clamped to the
+    // wave's last pair (its pages are already cached), so every load stays inside the
+    // attended pages, and computes past the end are no-ops; the loop body is one basic block
+    // with no early exit, so the loads stay in flight across the back-edge.
+    if (live) {
+        Raw buf[PF];
+        int ida[PF], idb[PF];   // block-table ids of the pair each buffer is loaded with next
+        const int klast = npairs - 1;
+        // (issue order here must match the loop body's: buffer 0 first, K before V)
+#pragma unroll
+        for (int i = 0; i < PF; ++i) {
+            int pa, pb;
+            size_t ha, hb;
+            fetch_ids(min(i, klast), pa, pb);
+            heads(pa, pb, ha, hb);
+            __builtin_amdgcn_sched_barrier(0);
+            load_pair<FMT, D>(buf[i], p, ln, ha, hb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fetch_ids(min(PF + i, klast), ida[i], idb[i]);
+        // The scheduling barriers keep each refill after the compute that frees its buffer:
+        // vmcnt retires in issue order, so a refill hoisted above an older pair's compute
+        // would make that compute wait for every younger load too.
+#pragma unroll 1
+        for (int k = 0; k < npairs; k += PF) {
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                compute(buf[i], k + i);
+                __builtin_amdgcn_sched_barrier(0);
+                size_t ha, hb;
+                heads(ida[i], idb[i], ha, hb);
+                load_pair<FMT, D>(buf[i], p, ln, ha, hb);
+                fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    // ---- merge the four waves --------------------------------------------------------------
+    // ---- results ---------------------------------------------------------------------------
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
     if constexpr (kTurbo) oscale *= sig_run;
+    const size_t row0 = (size_t)b * p.Hq + (size_t)hk * g;
+
+    if (si.split) {
+        // one partition per wave: its triple goes straight to the workspace
+        if (live && qlive) {
+            const size_t slot = (row0 + n) * p.P + part;
+            const float sc = bad_ids ? __builtin_nanf("") : oscale / l_run;
+#pragma unroll
+            for (int t = 0; t < VT; ++t)
+                *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
+            if (j == 0) {
+                p.ws_m[slot] = m_run;
+                p.ws_l[slot] = l_run;
+            }
+        }
+        return;
+    }
+
+    // unsplit: merge the four waves through LDS, then write the final rows
     if (qlive) {
         if (j == 0) {
             sm_m[wave][n] = m_run;
@@ -502,8 +664,6 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             for (int r = 0; r < 4; ++r) sm_o[wave][n][16 * t + 4 * j + r] = oacc[t][r] * oscale;
     }
     const bool wg_bad = __syncthreads_or(bad_ids ? 1 : 0) != 0;
-
-    const size_t row0 = (size_t)b * p.Hq + (size_t)hk * g;
     for (int i = tid; i < g * D; i += kThreads) {
         const int r = i / D, d = i % D;
         float M = sm_m[0][r];
@@ -512,66 +672,91 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         float wsum = 0.0f, acc = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float sc = fast_exp2(sm_m[w][r] - M);
+            const float sc = fast_exp2(sm_m[w][r] - M);   // 0 for waves without tokens
             wsum += sm_l[w][r] * sc;
             acc += sm_o[w][r][d] * sc;
         }
         float o = acc / wsum;
         if (wg_bad) o = __builtin_nanf("");
-        if (si.split) {
-            const size_t slot = (row0 + r) * p.P + part;
-            p.ws_o[slot * D + d] = o;
-            if (d == 0) {
-                p.ws_m[slot] = M;
-                p.ws_l[slot] = wsum;
-            }
-        } else if constexpr (kTurbo) {
-            sm_row[i] = o;
-        } else {
-            out_rows[i] = o;
-        }
+        if constexpr (kTurbo) sm_row[i] = o;
+        else out_rows[i] = o;
     }
-    if constexpr (kTurbo) {
-        if (!si.split) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
-            __syncthreads();
-            fwht_rows<D>(sm_row, g, tid, kThreads);
-            const float rs = 1.0f / sqrtf((float)D);
-            for (int i = tid; i < g * D; i += kThreads) out_rows[i] = sm_row[i] * p.sign[i % D] * rs;
-        }
+    if constexpr (kTurbo) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
+        __syncthreads();
+        fwht_rows<D>(sm_row, g, tid, kThreads);
+        const float rs = 1.0f / sqrtf((float)D);
+        for (int i = tid; i < g * D; i += kThreads) out_rows[i] = sm_row[i] * p.sign[i % D] * rs;
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
+// One wave per (query head, sequence); lane l owns output elements E*l .. E*l + E - 1
+// (E = D / 64).  Partition triples are read eight at a time so their loads overlap.
 template <int FMT, int D>
-__global__ __launch_bounds__(D) void reduce_kernel(const LaunchParams p) {
-    constexpr bool kTurbo = (FMT == KVD_TURBO4 || FMT == KVD_TURBO3);
-    __shared__ float sm[D];
-    const int hq = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
+    constexpr bool kTurbo = is_turbo<FMT>();
+    constexpr int E = D / 64;
+    constexpr int kBatch = 8;
+    const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const SeqInfo si = seq_info(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
     const int p0 = si.lo / p.part_size, p1 = (si.L - 1) / p.part_size;
     const size_t row = (size_t)b * p.Hq + hq;
     const float* ms = p.ws_m + row * p.P;
     const float* ls = p.ws_l + row * p.P;
-    const float* os = p.ws_o + row * p.P * D;
+    const float* os = p.ws_o + row * p.P * D + E * lane;
+
     float M = -INFINITY;
-    for (int q = p0; q <= p1; ++q) M = fmaxf(M, ms[q]);
-    float wsum = 0.0f, acc = 0.0f;
-    for (int q = p0; q <= p1; ++q) {
-        const float w = ls[q] * fast_exp2(ms[q] - M);
-        wsum += w;
-        acc += w * os[(size_t)q * D + d];
+    for (int q = p0 + lane; q <= p1; q += 64) M = fmaxf(M, ms[q]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+
+    float wsum = 0.0f, acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+#pragma unroll 1
+    for (int q = p0; q <= p1; q += kBatch) {
+        float w[kBatch], v[kBatch][E];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int qq = min(q + u, p1);
+            w[u] = (q + u <= p1) ? ls[qq] * fast_exp2(ms[qq] - M) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            wsum += w[u];
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += w[u] * v[u][e];
+        }
     }
-    float o = acc / wsum;
-    if constexpr (kTurbo) {
-        sm[d] = o;
-        __syncthreads();
-        fwht_rows<D>(sm, 1, d, D);
-        o = sm[d] * p.sign[d] * (1.0f / sqrtf((float)D));
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= inv;
+
+    if constexpr (kTurbo) {   // diag(s) H o / sqrt(D): butterflies in registers, then lanes
+        static_assert(E == 2, "codebook formats are built for head_dim 128");
+        const float a0 = acc[0], a1 = acc[1];
+        acc[0] = a0 + a1;
+        acc[1] = a0 - a1;
+#pragma unroll
+        for (int h = 1; h < 64; h <<= 1) {   // elements d and d + 2h live in lanes l and l ^ h
+            const bool upper = (lane & h) != 0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float other = __shfl_xor(acc[e], h);
+                acc[e] = upper ? other - acc[e] : acc[e] + other;
+            }
+        }
+        const float rs = 1.0f / sqrtf((float)D);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= p.sign[E * lane + e] * rs;
     }
-    p.out[row * D + d] = o;
+#pragma unroll
+    for (int e = 0; e < E; ++e) p.out[row * D + E * lane + e] = acc[e];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -622,14 +807,23 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     p.out[i] = val;
 }
 
+// Pairs in flight per wave: BF16 pairs are 16 KB (64 VGPRs), the others 8 KB or less (32
+// VGPRs).  Both depths divide the 16 pairs of a 512-token partition.
+template <int FMT>
+constexpr int prefetch_depth() { return FMT == KVD_BF16 ? 2 : 4; }
+
 template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
-    hipLaunchKernelGGL((partition_kernel<FMT, D>), grid, dim3(kThreads), 0, s, p);
+    constexpr int PF = prefetch_depth<FMT>();
+    if (p.softcap > 0.0f)
+        hipLaunchKernelGGL((partition_kernel<FMT, D, true, PF>), grid, dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((partition_kernel<FMT, D, false, PF>), grid, dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 template <int FMT, int D>
 hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((reduce_kernel<FMT, D>), dim3(p.Hq, p.B), dim3(D), 0, s, p);
+    hipLaunchKernelGGL((reduce_kernel<FMT, D>), dim3(p.Hq, p.B), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 
