@@ -139,8 +139,9 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
                           const int32_t* window, float softcap, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* Phase 1 alone (same arguments).  One workgroup per (partition, KV head, sequence).  For a
- * split sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and its triple goes
+/* Phase 1 alone (same arguments).  One wavefront per (partition, KV head, sequence), four per
+ * workgroup.  For a split sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and
+ * its triple goes
  * to the workspace at (b, h, p):  m = max_j z_j * log2(e)  (base-2 units),
  * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
  * rotated domain for the Turbo formats.  Empty partitions are not written.  Sequences that are
@@ -166,8 +167,10 @@ int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cac
  * sequence `seq`, KV head `kv_head`, gathered through the block table, written as fp32
  * [n_tokens][D] in the storage domain: BF16 widened; FP8 E4M3FN(code) * scale rounded to fp32;
  * Turbo norm * codebook[index] rounded to fp32 (still rotated).  is_v selects V (1) or K (0).
- * `scales`, `codebook` as for kvd_decode_attn_paged.  Uses the same unpack and decode device
- * code as the attention kernel.  Tokens must lie in [0, 16 * max_blocks_per_seq). */
+ * `scales`, `codebook` as for kvd_decode_attn_paged.  Uses the attention kernel's page
+ * addressing, index unpacking and FP8 decode (the attention kernel itself feeds the codebook
+ * levels to its matrix cores as fp16 hi + lo pairs).  Tokens must lie in
+ * [0, 16 * max_blocks_per_seq). */
 int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cache,
                        const float* scales, const float* codebook, const int32_t* block_table,
                        int32_t seq, int32_t kv_head, int32_t token_begin, int32_t n_tokens,
