@@ -17,9 +17,10 @@
 //           four 16-lane groups with two shuffles);
 //         - accumulates O^T += V^T P^T with the same MFMA shape.
 //       Operand precision: BF16 and FP8 caches use exact bf16 K/V/q operands and feed P as a
-//       bf16 hi + lo pair (2^-16 relative).  The codebook caches use fp16 operands split into
-//       hi + lo halves for the levels, the rotated query and P (three MFMAs per product,
-//       about 2^-20 relative), with power-of-two scalings that keep every fp16 value in range.
+//       bf16 hi + lo pair (2^-16 relative).  The codebook caches keep the levels and the
+//       rotated query as fp16 hi + lo pairs (about 2^-20 relative; the level error would
+//       otherwise be systematic) and round P once to fp16 (2^-12, random), with power-of-two
+//       scalings that keep every fp16 value in range.
 //       The MFMA output layout of S^T (lane = query, 4 lane groups x 4 rows = 16 tokens) is
 //       exactly the B-operand layout of P^T for the PV product once the pair's two pages are
 //       interleaved as below, so no data moves between the two products.
@@ -108,28 +109,28 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Codebook table entries hold the fp16 hi part in bits 0..15 and the fp16 lo part in bits
-// 16..31 of one dword.  8 table entries -> the hi operand and the lo operand (4 pairs each).
-__device__ __forceinline__ void split_pairs(const uint32_t (&r)[8], u32x4& hi, u32x4& lo) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        hi[i] = (r[2 * i] & 0xFFFFu) | (r[2 * i + 1] << 16);
-        lo[i] = (r[2 * i] >> 16) | (r[2 * i + 1] & 0xFFFF0000u);
-    }
+// Codebook pair tables.  Entry (i0 + n * i1), n = 16 (4-bit) or 8 (3-bit), holds the packed
+// fp16 dwords of the two levels (c[i0], c[i1]): .x = hi(c[i0]) | hi(c[i1]) << 16 and
+// .y = lo(c[i0]) | lo(c[i1]) << 16, with c ~= hi + lo.  One 8-byte LDS read per two indices.
+//
+// The reads land directly as "interleaved" MFMA operands: for eight indices e0..e7,
+//   a0 = {hi(e0,e1), lo(e0,e1), hi(e2,e3), lo(e2,e3)},  a1 = the same for e4..e7,
+// i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3].  Paired with a B operand whose slots repeat each
+// value, [x0 x1 x0 x1 x2 x3 x2 x3], one MFMA accumulates (hi + lo) * x for four elements; with
+// [y0 y1 0 0 y2 y3 0 0] it accumulates hi * y.
+// 8 4-bit indices (index e at bits 4e of w).
+__device__ __forceinline__ void lut_nib8(const u32x2* lut, uint32_t w, u32x4& a0, u32x4& a1) {
+    const u32x2 e0 = lut[w & 0xFFu], e1 = lut[(w >> 8) & 0xFFu];
+    const u32x2 e2 = lut[(w >> 16) & 0xFFu], e3 = lut[w >> 24];
+    a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
+    a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
 }
-// 8 4-bit indices (index e at bits 4e of w) -> hi / lo fp16 operands.
-__device__ __forceinline__ void lut_nib8(const uint32_t* lut, uint32_t w, u32x4& hi, u32x4& lo) {
-    uint32_t r[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = lut[(w >> (4 * e)) & 15u];
-    split_pairs(r, hi, lo);
-}
-// 8 3-bit indices (index e at bits 3e of the low 24 bits of f) -> hi / lo fp16 operands.
-__device__ __forceinline__ void lut_tri8(const uint32_t* lut, uint32_t f, u32x4& hi, u32x4& lo) {
-    uint32_t r[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = lut[(f >> (3 * e)) & 7u];
-    split_pairs(r, hi, lo);
+// 8 3-bit indices (index e at bits 3e of the low 24 bits of f).
+__device__ __forceinline__ void lut_tri8(const u32x2* lut, uint32_t f, u32x4& a0, u32x4& a1) {
+    const u32x2 e0 = lut[f & 0x3Fu], e1 = lut[(f >> 6) & 0x3Fu];
+    const u32x2 e2 = lut[(f >> 12) & 0x3Fu], e3 = lut[(f >> 18) & 0x3Fu];
+    a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
+    a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
 }
 // The 24-bit field holding indices 8h..8h+7 of a 32-index, 3-bit group (w0..w2 = its 12 bytes).
 __device__ __forceinline__ uint32_t tri_field(uint32_t w0, uint32_t w1, uint32_t w2, int h) {
@@ -293,8 +294,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     __shared__ float sm_o[kWaves][kMaxGroup][D];
     __shared__ float sm_row[kTurbo ? kMaxGroup * D : 1];   // query rotation / output rotation
     __shared__ float sm_rowscale[kMaxGroup];
-    __shared__ uint32_t sm_lut[2][16];
-    __shared__ float sm_lutscale[2];
+    __shared__ u32x2 sm_lut[2][kTurbo ? 256 : 1];   // K and V codebook pair tables
 
     const int xb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -339,30 +339,28 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
-    u32x4 qop[KS];
-    u32x4 qlo[kTurbo ? KS : 1];
+    u32x4 qop[KS];                      // BF16 / FP8: q (bf16) for step s
+    u32x4 qdup[kTurbo ? KS : 1][2];     // codebook formats: q hi, each pair repeated
+    u32x4 qlo0[kTurbo ? KS : 1][2];     // codebook formats: q lo pairs interleaved with zeros
     float zscale;           // logit -> base-2 softmax argument (without per-token factors)
     float oscale = 1.0f;    // accumulator -> output units (FP8 V scale / codebook scales)
 
     if constexpr (kTurbo) {
-        // codebook tables: fp16 hi | lo << 16, levels scaled by a power of two so the largest
-        // magnitude is in [0.5, 1)
-        if (wave == 0) {
-            const int kl = 1 << p.kbits;
-            const int which = lane >> 4, idx = lane & 15;
-            float c = 0.0f;
-            if (which == 0 && idx < kl) c = p.codebook[idx];
-            if (which == 1) c = p.codebook[kl + idx];
-            float mx = fabsf(c);
-            mx = fmaxf(mx, __shfl_xor(mx, 1));
-            mx = fmaxf(mx, __shfl_xor(mx, 2));
-            mx = fmaxf(mx, __shfl_xor(mx, 4));
-            mx = fmaxf(mx, __shfl_xor(mx, 8));
-            const float sc = pow2_normaliser(mx);
+        // codebook pair tables (levels scaled by a power of two so the largest magnitude is in
+        // [0.5, 1)); thread t builds entry t of both tables
+        const int kl = 1 << p.kbits;
+        float kmax = 0.0f, vmax = 0.0f;
+        for (int i = 0; i < kl; ++i) kmax = fmaxf(kmax, fabsf(p.codebook[i]));
+        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
+        const float ksc = pow2_normaliser(kmax), vsc = pow2_normaliser(vmax);
+        {
+            const int t = tid;   // 256 threads, 256 entries
+            const int ki0 = t % kl, ki1 = (t / kl) % kl;
             uint32_t h, l;
-            f16_hilo(c * sc, 0.0f, h, l);
-            if (which < 2) sm_lut[which][idx] = (h & 0xFFFFu) | (l << 16);
-            if (which < 2 && idx == 0) sm_lutscale[which] = sc;
+            f16_hilo(p.codebook[ki0] * ksc, p.codebook[ki1] * ksc, h, l);
+            sm_lut[0][t] = u32x2{h, l};
+            f16_hilo(p.codebook[kl + (t & 15)] * vsc, p.codebook[kl + (t >> 4)] * vsc, h, l);
+            sm_lut[1][t] = u32x2{h, l};
         }
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
         for (int i = tid; i < g * D; i += kThreads) {
@@ -383,16 +381,20 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = 32 * j + 8 * s;
+            uint32_t h[4], l[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint32_t h, l;
-                f16_hilo(sm_row[qn * D + d0 + 2 * i] * qs, sm_row[qn * D + d0 + 2 * i + 1] * qs, h, l);
-                qop[s][i] = qlive ? h : 0u;
-                qlo[s][i] = qlive ? l : 0u;
+                f16_hilo(sm_row[qn * D + d0 + 2 * i] * qs, sm_row[qn * D + d0 + 2 * i + 1] * qs,
+                         h[i], l[i]);
+                if (!qlive) h[i] = l[i] = 0u;
             }
+            qdup[s][0] = u32x4{h[0], h[0], h[1], h[1]};
+            qdup[s][1] = u32x4{h[2], h[2], h[3], h[3]};
+            qlo0[s][0] = u32x4{l[0], 0u, l[1], 0u};
+            qlo0[s][1] = u32x4{l[2], 0u, l[3], 0u};
         }
-        zscale = p.softmax_scale * kLog2e / (qs * sm_lutscale[0] * sqrtf((float)D));
-        oscale = 1.0f / sm_lutscale[1];
+        zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
+        oscale = 1.0f / vsc;
     } else {
         const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)hk * g + qn) * D;
 #pragma unroll
@@ -464,20 +466,22 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         } else {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                u32x4 xh, xl, yh, yl;
+                u32x4 x0, x1, y0, y1;
                 if constexpr (FMT == KVD_TURBO4) {
-                    lut_nib8(sm_lut[0], r.kx[s], xh, xl);
-                    lut_nib8(sm_lut[0], r.ky[s], yh, yl);
+                    lut_nib8(sm_lut[0], r.kx[s], x0, x1);
+                    lut_nib8(sm_lut[0], r.ky[s], y0, y1);
                 } else {
-                    lut_tri8(sm_lut[0], tri_field(r.kx[0], r.kx[1], r.kx[2], s), xh, xl);
-                    lut_tri8(sm_lut[0], tri_field(r.ky[0], r.ky[1], r.ky[2], s), yh, yl);
+                    lut_tri8(sm_lut[0], tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
+                    lut_tri8(sm_lut[0], tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
                 }
-                sx = mfma_f16(xh, qop[s], sx);
-                sx = mfma_f16(xl, qop[s], sx);
-                sx = mfma_f16(xh, qlo[s], sx);
-                sy = mfma_f16(yh, qop[s], sy);
-                sy = mfma_f16(yl, qop[s], sy);
-                sy = mfma_f16(yh, qlo[s], sy);
+                sx = mfma_f16(x0, qdup[s][0], sx);     // (k hi + k lo) * q hi
+                sx = mfma_f16(x1, qdup[s][1], sx);
+                sx = mfma_f16(x0, qlo0[s][0], sx);     // k hi * q lo
+                sx = mfma_f16(x1, qlo0[s][1], sx);
+                sy = mfma_f16(y0, qdup[s][0], sy);
+                sy = mfma_f16(y1, qdup[s][1], sy);
+                sy = mfma_f16(y0, qlo0[s][0], sy);
+                sy = mfma_f16(y1, qlo0[s][1], sy);
             }
         }
 
@@ -520,7 +524,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         l_run = l_run * alpha + psum;
         m_run = m_new;
 
-        uint32_t mk[4];
+        uint32_t mk[4];   // 16-bit lane masks of the eight V k-slots (BF16 / FP8 operands)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             mk[i] = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
@@ -538,27 +542,28 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             }
             vloc = max_over_groups(vloc);
             const float sig_new = fmaxf(sig_run, vloc);
-            const float f = alpha * (sig_run / sig_new);
+            const float inv_sig = __builtin_amdgcn_rcpf(sig_new);
+            const float f = alpha * sig_run * inv_sig;
             sig_run = sig_new;
-            const float inv_sig = 1.0f / sig_new;
-            u32x4 ph, pl;
+            // P' = p * vnorm / sigma in [0, 1], rounded once to fp16 (each value repeated to
+            // match the interleaved hi/lo V operand); the V levels keep their hi + lo precision
+            uint32_t ph[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                uint32_t h, l;
-                f16_hilo(pe[2 * i] * vn[2 * i] * inv_sig, pe[2 * i + 1] * vn[2 * i + 1] * inv_sig, h, l);
-                ph[i] = h;
-                pl[i] = l;
+                const f16x2 h = {(_Float16)(pe[2 * i] * vn[2 * i] * inv_sig),
+                                 (_Float16)(pe[2 * i + 1] * vn[2 * i + 1] * inv_sig)};
+                ph[i] = __builtin_bit_cast(uint32_t, h);
             }
+            const u32x4 pb0 = {ph[0], ph[0], ph[1], ph[1]}, pb1 = {ph[2], ph[2], ph[3], ph[3]};
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
-                u32x4 vh, vl;
-                lut_nib8(sm_lut[1], r.v[t], vh, vl);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) { vh[i] &= mk[i]; vl[i] &= mk[i]; }
+                u32x4 v0, v1;
+                // table levels are always finite and masked tokens have P = 0 exactly (their
+                // norms, possibly NaN, were zeroed above), so no V mask is needed here
+                lut_nib8(sm_lut[1], r.v[t], v0, v1);
                 f32x4 acc = oacc[t] * f;
-                acc = mfma_f16(vh, ph, acc);
-                acc = mfma_f16(vl, ph, acc);
-                oacc[t] = mfma_f16(vh, pl, acc);
+                acc = mfma_f16(v0, pb0, acc);
+                oacc[t] = mfma_f16(v1, pb1, acc);
             }
         } else {
             u32x4 phi, plo;
@@ -807,10 +812,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     p.out[i] = val;
 }
 
-// Pairs in flight per wave: BF16 pairs are 16 KB (64 VGPRs), the others 8 KB or less (32
-// VGPRs).  Both depths divide the 16 pairs of a 512-token partition.
+// Pairs in flight per wave: BF16 pairs are 16 KB (64 VGPRs), FP8 pairs 8 KB (32 VGPRs); the
+// codebook formats are compute-bound and keep their registers for the table lookups.  Both
+// depths divide the 16 pairs of a 512-token partition.
 template <int FMT>
-constexpr int prefetch_depth() { return FMT == KVD_BF16 ? 2 : 4; }
+constexpr int prefetch_depth() { return FMT == KVD_FP8_E4M3 ? 4 : 2; }
 
 template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
