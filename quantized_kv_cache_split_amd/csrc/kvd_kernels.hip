@@ -698,23 +698,26 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence); lane l owns output elements E*l .. E*l + E - 1
-// (E = D / 64).  Partition triples are read eight at a time so their loads overlap.
+// (E = D / 64).  The partition weights are computed lane-parallel (lane i owns partition
+// i of a 64-block) and broadcast with v_readlane; partition outputs are loaded 32 at a time so
+// their loads overlap.
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     constexpr bool kTurbo = is_turbo<FMT>();
     constexpr int E = D / 64;
-    constexpr int kBatch = 8;
+    constexpr int kBatch = 32;
     const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const SeqInfo si = seq_info(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
     const int p0 = si.lo / p.part_size, p1 = (si.L - 1) / p.part_size;
+    const int n = p1 - p0 + 1;
     const size_t row = (size_t)b * p.Hq + hq;
-    const float* ms = p.ws_m + row * p.P;
-    const float* ls = p.ws_l + row * p.P;
-    const float* os = p.ws_o + row * p.P * D + E * lane;
+    const float* ms = p.ws_m + row * p.P + p0;
+    const float* ls = p.ws_l + row * p.P + p0;
+    const float* os = p.ws_o + (row * p.P + p0) * D + E * lane;
 
     float M = -INFINITY;
-    for (int q = p0 + lane; q <= p1; q += 64) M = fmaxf(M, ms[q]);
+    for (int q = lane; q < n; q += 64) M = fmaxf(M, ms[q]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
 
@@ -722,22 +725,29 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 #pragma unroll 1
-    for (int q = p0; q <= p1; q += kBatch) {
-        float w[kBatch], v[kBatch][E];
+    for (int base = 0; base < n; base += 64) {
+        const int q = base + lane;
+        const float w = q < n ? ls[q] * fast_exp2(ms[q] - M) : 0.0f;   // 0 past the end
+        wsum += w;
+#pragma unroll 1
+        for (int c = 0; c < 64 && base + c < n; c += kBatch) {
+            float v[kBatch][E];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int qq = min(q + u, p1);
-            w[u] = (q + u <= p1) ? ls[qq] * fast_exp2(ms[qq] - M) : 0.0f;
+            for (int u = 0; u < kBatch; ++u) {
+                const int qq = min(base + c + u, n - 1);
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
-        }
+                for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
+            }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            wsum += w[u];
+            for (int u = 0; u < kBatch; ++u) {
+                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c + u));
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc[e] += w[u] * v[u][e];
+                for (int e = 0; e < E; ++e) acc[e] += wu * v[u][e];
+            }
         }
     }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o);
     const float inv = 1.0f / wsum;
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] *= inv;
