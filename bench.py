@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--workload", default="c4",
                     help="c1 c2 c3 c4 c5-t4 c5-t3 m-bf16 m-t4 m-t3 (see kvgen.SPECS)")
     ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--partitions-per-wave", type=int, default=0,
+                    help="launch tuning of the partition kernel (0 = the library's choice)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, time a plain device-to-device copy of this "
+                         "many MiB (calibrates HBM byte counters against a known size)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -84,6 +89,26 @@ def kvgen_bytes_per_token_head(s):
     return kvgen.kv_bytes_per_token_head(s.fmt, s.head_dim)
 
 
+def copy_probe(mib, steps):
+    """A plain copy kernel of known size: reads and writes mib MiB per launch."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    dt = e0.elapsed_time(e1) * 1e-3 / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": steps + 3,
+                      "copy_gbps_read_plus_write": round(2 * n / dt / 1e9, 2)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -91,6 +116,10 @@ def main():
               "(the per-(sequence, KV head, partition) work would shard by sequence or KV head "
               "with no exchange, see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
 
     import torch
 
@@ -106,7 +135,7 @@ def main():
     torch.cuda.set_device(0)
     t = to_torch(inp, dev)
     ps = args.partition_size if args.partition_size is not None else spec.partition_size
-    dims = kvd.Dims(**dims_kwargs(inp, ps))
+    dims = kvd.Dims(**dims_kwargs(inp, ps, args.partitions_per_wave))
     out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=torch.float32,
                       device=dev)
     nws = kvd.workspace_bytes(dims)

@@ -105,6 +105,13 @@ typedef struct kvd_dims {
                                     >= 1024 tokens, else a single partition;
                                     > 0: always split at that many tokens (a multiple of 16);
                                     -1: never split */
+    int32_t partitions_per_wave; /* launch tuning, results do not depend on it: how many
+                                    consecutive partitions of a split sequence one wavefront
+                                    walks (it writes every partition's triple).  0: auto (about
+                                    one wavefront per resident slot of the device, at most 8);
+                                    > 0: that many.  Capped at 4096 / (head_dim * Hq / Hkv) and
+                                    treated as 1 when the partition size is not a multiple of
+                                    32.  Must be >= 0. */
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: the per-partition fp32 triples
@@ -139,10 +146,10 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
                           const int32_t* window, float softcap, float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* Phase 1 alone (same arguments).  One wavefront per (partition, KV head, sequence), four per
- * workgroup.  For a split sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and
- * its triple goes
- * to the workspace at (b, h, p):  m = max_j z_j * log2(e)  (base-2 units),
+/* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
+ * partitions_per_wave partitions, four wavefronts per workgroup.  For a split sequence,
+ * partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and its triple goes to the
+ * workspace at (b, h, p):  m = max_j z_j * log2(e)  (base-2 units),
  * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
  * rotated domain for the Turbo formats.  Empty partitions are not written.  Sequences that are
  * not split get their final output row written here. */

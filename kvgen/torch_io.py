@@ -4,13 +4,14 @@ from __future__ import annotations
 import numpy as np
 
 
-def dims_kwargs(inp, partition_size: int | None = None) -> dict:
+def dims_kwargs(inp, partition_size: int | None = None, partitions_per_wave: int = 0) -> dict:
     """Field values of the C ABI's kvd_dims for a batch."""
     s = inp.spec
     return dict(num_seqs=s.num_seqs, num_q_heads=s.num_q_heads, num_kv_heads=s.num_kv_heads,
                 head_dim=s.head_dim, block_size=16, max_blocks_per_seq=inp.max_blocks_per_seq,
                 num_pool_blocks=inp.num_pool_blocks, max_context_len=inp.max_context_len,
-                partition_size=s.partition_size if partition_size is None else partition_size)
+                partition_size=s.partition_size if partition_size is None else partition_size,
+                partitions_per_wave=partitions_per_wave)
 
 
 def to_torch(inp, device) -> dict:

@@ -36,6 +36,37 @@ struct Plan {
     size_t off_l, off_o, bytes;
 };
 
+// Compute units of the current device (256 on MI355X when the query fails).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return 256;
+    return cus;
+}
+
+// Partitions each wave of the partition kernel walks.  A wave pays a fixed start-up (query
+// staging, the block-table -> page-load latency chain, filling its load pipeline) and leaves a
+// tail when it ends; walking several partitions amortises both.  The automatic choice keeps
+// about one wave per resident slot of the chip (P * Hkv * B waves / (CUs * 8)), capped at
+// kMaxRun, and at the rows a wave can stage in LDS (stage_rows(D) / group).  Runs need
+// partition boundaries on even pages (partition size a multiple of 32).
+int choose_run(const kvd_dims* d, const Plan& pl) {
+    if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return 1;
+    int64_t r = d->partitions_per_wave;
+    if (r == 0) {
+        const int64_t waves = (int64_t)pl.P * d->num_kv_heads * d->num_seqs;
+        const int64_t slots = (int64_t)device_cus() * kvd::kWavesPerCU;
+        r = (waves + slots - 1) / slots;
+        if (r > kvd::kMaxRun) r = kvd::kMaxRun;
+    }
+    const int64_t cap = kvd::stage_rows(d->head_dim) / (d->num_q_heads / d->num_kv_heads);
+    if (r > cap) r = cap;
+    if (r > pl.P) r = pl.P;
+    return r < 1 ? 1 : (int)r;
+}
+
 // Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
 int check_dims(const kvd_dims* d, int fmt) {
     if (!d) return KVD_ERR_NULL;
@@ -53,6 +84,7 @@ int check_dims(const kvd_dims* d, int fmt) {
     const int ps = d->partition_size;
     if (!(ps == 0 || ps == -1 || (ps > 0 && ps % kvd::kPageTokens == 0))) return KVD_ERR_SHAPE;
     if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return KVD_ERR_SHAPE;   // grid limits
+    if (d->partitions_per_wave < 0) return KVD_ERR_SHAPE;
     return KVD_OK;
 }
 
@@ -135,14 +167,17 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.part_size = pl.part_size;
     p.P = pl.P;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    p.run = choose_run(d, pl);
+    // token indices of every partition a workgroup can name must fit in int32
+    if (pl.P && ((int64_t)pl.P + 4LL * p.run) * pl.part_size > 0x7FFFFFFFLL) return KVD_ERR_SHAPE;
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (phases & kPhase1) {
-        // one wave per partition, four partitions per workgroup
-        const int px = pl.P ? (pl.P + 3) / 4 : 1;
+        // four waves per workgroup, p.run partitions per wave
+        const int px = pl.P ? (pl.P + 4 * p.run - 1) / (4 * p.run) : 1;
         const dim3 grid(px, d->num_kv_heads, d->num_seqs);
         e = kvd::launch_partitions(fmt, p, grid, s);
         if (e != hipSuccess) return KVD_ERR_HIP;

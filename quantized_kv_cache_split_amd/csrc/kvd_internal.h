@@ -12,6 +12,11 @@ constexpr int kPageTokens = 16;     // tokens per page (block_size)
 constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
 constexpr int kMaxGroup = 16;       // query heads per KV head one workgroup handles
+constexpr int kMaxRun = 8;          // cap on the automatic partitions-per-wave choice
+constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
+// (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
+// a wave's run of partitions is capped at stage_rows(D) / group.
+constexpr int stage_rows(int d) { return 4096 / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };
 
@@ -38,6 +43,7 @@ struct LaunchParams {
     int32_t part_size;        // tokens per partition (split sequences)
     int32_t P;                // partitions per sequence in the workspace / grid
     int32_t kbits;            // turbo K index width (4 or 3)
+    int32_t run;              // partitions one wave walks (split sequences), >= 1
     float softmax_scale;
     float softcap;
 };

@@ -118,10 +118,30 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
 // i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3].  Paired with a B operand whose slots repeat each
 // value, [x0 x1 x0 x1 x2 x3 x2 x3], one MFMA accumulates (hi + lo) * x for four elements; with
 // [y0 y1 0 0 y2 y3 0 0] it accumulates hi * y.
+// Byte K of w times 8 (the byte offset of an 8-byte table entry) in one VALU instruction:
+// gfx9 SDWA selects and zero-extends the byte as the shift's source operand.
+template <int K>
+__device__ __forceinline__ uint32_t byte_times8(uint32_t w) {
+    static_assert(K >= 0 && K < 4, "byte index");
+    uint32_t r;
+    if constexpr (K == 0)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
+    else if constexpr (K == 1)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
+    else if constexpr (K == 2)
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
+    else
+        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
+    return r;
+}
+template <int K>
+__device__ __forceinline__ u32x2 lut_byte(const u32x2* lut, uint32_t w) {
+    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(lut) + byte_times8<K>(w));
+}
 // 8 4-bit indices (index e at bits 4e of w).
 __device__ __forceinline__ void lut_nib8(const u32x2* lut, uint32_t w, u32x4& a0, u32x4& a1) {
-    const u32x2 e0 = lut[w & 0xFFu], e1 = lut[(w >> 8) & 0xFFu];
-    const u32x2 e2 = lut[(w >> 16) & 0xFFu], e3 = lut[w >> 24];
+    const u32x2 e0 = lut_byte<0>(lut, w), e1 = lut_byte<1>(lut, w);
+    const u32x2 e2 = lut_byte<2>(lut, w), e3 = lut_byte<3>(lut, w);
     a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
     a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
 }
@@ -277,10 +297,15 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-// Grid (ceil(P / 4), Hkv, B), 4 waves.  For a split sequence wave w of workgroup x owns
-// partition 4x + w on its own and writes that partition's triple straight from registers.
-// For an unsplit sequence (workgroup 0 only) the four waves share the attended range
-// (consecutive quarters of its page pairs) and merge through LDS.
+// Grid (ceil(P / (4 R)), Hkv, B), 4 waves, R = p.run partitions per wave.  For a split
+// sequence wave w of workgroup x owns the run of R consecutive partitions that starts at
+// partition plo + (4x + w) R (plo = the first partition the attended range touches), streams
+// through all of them without draining its load pipeline, and writes each partition's triple
+// straight from registers once the partition's last page pair is done.  For an unsplit
+// sequence (workgroup 0 only) the four waves share the attended range (consecutive quarters of
+// its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
+// partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
+// partitions.
 template <int FMT, int D, bool CAP, int PF>
 __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchParams p) {
     constexpr bool kTurbo = is_turbo<FMT>();
@@ -289,12 +314,30 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     static_assert(!kTurbo || D == 128, "codebook formats are built for head_dim 128");
     using Raw = PairRaw<FMT, D>;
 
-    __shared__ float sm_m[kWaves][kMaxGroup];
-    __shared__ float sm_l[kWaves][kMaxGroup];
-    __shared__ float sm_o[kWaves][kMaxGroup][D];
-    __shared__ float sm_row[kTurbo ? kMaxGroup * D : 1];   // query rotation / output rotation
-    __shared__ float sm_rowscale[kMaxGroup];
-    __shared__ u32x2 sm_lut[2][kTurbo ? 256 : 1];   // K and V codebook pair tables
+    // Per-wave staging of finished (m, l, o) rows: a split wave stages the triples of the
+    // partitions it closes (row r * g + n for the r-th partition of its run, query n) and copies
+    // them to the workspace after its walk, so no global store joins the in-order stream of its
+    // loads; the unsplit merge uses rows 0..g-1.  Rows are D + 4 floats apart so the 16 query
+    // rows a ds_write_b128 touches start in different banks.
+    constexpr int SR = stage_rows(D);
+    constexpr int SD = D + 4;
+    // All LDS in one block, codebook tables first: their addresses then fit the 16-bit offset
+    // field of ds_read, so a table lookup costs one address instruction.
+    struct Lds {
+        u32x2 lut[2][kTurbo ? 256 : 1];          // K and V codebook pair tables
+        float rowscale[kMaxGroup];
+        float m[kWaves][SR];
+        float l[kWaves][SR];
+        float row[kTurbo ? kMaxGroup * D : 1];   // query rotation / output rotation
+        f32x4 o[kWaves][SR * SD / 4];
+    };
+    __shared__ Lds lds;
+    auto& sm_lut = lds.lut;
+    auto& sm_rowscale = lds.rowscale;
+    auto& sm_m = lds.m;
+    auto& sm_l = lds.l;
+    float* const sm_row = lds.row;
+    float (&sm_o)[kWaves][SR * SD] = *reinterpret_cast<float (*)[kWaves][SR * SD]>(&lds.o);
 
     const int xb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -310,16 +353,20 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         }
         return;
     }
-    // token range [lo, hi) of this wave (uniform per workgroup: whether any wave has work)
-    int lo, hi, part = 0;
+    // token range [lo, hi) of this wave (uniform per workgroup: whether any wave has work);
+    // split waves also track the partition being accumulated and where its tokens end
+    int lo, hi, part = 0, part_end = 0, part_first = 0;
     if (si.split) {
-        if (xb * kWaves * p.part_size >= si.L) return;
-        part = xb * kWaves + wave;
+        const int plo = si.lo / p.part_size, phi = (si.L - 1) / p.part_size;
+        if (plo + xb * kWaves * p.run > phi) return;
+        part = part_first = plo + (xb * kWaves + wave) * p.run;
+        const int pend = min(part + p.run, phi + 1);
         lo = max(si.lo, part * p.part_size);
-        hi = min(si.L, (part + 1) * p.part_size);
+        hi = min(si.L, pend * p.part_size);
+        part_end = min(hi, (part + 1) * p.part_size);
     } else {
         if (xb != 0) return;
-        const int pg0 = si.lo / kPageTokens, pg1 = (si.L - 1) / kPageTokens + 1;
+        const int pg0 = (si.lo / kPageTokens) & ~1, pg1 = (si.L - 1) / kPageTokens + 1;
         const int np = (pg1 - pg0 + 1) >> 1;
         const int per = (np + kWaves - 1) / kWaves;
         lo = max(si.lo, (pg0 + 2 * per * wave) * kPageTokens);
@@ -416,19 +463,27 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     f32x4 oacc[VT];
 #pragma unroll
     for (int i = 0; i < VT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;
-    float sig_run = 1.17549435e-38f;   // running max of V norms (codebook formats)
+    float m_run = -INFINITY, l_run = 0.0f;   // softmax reference max (base 2) and sum
+    float m_true = -INFINITY;                 // the exact running max of the logits
+    constexpr float kSigInit = 1.17549435e-38f;
+    constexpr float kLazyLog2 = 8.0f, kLazySig = 16.0f;
+    float sig_run = kSigInit;   // reference V norm (codebook formats), 1 / sig_run
+    float inv_sig = 1.0f / kSigInit;
     bool bad_ids = false;
 
-    const int pg0 = live ? lo / kPageTokens : 0, pg1 = live ? (hi - 1) / kPageTokens + 1 : 1;
+    // pair k covers pages pg0 + 2k and pg0 + 2k + 1 (pg0 even)
+    const int pgLo = live ? lo / kPageTokens : 0;
+    const int pg0 = pgLo & ~1, pg1 = live ? (hi - 1) / kPageTokens + 1 : 1;
     const int npairs = live ? (pg1 - pg0 + 1) >> 1 : 0;
     const_i32_ptr btrow = (const_i32_ptr)(p.bt + (size_t)b * p.max_blocks);
 
-    // physical pages of pair k (scalar loads; a missing second page reads the first page's
-    // row, which the mask then hides; ids outside the pool are clamped and flagged)
+    // physical pages of pair k (scalar loads).  Only entries of pages inside [pgLo, pg1) are
+    // read: a first page below the range or a missing second page reads the row of the
+    // range's page next to it, whose tokens the mask then hides.  Ids outside the pool are
+    // clamped and flagged.
     auto fetch_ids = [&](int k, int& pa, int& pb) {
         const int pgA = pg0 + 2 * k;
-        pa = btrow[pgA];
+        pa = btrow[max(pgA, pgLo)];
         pb = btrow[min(pgA + 1, pg1 - 1)];
     };
     auto heads = [&](int pa, int pb, size_t& ha, size_t& hb) {
@@ -440,8 +495,8 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 
     // ---- one pair: logits, online softmax, PV ------------------------------------------
     // A pair index at or past npairs is a no-op: its token window is empty, so every logit
-    // is -inf, p = 0, alpha = 1 and the V operands are zero.
-    auto compute = [&](const Raw& r, int k) {
+    // is -inf, no reference moves, p = 0 and the V values are zero.
+    auto compute = [&](Raw& r, int k) {
         const int pgA = pg0 + 2 * min(k, npairs - 1);
         const bool hasB = pgA + 1 < pg1;
         const int hi_k = k < npairs ? hi : lo;
@@ -499,71 +554,105 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
                 z[e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
             }
         }
-        // tokens outside [lo, hi) (and a missing second page) are selected out, never
-        // multiplied: their logits become -inf and their V operands zero
-        uint32_t vmask = 0;
-        {
+        float vn[8];   // V norms (codebook formats)
+        if constexpr (kTurbo) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { vn[e] = r.vn0[e]; vn[4 + e] = r.vn1[e]; }
+        }
+        // Tokens outside [lo, hi) (and a missing second page) are selected out, never
+        // multiplied: their logits become -inf and their V values zero.  Only the first and
+        // last pair of a range can be partial; the test is uniform over the wave.
+        if (!full) {
             const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
+            uint32_t vmask = 0;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = tok0 + e;
-                const bool ok = full || ((t >= lo) && (t < hi_k) && (ln.v_sel == 0 || hasB));
+                const bool ok = (t >= lo) && (t < hi_k) && (ln.v_sel == 0 || hasB);
                 vmask |= (ok ? 1u : 0u) << e;
                 z[e] = ok ? z[e] : -INFINITY;
+            }
+            if constexpr (kTurbo) {
+                // table levels are always finite, so zero norms (possibly NaN in unused slots)
+                // make the masked P' exactly 0
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vn[e] = ((vmask >> e) & 1u) ? vn[e] : 0.0f;
+            } else if constexpr (FMT == KVD_BF16) {
+                uint32_t mk[4];   // 16-bit lane masks of the eight V k-slots
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    mk[i] = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
+                            (((vmask >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) r.v[t][i] &= mk[i];
+            } else {
+                uint32_t mb[2];   // byte masks of the eight V codes (code 0 is +0.0)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    mb[h] = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mb[h] |= (((vmask >> (4 * h + e)) & 1u) ? 0xFFu : 0u) << (8 * e);
+                }
+#pragma unroll
+                for (int t = 0; t < VT; ++t) { r.v[t][0] &= mb[0]; r.v[t][1] &= mb[1]; }
             }
         }
         float mloc = z[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, z[e]);
         mloc = max_over_groups(mloc);
-        const float m_new = fmaxf(m_run, mloc);
-        const float alpha = fast_exp2(m_run - m_new);
+        m_true = fmaxf(m_true, mloc);
+        // Lazy rescaling: the reference max m_run (and, for the codebook formats, the V-norm
+        // reference sig_run) only moves when some query's new logits exceed it by more than
+        // 2^kLazyLog2 (or a norm exceeds it kLazySig-fold), so P stays <= 2^8 (P' <= 2^12) and
+        // the accumulator rescale is skipped on almost every pair.  The choice is wave-uniform.
+        bool grow = mloc > m_run + kLazyLog2;
+        float vloc = 0.0f;
+        if constexpr (kTurbo) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vloc = fmaxf(vloc, vn[e]);
+            vloc = max_over_groups(vloc);
+            grow = grow || (vloc > sig_run * kLazySig);
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m_run, mloc);
+            float f = fast_exp2(m_run - m_new);
+            l_run *= f;
+            if constexpr (kTurbo) {
+                const float sig_new = fmaxf(sig_run, vloc);
+                inv_sig = __builtin_amdgcn_rcpf(sig_new);
+                f *= sig_run * inv_sig;
+                sig_run = sig_new;
+            }
+#pragma unroll
+            for (int t = 0; t < VT; ++t) oacc[t] *= f;
+            m_run = m_new;
+        }
         float pe[8], psum = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_new); psum += pe[e]; }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-
-        uint32_t mk[4];   // 16-bit lane masks of the eight V k-slots (BF16 / FP8 operands)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mk[i] = (((vmask >> (2 * i)) & 1u) ? 0x0000FFFFu : 0u) |
-                    (((vmask >> (2 * i + 1)) & 1u) ? 0xFFFF0000u : 0u);
+        for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_run); psum += pe[e]; }
+        l_run += psum;
 
         if constexpr (kTurbo) {
-            float vn[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { vn[e] = r.vn0[e]; vn[4 + e] = r.vn1[e]; }
-            float vloc = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                vn[e] = ((vmask >> e) & 1u) ? vn[e] : 0.0f;
-                vloc = fmaxf(vloc, vn[e]);
-            }
-            vloc = max_over_groups(vloc);
-            const float sig_new = fmaxf(sig_run, vloc);
-            const float inv_sig = __builtin_amdgcn_rcpf(sig_new);
-            const float f = alpha * sig_run * inv_sig;
-            sig_run = sig_new;
-            // P' = p * vnorm / sigma in [0, 1], rounded once to fp16 (each value repeated to
-            // match the interleaved hi/lo V operand); the V levels keep their hi + lo precision
+            // P' = p * vnorm / sigma, rounded once to fp16 (each value repeated to match the
+            // interleaved hi/lo V operand); the V levels keep their hi + lo precision
             uint32_t ph[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f16x2 h = {(_Float16)(pe[2 * i] * vn[2 * i] * inv_sig),
-                                 (_Float16)(pe[2 * i + 1] * vn[2 * i + 1] * inv_sig)};
+                const f16x2 h = {(_Float16)(pe[2 * i] * (vn[2 * i] * inv_sig)),
+                                 (_Float16)(pe[2 * i + 1] * (vn[2 * i + 1] * inv_sig))};
                 ph[i] = __builtin_bit_cast(uint32_t, h);
             }
             const u32x4 pb0 = {ph[0], ph[0], ph[1], ph[1]}, pb1 = {ph[2], ph[2], ph[3], ph[3]};
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
                 u32x4 v0, v1;
-                // table levels are always finite and masked tokens have P = 0 exactly (their
-                // norms, possibly NaN, were zeroed above), so no V mask is needed here
                 lut_nib8(sm_lut[1], r.v[t], v0, v1);
-                f32x4 acc = oacc[t] * f;
-                acc = mfma_f16(v0, pb0, acc);
-                oacc[t] = mfma_f16(v1, pb1, acc);
+                oacc[t] = mfma_f16(v0, pb0, oacc[t]);
+                oacc[t] = mfma_f16(v1, pb1, oacc[t]);
             }
         } else {
             u32x4 phi, plo;
@@ -585,12 +674,45 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
                     const u32x2 a0 = fp8x4_to_bf16(r.v[t][0]), a1 = fp8x4_to_bf16(r.v[t][1]);
                     vop = u32x4{a0[0], a0[1], a1[0], a1[1]};
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vop[i] &= mk[i];
-                f32x4 acc = oacc[t] * alpha;
-                acc = mfma_bf16(vop, phi, acc);
-                oacc[t] = mfma_bf16(vop, plo, acc);
+                oacc[t] = mfma_bf16(vop, phi, oacc[t]);
+                oacc[t] = mfma_bf16(vop, plo, oacc[t]);
             }
+        }
+    };
+
+    const size_t row0 = (size_t)b * p.Hq + (size_t)hk * g;
+
+    // ---- split sequences: close a partition after its last pair ------------------------
+    // Writes the partition's triple (m = the exact max logit in base-2 units, l = the sum
+    // taken relative to it, o = O / l in output units, which no reference choice affects) and
+    // restarts the softmax state for the next partition of the run exactly as a fresh wave
+    // starts it, so the triples do not depend on how many partitions a wave walks.  The
+    // condition is wave-uniform; pairs past the end never close anything.
+    auto close_partition = [&](int k) {
+        const int tend = (pg0 + 2 * k + 2) * kPageTokens;   // first token after pair k
+        if (k < npairs && tend >= part_end) {
+            float lt = l_run + __shfl_xor(l_run, 16);
+            lt += __shfl_xor(lt, 32);
+            const int row = (part - part_first) * g + n;
+            if (qlive && row < SR) {   // the host keeps run * g <= SR
+                const float osc = kTurbo ? oscale * sig_run : oscale;
+                const float sc = bad_ids ? __builtin_nanf("") : osc / lt;
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+                    *reinterpret_cast<f32x4*>(&sm_o[wave][row * SD + 16 * t + 4 * j]) = oacc[t] * sc;
+                if (j == 0) {   // the sum restated relative to the exact max
+                    sm_m[wave][row] = m_true;
+                    sm_l[wave][row] = lt * fast_exp2(m_run - m_true);
+                }
+            }
+            m_run = m_true = -INFINITY;
+            l_run = 0.0f;
+            sig_run = kSigInit;
+            inv_sig = 1.0f / kSigInit;
+#pragma unroll
+            for (int t = 0; t < VT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            ++part;
+            part_end = min(hi, part_end + p.part_size);
         }
     };
 
@@ -625,6 +747,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
                 compute(buf[i], k + i);
+                if (si.split) close_partition(k + i);
                 __builtin_amdgcn_sched_barrier(0);
                 size_t ha, hb;
                 heads(ida[i], idb[i], ha, hb);
@@ -636,26 +759,33 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     }
 
     // ---- results ---------------------------------------------------------------------------
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if constexpr (kTurbo) oscale *= sig_run;
-    const size_t row0 = (size_t)b * p.Hq + (size_t)hk * g;
-
     if (si.split) {
-        // one partition per wave: its triple goes straight to the workspace
-        if (live && qlive) {
-            const size_t slot = (row0 + n) * p.P + part;
-            const float sc = bad_ids ? __builtin_nanf("") : oscale / l_run;
-#pragma unroll
-            for (int t = 0; t < VT; ++t)
-                *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
-            if (j == 0) {
-                p.ws_m[slot] = m_run;
-                p.ws_l[slot] = l_run;
-            }
+        // copy the run's staged triples to the workspace (this wave's own LDS rows: a
+        // wavefront-scope fence orders the other lanes' writes before the reads)
+        if (!live) return;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int nrows = min((part - part_first) * g, SR);
+        constexpr int C = D / 4;   // f32x4 per row
+        for (int i = lane; i < nrows * C; i += 64) {
+            const int row = i / C, c = i % C;
+            const int r = row / g, qn_ = row - r * g;
+            const size_t slot = (row0 + qn_) * p.P + part_first + r;
+            *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 4 * c) =
+                *reinterpret_cast<const f32x4*>(&sm_o[wave][row * SD + 4 * c]);
+        }
+        for (int row = lane; row < nrows; row += 64) {
+            const int r = row / g, qn_ = row - r * g;
+            const size_t slot = (row0 + qn_) * p.P + part_first + r;
+            p.ws_m[slot] = sm_m[wave][row];
+            p.ws_l[slot] = sm_l[wave][row];
         }
         return;
     }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if constexpr (kTurbo) oscale *= sig_run;
 
     // unsplit: merge the four waves through LDS, then write the final rows
     if (qlive) {
@@ -666,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 #pragma unroll
         for (int t = 0; t < VT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm_o[wave][n][16 * t + 4 * j + r] = oacc[t][r] * oscale;
+            for (int r = 0; r < 4; ++r) sm_o[wave][n * SD + 16 * t + 4 * j + r] = oacc[t][r] * oscale;
     }
     const bool wg_bad = __syncthreads_or(bad_ids ? 1 : 0) != 0;
     for (int i = tid; i < g * D; i += kThreads) {
@@ -679,7 +809,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         for (int w = 0; w < kWaves; ++w) {
             const float sc = fast_exp2(sm_m[w][r] - M);   // 0 for waves without tokens
             wsum += sm_l[w][r] * sc;
-            acc += sm_o[w][r][d] * sc;
+            acc += sm_o[w][r * SD + d] * sc;
         }
         float o = acc / wsum;
         if (wg_bad) o = __builtin_nanf("");
@@ -698,14 +828,15 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence); lane l owns output elements E*l .. E*l + E - 1
-// (E = D / 64).  The partition weights are computed lane-parallel (lane i owns partition
-// i of a 64-block) and broadcast with v_readlane; partition outputs are loaded 32 at a time so
-// their loads overlap.
+// (E = D / 64).  Partitions are taken 64 at a time: each lane loads the (m, l) of one of them
+// and then every lane loads its slice of all 64 partition outputs, so a block costs one memory
+// round trip.  The block's weights are computed lane-parallel and broadcast with v_readlane;
+// blocks after the first rescale the running sums to the new maximum (online LSE).
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     constexpr bool kTurbo = is_turbo<FMT>();
     constexpr int E = D / 64;
-    constexpr int kBatch = 32;
+    constexpr int kBlock = 64;
     const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
     const SeqInfo si = seq_info(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
@@ -716,35 +847,39 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     const float* ls = p.ws_l + row * p.P + p0;
     const float* os = p.ws_o + (row * p.P + p0) * D + E * lane;
 
-    float M = -INFINITY;
-    for (int q = lane; q < n; q += 64) M = fmaxf(M, ms[q]);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
-
-    float wsum = 0.0f, acc[E];
+    float M = -INFINITY, wsum = 0.0f, acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0f;
 #pragma unroll 1
-    for (int base = 0; base < n; base += 64) {
-        const int q = base + lane;
-        const float w = q < n ? ls[q] * fast_exp2(ms[q] - M) : 0.0f;   // 0 past the end
-        wsum += w;
-#pragma unroll 1
-        for (int c = 0; c < 64 && base + c < n; c += kBatch) {
-            float v[kBatch][E];
+    for (int base = 0; base < n; base += kBlock) {
+        // indices past the end are clamped (their loads stay in bounds) and weighted 0
+        const int q = min(base + lane, n - 1);
+        const float mq = ms[q], lq = ls[q];
+        float v[kBlock][E];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int qq = min(base + c + u, n - 1);
+        for (int u = 0; u < kBlock; ++u) {
+            const int qq = min(base + u, n - 1);
 #pragma unroll
-                for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
-            }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), c + u));
-#pragma unroll
-                for (int e = 0; e < E; ++e) acc[e] += wu * v[u][e];
-            }
+            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
         }
+        __builtin_amdgcn_sched_barrier(0);   // keep all of the block's loads ahead of any use
+        const bool in = base + lane < n;
+        float mb = in ? mq : -INFINITY;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
+        const float Mn = fmaxf(M, mb);
+        const float sc = fast_exp2(M - Mn);   // 0 on the first block (M = -inf)
+        const float w = in ? lq * fast_exp2(mq - Mn) : 0.0f;
+        wsum = wsum * sc + w;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] *= sc;
+#pragma unroll
+        for (int u = 0; u < kBlock; ++u) {
+            const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += wu * v[u][e];
+        }
+        M = Mn;
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) wsum += __shfl_xor(wsum, o);

@@ -14,12 +14,12 @@ REL_TOL = 1e-2     # max over rows of max_d |gpu - oracle| / max_d |oracle|
 class GpuBatch:
     """Device copy of one batch plus output and workspace buffers."""
 
-    def __init__(self, inp, partition_size=None, device="cuda:0"):
+    def __init__(self, inp, partition_size=None, device="cuda:0", partitions_per_wave=0):
         import torch
         import quantized_kv_cache_split_amd as kvd
         self.kvd = kvd
         self.inp = inp
-        self.dims = kvd.Dims(**dims_kwargs(inp, partition_size))
+        self.dims = kvd.Dims(**dims_kwargs(inp, partition_size, partitions_per_wave))
         self.t = to_torch(inp, device)
         s = inp.spec
         self.out = torch.full((s.num_seqs, s.num_q_heads, s.head_dim), float("nan"),

@@ -138,6 +138,29 @@ def test_partition_sizes_agree(fmt, ps):
     assert_close(GpuBatch(inp, partition_size=ps).run(), _oracle(inp), f"{fmt} ps={ps}")
 
 
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_partitions_per_wave_bit_identical(fmt):
+    """Walking several partitions per wave changes the launch, not the results: every run length
+    gives the same bits (each partition restarts the state exactly as a fresh wave), and those
+    bits match the oracle.  Windows put the first attended token on odd and even pages."""
+    lengths = [5000, 4100, 3000, 1100, 2600, 700]
+    windows = [1100, 0, 1333, 0, 2049, 100]
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=len(lengths), num_q_heads=8,
+                                       num_kv_heads=2, softcap=0.0),
+                            lengths=lengths, windows=windows, poison_before_window=True)
+    for b, (L, W) in enumerate(zip(lengths, windows)):   # entries before a window: never read
+        if W:
+            inp.block_table[b, : max(0, L - W) // 16] = -1
+    ref = _oracle(inp)
+    outs = {}
+    for ps in (0, 128):
+        for run in (1, 2, 3, 5, 8):
+            outs[ps, run] = GpuBatch(inp, partition_size=ps, partitions_per_wave=run).run()
+            assert_close(outs[ps, run], ref, f"{fmt} ps={ps} run={run}")
+        for run in (2, 3, 5, 8):
+            assert (outs[ps, run].view(np.uint64) == outs[ps, 1].view(np.uint64)).all(), (ps, run)
+
+
 # --------------------------------------------------------------------------------------------
 # structure: permutation invariance, poison, identities, partials, error rows
 # --------------------------------------------------------------------------------------------
@@ -191,10 +214,11 @@ def test_uniform_v():
     assert np.abs(gpu + 1.25).max() < 1e-5
 
 
+@pytest.mark.parametrize("run", [1, 3])
 @pytest.mark.parametrize("fmt", kvgen.FORMATS)
-def test_partials_match_oracle(fmt):
+def test_partials_match_oracle(fmt, run):
     inp = _small(fmt, context=None, ctx_range=(200, 700), num_seqs=2)
-    gb = GpuBatch(inp, partition_size=128)
+    gb = GpuBatch(inp, partition_size=128, partitions_per_wave=run)
     gb.run_phase1()
     m, l, o = gb.partials()
     s = inp.spec
