@@ -107,11 +107,12 @@ typedef struct kvd_dims {
                                     -1: never split */
     int32_t partitions_per_wave; /* launch tuning, results do not depend on it: how many
                                     consecutive partitions of a split sequence one wavefront
-                                    walks (it writes every partition's triple).  0: auto (about
-                                    one wavefront per resident slot of the device, at most 8);
-                                    > 0: that many.  Capped at 4096 / (head_dim * Hq / Hkv) and
-                                    treated as 1 when the partition size is not a multiple of
-                                    32.  Must be >= 0. */
+                                    walks (it writes every partition's triple).  0: auto
+                                    (about one wavefront per resident slot of the device when
+                                    every sequence had max_context_len tokens, at most 4);
+                                    > 0: that many.  Capped at 4096 / (head_dim * Hq / Hkv)
+                                    and treated as 1 when the partition size is not a
+                                    multiple of 32.  Must be >= 0. */
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: the per-partition fp32 triples

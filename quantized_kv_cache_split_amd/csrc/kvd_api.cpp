@@ -49,8 +49,10 @@ int device_cus() {
 // Partitions each wave of the partition kernel walks.  A wave pays a fixed start-up (query
 // staging, the block-table -> page-load latency chain, filling its load pipeline) and leaves a
 // tail when it ends; walking several partitions amortises both.  The automatic choice keeps
-// about one wave per resident slot of the chip (P * Hkv * B waves / (CUs * 8)), capped at
-// kMaxRun, and at the rows a wave can stage in LDS (stage_rows(D) / group).  Runs need
+// about one wave per resident slot of the chip (P * Hkv * B waves / (CUs * 8)) as if every
+// sequence were max_context_len long, capped at kMaxRun (ragged batches, whose real work is
+// smaller, do better with short runs) and at the rows a wave can stage in LDS
+// (stage_rows(D) / group).  Runs need
 // partition boundaries on even pages (partition size a multiple of 32).
 int choose_run(const kvd_dims* d, const Plan& pl) {
     if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return 1;
@@ -178,7 +180,9 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     if (phases & kPhase1) {
         // four waves per workgroup, p.run partitions per wave
         const int px = pl.P ? (pl.P + 4 * p.run - 1) / (4 * p.run) : 1;
-        const dim3 grid(px, d->num_kv_heads, d->num_seqs);
+        const int64_t wgs = (int64_t)px * d->num_kv_heads * d->num_seqs;
+        if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
+        const dim3 grid((unsigned)wgs);
         e = kvd::launch_partitions(fmt, p, grid, s);
         if (e != hipSuccess) return KVD_ERR_HIP;
     }

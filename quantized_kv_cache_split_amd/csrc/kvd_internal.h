@@ -12,7 +12,7 @@ constexpr int kPageTokens = 16;     // tokens per page (block_size)
 constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
 constexpr int kMaxGroup = 16;       // query heads per KV head one workgroup handles
-constexpr int kMaxRun = 8;          // cap on the automatic partitions-per-wave choice
+constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
 constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
 // (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
 // a wave's run of partitions is capped at stage_rows(D) / group.

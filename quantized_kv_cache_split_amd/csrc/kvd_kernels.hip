@@ -297,7 +297,7 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-// Grid (ceil(P / (4 R)), Hkv, B), 4 waves, R = p.run partitions per wave.  For a split
+// Grid ceil(P / (4 R)) * Hkv * B (1-D), 4 waves, R = p.run partitions per wave.  For a split
 // sequence wave w of workgroup x owns the run of R consecutive partitions that starts at
 // partition plo + (4x + w) R (plo = the first partition the attended range touches), streams
 // through all of them without draining its load pipeline, and writes each partition's triple
@@ -339,7 +339,12 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     float* const sm_row = lds.row;
     float (&sm_o)[kWaves][SR * SD] = *reinterpret_cast<float (*)[kWaves][SR * SD]>(&lds.o);
 
-    const int xb = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    // 1-D grid, KV head fastest, then sequence, then the partition slot x.  Workgroups are
+    // handed to the eight XCDs round-robin by linear id, so this order spreads every
+    // sequence's work over the XCDs (with 8 KV heads each XCD gets one head of every
+    // sequence); x fastest would pile the short sequences' work onto the XCDs of small x.
+    const int wg = blockIdx.x;
+    const int hk = wg % p.Hkv, b = (wg / p.Hkv) % p.B, xb = wg / (p.Hkv * p.B);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = p.g;
