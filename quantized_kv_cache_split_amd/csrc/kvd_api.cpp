@@ -54,7 +54,7 @@ int device_cus() {
 // smaller, do better with short runs) and at the rows a wave can stage in LDS
 // (stage_rows(D) / group).  Runs need
 // partition boundaries on even pages (partition size a multiple of 32).
-int choose_run(const kvd_dims* d, const Plan& pl) {
+int choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return 1;
     int64_t r = d->partitions_per_wave;
     if (r == 0) {
@@ -63,8 +63,10 @@ int choose_run(const kvd_dims* d, const Plan& pl) {
         r = (waves + slots - 1) / slots;
         if (r > kvd::kMaxRun) r = kvd::kMaxRun;
     }
-    const int64_t cap = kvd::stage_rows(d->head_dim) / (d->num_q_heads / d->num_kv_heads);
-    if (r > cap) r = cap;
+    if (fmt < KVD_TURBO4) {   // BF16 / FP8 stage the run's triples in LDS
+        const int64_t cap = kvd::stage_rows(d->head_dim) / (d->num_q_heads / d->num_kv_heads);
+        if (r > cap) r = cap;
+    }
     if (r > pl.P) r = pl.P;
     return r < 1 ? 1 : (int)r;
 }
@@ -169,17 +171,19 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.part_size = pl.part_size;
     p.P = pl.P;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
-    p.run = choose_run(d, pl);
+    p.run = choose_run(d, pl, fmt);
+    const int waves = kvd::waves_per_group(fmt);
     // token indices of every partition a workgroup can name must fit in int32
-    if (pl.P && ((int64_t)pl.P + 4LL * p.run) * pl.part_size > 0x7FFFFFFFLL) return KVD_ERR_SHAPE;
+    if (pl.P && ((int64_t)pl.P + (int64_t)waves * p.run) * pl.part_size > 0x7FFFFFFFLL)
+        return KVD_ERR_SHAPE;
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (phases & kPhase1) {
-        // four waves per workgroup, p.run partitions per wave
-        const int px = pl.P ? (pl.P + 4 * p.run - 1) / (4 * p.run) : 1;
+        // `waves` waves per workgroup, p.run partitions per wave
+        const int px = pl.P ? (pl.P + waves * p.run - 1) / (waves * p.run) : 1;
         const int64_t wgs = (int64_t)px * d->num_kv_heads * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);

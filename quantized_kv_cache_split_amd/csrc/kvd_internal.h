@@ -14,8 +14,11 @@ constexpr int kAutoSplitMin = 1024; // automatic split only from this many atten
 constexpr int kMaxGroup = 16;       // query heads per KV head one workgroup handles
 constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
 constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
+// Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
+// the codebook formats (one per CU, sharing 128 KB of conflict-free codebook tables).
+constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
 // (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
-// a wave's run of partitions is capped at stage_rows(D) / group.
+// a wave's run of partitions is capped at stage_rows(D) / group (BF16 / FP8).
 constexpr int stage_rows(int d) { return 4096 / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };

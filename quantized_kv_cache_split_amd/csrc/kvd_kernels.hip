@@ -40,6 +40,8 @@
 //   which is also the k-slot order of group j in the PV product.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvd_internal.h"
 #include "kvdecode.h"
 
@@ -55,8 +57,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kLutCopies = 32;   // copies of each codebook pair table (one per LDS bank pair)
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int FMT>
@@ -113,44 +114,43 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
 // fp16 dwords of the two levels (c[i0], c[i1]): .x = hi(c[i0]) | hi(c[i1]) << 16 and
 // .y = lo(c[i0]) | lo(c[i1]) << 16, with c ~= hi + lo.  One 8-byte LDS read per two indices.
 //
+// Bank-conflict-free layout: each table is stored kLutCopies = 32 times, entry e of copy c at
+// byte e * 256 + c * 8 (64 KB per table; the V table starts at byte 65536).  Lane l reads copy
+// l % 32, so whatever the indices, the 32 lanes of one LDS pass read 32 different bank pairs
+// (a single shared table costs about 3.3x more LDS cycles for random indices).  With
+// lanebase = (l % 32) * 8 (+ 65536 for the V table), the address of entry b (a byte of w) is
+// lanebase.byte0 | b << 8 | lanebase.byte2 << 16: one v_perm_b32.
+//
 // The reads land directly as "interleaved" MFMA operands: for eight indices e0..e7,
 //   a0 = {hi(e0,e1), lo(e0,e1), hi(e2,e3), lo(e2,e3)},  a1 = the same for e4..e7,
 // i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3].  Paired with a B operand whose slots repeat each
 // value, [x0 x1 x0 x1 x2 x3 x2 x3], one MFMA accumulates (hi + lo) * x for four elements; with
 // [y0 y1 0 0 y2 y3 0 0] it accumulates hi * y.
-// Byte K of w times 8 (the byte offset of an 8-byte table entry) in one VALU instruction:
-// gfx9 SDWA selects and zero-extends the byte as the shift's source operand.
 template <int K>
-__device__ __forceinline__ uint32_t byte_times8(uint32_t w) {
+__device__ __forceinline__ u32x2 lut_byte(const char* lds, uint32_t lanebase, uint32_t w) {
     static_assert(K >= 0 && K < 4, "byte index");
-    uint32_t r;
-    if constexpr (K == 0)
-        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0" : "=v"(r) : "v"(w));
-    else if constexpr (K == 1)
-        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1" : "=v"(r) : "v"(w));
-    else if constexpr (K == 2)
-        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2" : "=v"(r) : "v"(w));
-    else
-        asm("v_lshlrev_b32_sdwa %0, 3, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3" : "=v"(r) : "v"(w));
-    return r;
-}
-template <int K>
-__device__ __forceinline__ u32x2 lut_byte(const u32x2* lut, uint32_t w) {
-    return *reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(lut) + byte_times8<K>(w));
+    const uint32_t addr = __builtin_amdgcn_perm(w, lanebase, (12u << 24) | (2u << 16) | ((4u + K) << 8));
+    return *reinterpret_cast<const u32x2*>(lds + addr);
 }
 // 8 4-bit indices (index e at bits 4e of w).
-__device__ __forceinline__ void lut_nib8(const u32x2* lut, uint32_t w, u32x4& a0, u32x4& a1) {
-    const u32x2 e0 = lut_byte<0>(lut, w), e1 = lut_byte<1>(lut, w);
-    const u32x2 e2 = lut_byte<2>(lut, w), e3 = lut_byte<3>(lut, w);
+__device__ __forceinline__ void lut_nib8(const char* lds, uint32_t lanebase, uint32_t w,
+                                         u32x4& a0, u32x4& a1) {
+    const u32x2 e0 = lut_byte<0>(lds, lanebase, w), e1 = lut_byte<1>(lds, lanebase, w);
+    const u32x2 e2 = lut_byte<2>(lds, lanebase, w), e3 = lut_byte<3>(lds, lanebase, w);
     a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
     a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
 }
-// 8 3-bit indices (index e at bits 3e of the low 24 bits of f).
-__device__ __forceinline__ void lut_tri8(const u32x2* lut, uint32_t f, u32x4& a0, u32x4& a1) {
-    const u32x2 e0 = lut[f & 0x3Fu], e1 = lut[(f >> 6) & 0x3Fu];
-    const u32x2 e2 = lut[(f >> 12) & 0x3Fu], e3 = lut[(f >> 18) & 0x3Fu];
-    a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
-    a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
+// 8 3-bit indices (index e at bits 3e of the low 24 bits of f): 6-bit pair indices.
+__device__ __forceinline__ void lut_tri8(const char* lds, uint32_t lanebase, uint32_t f,
+                                         u32x4& a0, u32x4& a1) {
+    u32x2 e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t addr = (__builtin_amdgcn_ubfe(f, 6 * i, 6) << 8) | lanebase;
+        e[i] = *reinterpret_cast<const u32x2*>(lds + addr);
+    }
+    a0 = u32x4{e[0][0], e[0][1], e[1][0], e[1][1]};
+    a1 = u32x4{e[2][0], e[2][1], e[3][0], e[3][1]};
 }
 // The 24-bit field holding indices 8h..8h+7 of a 32-index, 3-bit group (w0..w2 = its 12 bytes).
 __device__ __forceinline__ uint32_t tri_field(uint32_t w0, uint32_t w1, uint32_t w2, int h) {
@@ -307,37 +307,48 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
 // partitions.
 template <int FMT, int D, bool CAP, int PF>
-__global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchParams p) {
+__global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel(const LaunchParams p) {
     constexpr bool kTurbo = is_turbo<FMT>();
+    constexpr int kW = waves_per_group(FMT);   // waves per workgroup
+    constexpr int kThr = 64 * kW;
     constexpr int KS = D / 32;   // QK MFMA steps (k = 32 head elements each)
     constexpr int VT = D / 16;   // PV MFMA tiles (16 head elements each)
     static_assert(!kTurbo || D == 128, "codebook formats are built for head_dim 128");
     using Raw = PairRaw<FMT, D>;
 
-    // Per-wave staging of finished (m, l, o) rows: a split wave stages the triples of the
-    // partitions it closes (row r * g + n for the r-th partition of its run, query n) and copies
-    // them to the workspace after its walk, so no global store joins the in-order stream of its
-    // loads; the unsplit merge uses rows 0..g-1.  Rows are D + 4 floats apart so the 16 query
-    // rows a ds_write_b128 touches start in different banks.
-    constexpr int SR = stage_rows(D);
+    // LDS.  BF16 / FP8 (4 waves, two workgroups per CU): per-wave staging of finished (m, l, o)
+    // rows -- a split wave stages the triples of the partitions it closes (row r * g + n for
+    // the r-th partition of its run, query n) and copies them to the workspace after its walk,
+    // so no global store joins the in-order stream of its loads; the unsplit merge uses rows
+    // 0..g-1.  Rows are D + 4 floats apart so the 16 query rows a ds_write_b128 touches start
+    // in different banks.  Codebook formats (8 waves, one workgroup per CU): the two
+    // conflict-free pair tables (128 KB, at LDS address 0), reused for the unsplit merge once
+    // every wave has finished its walk; these compute-bound waves write partials directly.
+    constexpr int SR = kTurbo ? kMaxGroup : stage_rows(D);
     constexpr int SD = D + 4;
-    // All LDS in one block, codebook tables first: their addresses then fit the 16-bit offset
-    // field of ds_read, so a table lookup costs one address instruction.
-    struct Lds {
-        u32x2 lut[2][kTurbo ? 256 : 1];          // K and V codebook pair tables
-        float rowscale[kMaxGroup];
-        float m[kWaves][SR];
-        float l[kWaves][SR];
-        float row[kTurbo ? kMaxGroup * D : 1];   // query rotation / output rotation
-        f32x4 o[kWaves][SR * SD / 4];
+    struct Merge {
+        float m[kW][SR];
+        float l[kW][SR];
+        f32x4 o[kW][SR * SD / 4];
     };
+    struct LdsStage {
+        Merge st;
+    };
+    struct LdsTurbo {
+        union {
+            u32x4 lut[2][256 * kLutCopies / 2];   // K table at byte 0, V table at byte 65536
+            Merge st;
+        } u;
+        float row[kMaxGroup * D];                 // query rotation / output rotation
+        float rowscale[kMaxGroup];
+    };
+    using Lds = typename std::conditional<kTurbo, LdsTurbo, LdsStage>::type;
     __shared__ Lds lds;
-    auto& sm_lut = lds.lut;
-    auto& sm_rowscale = lds.rowscale;
-    auto& sm_m = lds.m;
-    auto& sm_l = lds.l;
-    float* const sm_row = lds.row;
-    float (&sm_o)[kWaves][SR * SD] = *reinterpret_cast<float (*)[kWaves][SR * SD]>(&lds.o);
+    Merge& stg = [&]() -> Merge& { if constexpr (kTurbo) return lds.u.st; else return lds.st; }();
+    auto& sm_m = stg.m;
+    auto& sm_l = stg.l;
+    float (&sm_o)[kW][SR * SD] = *reinterpret_cast<float (*)[kW][SR * SD]>(&stg.o);
+    const char* const lds_bytes = reinterpret_cast<const char*>(&lds);
 
     // 1-D grid, KV head fastest, then sequence, then the partition slot x.  Workgroups are
     // handed to the eight XCDs round-robin by linear id, so this order spreads every
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     if (si.bad || si.L == 0) {
         if (xb == 0) {
             const float v = si.bad ? __builtin_nanf("") : 0.0f;
-            for (int i = tid; i < g * D; i += kThreads) out_rows[i] = v;
+            for (int i = tid; i < g * D; i += kThr) out_rows[i] = v;
         }
         return;
     }
@@ -363,8 +374,8 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     int lo, hi, part = 0, part_end = 0, part_first = 0;
     if (si.split) {
         const int plo = si.lo / p.part_size, phi = (si.L - 1) / p.part_size;
-        if (plo + xb * kWaves * p.run > phi) return;
-        part = part_first = plo + (xb * kWaves + wave) * p.run;
+        if (plo + xb * kW * p.run > phi) return;
+        part = part_first = plo + (xb * kW + wave) * p.run;
         const int pend = min(part + p.run, phi + 1);
         lo = max(si.lo, part * p.part_size);
         hi = min(si.L, pend * p.part_size);
@@ -373,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         if (xb != 0) return;
         const int pg0 = (si.lo / kPageTokens) & ~1, pg1 = (si.L - 1) / kPageTokens + 1;
         const int np = (pg1 - pg0 + 1) >> 1;
-        const int per = (np + kWaves - 1) / kWaves;
+        const int per = (np + kW - 1) / kW;
         lo = max(si.lo, (pg0 + 2 * per * wave) * kPageTokens);
         hi = min(si.L, (pg0 + 2 * per * (wave + 1)) * kPageTokens);
     }
@@ -387,6 +398,8 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     ln.v_sel = ln.j >> 1;
     ln.v_pos0 = 8 * (ln.j & 1);
     const int n = ln.n, j = ln.j;
+    const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;   // copy of this lane
+    const uint32_t kbase = lut_lane, vbase = lut_lane | 0x10000u;       // K / V table
 
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
@@ -406,23 +419,32 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
         const float ksc = pow2_normaliser(kmax), vsc = pow2_normaliser(vmax);
         {
-            const int t = tid;   // 256 threads, 256 entries
-            const int ki0 = t % kl, ki1 = (t / kl) % kl;
+            // 512 threads: thread t fills half the copies of entry t / 2 of both tables
+            static_assert(kThr == 2 * 256, "one thread pair per table entry");
+            const int e = tid >> 1, c0 = (tid & 1) * (kLutCopies / 2);
+            const int ki0 = e % kl, ki1 = (e / kl) % kl;
             uint32_t h, l;
             f16_hilo(p.codebook[ki0] * ksc, p.codebook[ki1] * ksc, h, l);
-            sm_lut[0][t] = u32x2{h, l};
-            f16_hilo(p.codebook[kl + (t & 15)] * vsc, p.codebook[kl + (t >> 4)] * vsc, h, l);
-            sm_lut[1][t] = u32x2{h, l};
+            const u32x4 kv = {h, l, h, l};
+            f16_hilo(p.codebook[kl + (e & 15)] * vsc, p.codebook[kl + (e >> 4)] * vsc, h, l);
+            const u32x4 vv = {h, l, h, l};
+#pragma unroll
+            for (int c = 0; c < kLutCopies / 2; c += 2) {
+                lds.u.lut[0][(e * kLutCopies + c0 + c) / 2] = kv;
+                lds.u.lut[1][(e * kLutCopies + c0 + c) / 2] = vv;
+            }
         }
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
-        for (int i = tid; i < g * D; i += kThreads) {
+        for (int i = tid; i < g * D; i += kThr) {
             const int r = i / D, d = i % D;
             const uint16_t qb = p.q[((size_t)b * p.Hq + (size_t)hk * g + r) * D + d];
-            sm_row[i] = bf16_bits_to_f32(qb) * p.sign[d];
+            lds.row[i] = bf16_bits_to_f32(qb) * p.sign[d];
         }
         __syncthreads();
-        fwht_rows<D>(sm_row, g, tid, kThreads);
-        for (int r = wave; r < g; r += kWaves) {       // per-row power-of-two normaliser
+        fwht_rows<D>(lds.row, g, tid, kThr);
+        float* const sm_row = lds.row;
+        auto& sm_rowscale = lds.rowscale;
+        for (int r = wave; r < g; r += kW) {       // per-row power-of-two normaliser
             float mx = fmaxf(fabsf(sm_row[r * D + lane]), fabsf(sm_row[r * D + 64 + lane]));
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
@@ -528,11 +550,11 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             for (int s = 0; s < KS; ++s) {
                 u32x4 x0, x1, y0, y1;
                 if constexpr (FMT == KVD_TURBO4) {
-                    lut_nib8(sm_lut[0], r.kx[s], x0, x1);
-                    lut_nib8(sm_lut[0], r.ky[s], y0, y1);
+                    lut_nib8(lds_bytes, kbase, r.kx[s], x0, x1);
+                    lut_nib8(lds_bytes, kbase, r.ky[s], y0, y1);
                 } else {
-                    lut_tri8(sm_lut[0], tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
-                    lut_tri8(sm_lut[0], tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
+                    lut_tri8(lds_bytes, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
+                    lut_tri8(lds_bytes, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
                 }
                 sx = mfma_f16(x0, qdup[s][0], sx);     // (k hi + k lo) * q hi
                 sx = mfma_f16(x1, qdup[s][1], sx);
@@ -655,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
                 u32x4 v0, v1;
-                lut_nib8(sm_lut[1], r.v[t], v0, v1);
+                lut_nib8(lds_bytes, vbase, r.v[t], v0, v1);
                 oacc[t] = mfma_f16(v0, pb0, oacc[t]);
                 oacc[t] = mfma_f16(v1, pb1, oacc[t]);
             }
@@ -698,16 +720,30 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
         if (k < npairs && tend >= part_end) {
             float lt = l_run + __shfl_xor(l_run, 16);
             lt += __shfl_xor(lt, 32);
-            const int row = (part - part_first) * g + n;
-            if (qlive && row < SR) {   // the host keeps run * g <= SR
-                const float osc = kTurbo ? oscale * sig_run : oscale;
-                const float sc = bad_ids ? __builtin_nanf("") : osc / lt;
+            const float osc = kTurbo ? oscale * sig_run : oscale;
+            const float sc = bad_ids ? __builtin_nanf("") : osc / lt;
+            const float lx = lt * fast_exp2(m_run - m_true);   // the sum relative to the exact max
+            if constexpr (kTurbo) {
+                if (qlive) {
+                    const size_t slot = (row0 + n) * p.P + part;
 #pragma unroll
-                for (int t = 0; t < VT; ++t)
-                    *reinterpret_cast<f32x4*>(&sm_o[wave][row * SD + 16 * t + 4 * j]) = oacc[t] * sc;
-                if (j == 0) {   // the sum restated relative to the exact max
-                    sm_m[wave][row] = m_true;
-                    sm_l[wave][row] = lt * fast_exp2(m_run - m_true);
+                    for (int t = 0; t < VT; ++t)
+                        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
+                    if (j == 0) {
+                        p.ws_m[slot] = m_true;
+                        p.ws_l[slot] = lx;
+                    }
+                }
+            } else {
+                const int row = (part - part_first) * g + n;
+                if (qlive && row < SR) {   // the host keeps run * g <= SR
+#pragma unroll
+                    for (int t = 0; t < VT; ++t)
+                        *reinterpret_cast<f32x4*>(&sm_o[wave][row * SD + 16 * t + 4 * j]) = oacc[t] * sc;
+                    if (j == 0) {
+                        sm_m[wave][row] = m_true;
+                        sm_l[wave][row] = lx;
+                    }
                 }
             }
             m_run = m_true = -INFINITY;
@@ -765,9 +801,9 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
 
     // ---- results ---------------------------------------------------------------------------
     if (si.split) {
+        if (kTurbo || !live) return;   // codebook formats wrote their triples directly
         // copy the run's staged triples to the workspace (this wave's own LDS rows: a
         // wavefront-scope fence orders the other lanes' writes before the reads)
-        if (!live) return;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -792,7 +828,9 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
     l_run += __shfl_xor(l_run, 32);
     if constexpr (kTurbo) oscale *= sig_run;
 
-    // unsplit: merge the four waves through LDS, then write the final rows
+    // unsplit: merge the waves through LDS, then write the final rows (the codebook formats'
+    // merge rows reuse the tables, so every wave must have finished its walk first)
+    if constexpr (kTurbo) __syncthreads();
     if (qlive) {
         if (j == 0) {
             sm_m[wave][n] = m_run;
@@ -804,28 +842,28 @@ __global__ __launch_bounds__(kThreads, 2) void partition_kernel(const LaunchPara
             for (int r = 0; r < 4; ++r) sm_o[wave][n * SD + 16 * t + 4 * j + r] = oacc[t][r] * oscale;
     }
     const bool wg_bad = __syncthreads_or(bad_ids ? 1 : 0) != 0;
-    for (int i = tid; i < g * D; i += kThreads) {
+    for (int i = tid; i < g * D; i += kThr) {
         const int r = i / D, d = i % D;
         float M = sm_m[0][r];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
+        for (int w = 1; w < kW; ++w) M = fmaxf(M, sm_m[w][r]);
         float wsum = 0.0f, acc = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kW; ++w) {
             const float sc = fast_exp2(sm_m[w][r] - M);   // 0 for waves without tokens
             wsum += sm_l[w][r] * sc;
             acc += sm_o[w][r * SD + d] * sc;
         }
         float o = acc / wsum;
         if (wg_bad) o = __builtin_nanf("");
-        if constexpr (kTurbo) sm_row[i] = o;
+        if constexpr (kTurbo) lds.row[i] = o;
         else out_rows[i] = o;
     }
     if constexpr (kTurbo) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
         __syncthreads();
-        fwht_rows<D>(sm_row, g, tid, kThreads);
+        fwht_rows<D>(lds.row, g, tid, kThr);
         const float rs = 1.0f / sqrtf((float)D);
-        for (int i = tid; i < g * D; i += kThreads) out_rows[i] = sm_row[i] * p.sign[i % D] * rs;
+        for (int i = tid; i < g * D; i += kThr) out_rows[i] = lds.row[i] * p.sign[i % D] * rs;
     }
 }
 
@@ -972,9 +1010,9 @@ template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
     constexpr int PF = prefetch_depth<FMT>();
     if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((partition_kernel<FMT, D, true, PF>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((partition_kernel<FMT, D, true, PF>), grid, dim3(64 * waves_per_group(FMT)), 0, s, p);
     else
-        hipLaunchKernelGGL((partition_kernel<FMT, D, false, PF>), grid, dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((partition_kernel<FMT, D, false, PF>), grid, dim3(64 * waves_per_group(FMT)), 0, s, p);
     return hipGetLastError();
 }
 template <int FMT, int D>
