@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per partition-kernel launch")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "hbm_traffic.json"),
+                    help="JSON with HBM bytes per partition-kernel launch measured by rocprofv3 "
+                         "(used only while the kernel sources are unchanged since)")
     return ap.parse_args()
 
 
@@ -82,6 +83,32 @@ def cpu_baseline(inp, seconds):
             "kind": "oracle",
             "sample": f"{pairs} of {len(order)} (sequence, KV head) pairs, {done_bytes / 1e6:.1f} MB "
                       f"of KV in {dt:.1f} s (NumPy fp64 oracle, host cores {os.cpu_count()})"}
+
+
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_split_amd", "csrc", f)
+                  for f in ("kvd_kernels.hip", "kvd_api.cpp", "kvd_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the HIP kernel and launch sources (ties counter readings to a kernel)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path, workload):
+    """HBM bytes per partition-kernel launch from the counter record, or None when the record
+    is missing, covers another workload or predates the current kernel sources."""
+    if not path or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    entry = rec.get("workloads", {}).get(workload)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 def kvgen_bytes_per_token_head(s):
@@ -182,11 +209,7 @@ def main():
     mean_call = float(t_call.mean())
     value = kv_bytes / mean_call / 1e9
     achieved = kv_bytes / float(t_part.mean()) / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        rec = json.load(open(args.traffic))
-        if rec.get("workload") == args.workload:
-            traffic = rec.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(args.traffic, args.workload)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
