@@ -93,13 +93,17 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 // Max over the four 16-lane groups (rows) of a wave, returned in every lane.  gfx950's
 // permlane swaps exchange rows 1<->0, 3<->2 (16) and rows 2,3<->0,1 (32) in registers, without
 // LDS traffic.
+// The max is v_max_f32 written out: the swap results arrive as integers, and fmaxf on them
+// would first quiet possible signalling NaNs (an extra v_max per operand); nothing here
+// produces one.
 __device__ __forceinline__ float max_over_groups(float v) {
     const uint32_t u = __float_as_uint(v);
     const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const float m1 = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const uint32_t w = __float_as_uint(m1);
+    uint32_t w, r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(w) : "v"(a[0]), "v"(a[1]));
     const auto c = __builtin_amdgcn_permlane32_swap(w, w, false, false);
-    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(c[0]), "v"(c[1]));
+    return __uint_as_float(r);
 }
 
 // 4 E4M3FN codes (little-endian bytes of w) -> 4 bf16 in two packed pairs.  Exact: every
@@ -530,6 +534,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         const bool full = (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
 
         f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == KVD_BF16) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
@@ -556,15 +561,18 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                     lut_tri8(lds_bytes, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
                     lut_tri8(lds_bytes, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
                 }
+                // two accumulator chains per tile halve the dependent-MFMA latency
                 sx = mfma_f16(x0, qdup[s][0], sx);     // (k hi + k lo) * q hi
-                sx = mfma_f16(x1, qdup[s][1], sx);
+                sx2 = mfma_f16(x1, qdup[s][1], sx2);
                 sx = mfma_f16(x0, qlo0[s][0], sx);     // k hi * q lo
-                sx = mfma_f16(x1, qlo0[s][1], sx);
+                sx2 = mfma_f16(x1, qlo0[s][1], sx2);
                 sy = mfma_f16(y0, qdup[s][0], sy);
-                sy = mfma_f16(y1, qdup[s][1], sy);
+                sy2 = mfma_f16(y1, qdup[s][1], sy2);
                 sy = mfma_f16(y0, qlo0[s][0], sy);
-                sy = mfma_f16(y1, qlo0[s][1], sy);
+                sy2 = mfma_f16(y1, qlo0[s][1], sy2);
             }
+            sx += sx2;
+            sy += sy2;
         }
 
         float z[8];
