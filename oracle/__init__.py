@@ -1,6 +1,7 @@
 """Oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
 
-Plain fp64 CPU definition (``attention``) and a 40-digit ``decimal`` brute force (``brute``).
+Plain fp64 CPU definition of decode attention (``attention``), a 40-digit ``decimal`` brute
+force (``brute``) and the cache writer that stores new tokens (``encode``).
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
 this package; the GPU library never does, and the two share no code.
 """
@@ -21,3 +22,4 @@ from .attention import (  # noqa: F401
     unpack_le,
     unrotate,
 )
+from . import encode  # noqa: F401,E402
