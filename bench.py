@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, time a plain device-to-device copy of this "
                          "many MiB (calibrates HBM byte counters against a known size)")
+    ap.add_argument("--append", type=int, default=0, metavar="T",
+                    help="instead of decode attention, time the KV append (quantize-on-write) "
+                         "of T new tokens per sequence into the workload's cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -136,6 +139,61 @@ def copy_probe(mib, steps):
                       "copy_gbps_read_plus_write": round(2 * n / dt / 1e9, 2)}), flush=True)
 
 
+def append_bench(args):
+    """KV append: T new fp32 tokens per sequence (K and V, all KV heads) encoded into the
+    workload's paged cache.  Algorithmic bytes per (token, KV head): the fp32 K and V read
+    (8 D) plus the cache bytes written (K and V codes, and for the codebook formats 8 bytes of
+    norms).  The new tokens overwrite the last T of each sequence (their pages are mapped)."""
+    import torch
+
+    import kvgen
+    import quantized_kv_cache_split_amd as kvd
+    from kvgen.torch_io import dims_kwargs, to_torch
+
+    spec = kvgen.SPECS[args.workload]
+    inp = kvgen.make_inputs(spec)
+    t = to_torch(inp, "cuda:0")
+    T = args.append
+    B, Hkv, D = spec.num_seqs, spec.num_kv_heads, spec.head_dim
+    dims = kvd.Dims(**dims_kwargs(inp, 0))
+    g = torch.Generator(device="cuda:0").manual_seed(1)
+    kn = torch.randn((B, T, Hkv, D), generator=g, device="cuda:0", dtype=torch.float32)
+    vn = torch.randn((B, T, Hkv, D), generator=g, device="cuda:0", dtype=torch.float32)
+    pos = (t["context_lens"] - T).clamp(min=0).to(torch.int32)
+    call = (dims, spec.fmt, kn, vn, t["block_table"], pos, T, t["k_cache"], t["v_cache"],
+            t["scales"], t["codebook"], t["sign_pattern"])
+    flush = torch.ones(64 << 20, dtype=torch.int64, device="cuda:0")
+    sink = torch.empty(1, dtype=torch.int64, device="cuda:0")
+    for _ in range(args.warmup):
+        kvd.append_kv(*call)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in ev:
+        torch.sum(flush, dim=0, keepdim=True, out=sink)
+        e[0].record()
+        kvd.append_kv(*call)
+        e[1].record()
+    torch.cuda.synchronize()
+    ts = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    per = 8 * D + kvgen.kv_bytes_per_token_head(spec.fmt, D)
+    nbytes = B * T * Hkv * per
+    mean = float(ts.mean())
+    res = {"metric": "kv append (quantize-on-write): GB/s of fp32 input read + cache written",
+           "value": round(nbytes / mean / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(mean * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32->" + spec.fmt, "data": "synthetic",
+           "config": {"workload": f"{args.workload}: {spec.name}", "new_tokens_per_seq": T,
+                      "num_seqs": B, "num_kv_heads": Hkv, "head_dim": D,
+                      "bytes_per_token_head": per, "bytes_per_call": nbytes},
+           "tokens_per_s": round(B * T / mean, 1),
+           "ms_per_step_p10_p50_p90": [round(float(np.percentile(ts, q)) * 1e3, 4) for q in (10, 50, 90)],
+           "roofline": {"bound": "hbm", "achieved": round(nbytes / mean / 1e9, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(nbytes / mean / 1e9 / HBM_PEAK_GBS, 4), "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,6 +204,9 @@ def main():
 
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
+        return
+    if args.append:
+        append_bench(args)
         return
 
     import torch

@@ -184,6 +184,38 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
                        int32_t seq, int32_t kv_head, int32_t token_begin, int32_t n_tokens,
                        float* out, void* stream);
 
+/* KV append (quantize-on-write): stores n_new new tokens of every sequence in the paged cache,
+ * in the layout above, so the decode entry points read them back.  Sources: the attention.rs
+ * README "KV Cache Formats" table (the four storage formats) and the compressed-cache recipe
+ * (each token vector is flipped by the +-1 sign pattern, transformed by the orthonormal
+ * Walsh-Hadamard transform, normalised by its fp32 L2 norm, stored per token, and each
+ * coordinate replaced by the index of the nearest codebook level, indices bit-packed
+ * little-endian); turboquant-rs 0.4.1 src/cache/cuda/attention.rs reads those packed indices,
+ * per-token scales, the sign pattern and the codebook.
+ *   k_new, v_new  fp32 [B][n_new][Hkv][D], device; 8-byte aligned
+ *   block_table   int32 [B][max_blocks_per_seq]; must already map the pages of the new tokens
+ *   positions     int32 [B]: new token i of sequence b is token positions[b] + i (its page is
+ *                 block_table[b][(positions[b] + i) / 16], slot (positions[b] + i) % 16)
+ *   n_new         tokens per sequence in this call (>= 0; 0 does nothing)
+ *   k_cache, v_cache  the pools, updated in place (other tokens' bytes are preserved)
+ *   scales        KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv] per-head scales
+ *                 (read); Turbo: fp32 per-token norms [2][num_pool_blocks][Hkv][16] (written)
+ *   codebook, sign_pattern  Turbo: as for kvd_decode_attn_paged; else unused
+ * Codes, decided exactly (readings where the pages are silent):
+ *   BF16  round to nearest even; NaN stored as 0x7FC0.
+ *   FP8   E4M3FN(fp32(x / scale)), round to nearest even, saturating to +-448; NaN as 0x7F.
+ *   Turbo r = H (s * x) / sqrt(D) in fp64; norm = fp32(sqrt(sum x_i^2)), the fp64 sum taken as
+ *         a pairwise tree over adjacent elements; u = r / norm in fp64; index = the number of
+ *         level midpoints (c_k + c_{k+1}) / 2 below u (a tie takes the lower level); a zero
+ *         vector stores norm 0 and the level nearest 0.
+ * Tokens whose page index is out of range or whose page id lies outside [0, num_pool_blocks)
+ * are skipped (nothing written).  Different tokens of one call may share pages; calls that
+ * overlap in time on different streams must not write the same page. */
+int kvd_append_kv(const kvd_dims* dims, int fmt, const float* k_new, const float* v_new,
+                  const int32_t* block_table, const int32_t* positions, int32_t n_new,
+                  void* k_cache, void* v_cache, float* scales, const float* codebook,
+                  const float* sign_pattern, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* kvd_status_str(int status);
 

@@ -185,7 +185,8 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
 
     k_new, v_new: fp32 [B][T][Hkv][D]; new token i of sequence b is token positions[b] + i,
     stored in page block_table[b][(positions[b] + i) // 16], slot (positions[b] + i) % 16.
-    Pages whose id lies outside the pool are skipped.  Returns (k_cache, v_cache, scales);
+    Tokens whose page index lies past the block table row, or whose page id lies outside the
+    pool, are skipped.  Returns (k_cache, v_cache, scales);
     for the rotated formats the per-token norms go to scales [2][pool][Hkv][16]."""
     k_cache = np.array(k_cache, copy=True)
     v_cache = np.array(v_cache, copy=True)
@@ -197,6 +198,8 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
     for b in range(B):
         for i in range(T):
             tok = int(positions[b]) + i
+            if tok < 0 or tok // BLOCK >= len(block_table[b]):
+                continue
             phys = int(block_table[b][tok // BLOCK])
             slot = tok % BLOCK
             if phys < 0 or phys >= pool:

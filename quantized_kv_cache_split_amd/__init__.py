@@ -67,6 +67,12 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_void_p]
         lib.kvd_dequant_gather.restype = ctypes.c_int
+        lib.kvd_append_kv.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p]
+        lib.kvd_append_kv.restype = ctypes.c_int
         lib.kvd_status_str.argtypes = [ctypes.c_int]
         lib.kvd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -150,6 +156,18 @@ def dequant_gather(dims, fmt, is_v, cache, scales, codebook, block_table, seq, k
     if st != 0:
         raise KvdError(st, "kvd_dequant_gather")
     return out
+
+
+def append_kv(dims, fmt, k_new, v_new, block_table, positions, n_new, k_cache, v_cache, scales,
+              codebook=None, sign_pattern=None, stream=None):
+    """Write n_new new tokens per sequence (k_new / v_new fp32 [B][n_new][Hkv][D]) into the
+    paged cache in place (kvd_append_kv)."""
+    st = load().kvd_append_kv(ctypes.byref(dims), _fmt(fmt), _ptr(k_new), _ptr(v_new),
+                              _ptr(block_table), _ptr(positions), int(n_new), _ptr(k_cache),
+                              _ptr(v_cache), _ptr(scales), _ptr(codebook), _ptr(sign_pattern),
+                              _stream(stream))
+    if st != 0:
+        raise KvdError(st, "kvd_append_kv")
 
 
 load()

@@ -273,6 +273,47 @@ int kvd_dequant_gather(const kvd_dims* d, int fmt, int is_v, const void* cache,
                                                                                  : KVD_ERR_HIP;
 }
 
+int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v_new,
+                  const int32_t* block_table, const int32_t* positions, int32_t n_new,
+                  void* k_cache, void* v_cache, float* scales, const float* codebook,
+                  const float* sign_pattern, void* stream) {
+    int st = check_dims(d, fmt);
+    if (st != KVD_OK) return st;
+    if (n_new < 0) return KVD_ERR_SHAPE;
+    if (!k_new || !v_new || !block_table || !positions || !k_cache || !v_cache) return KVD_ERR_NULL;
+    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (fmt >= KVD_TURBO4 && (!codebook || !sign_pattern)) return KVD_ERR_NULL;
+    if (!aligned(k_new, 8) || !aligned(v_new, 8) || !aligned(block_table, 4) ||
+        !aligned(positions, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        (scales && !aligned(scales, 4)) || (codebook && !aligned(codebook, 4)) ||
+        (sign_pattern && !aligned(sign_pattern, 4)))
+        return KVD_ERR_ALIGN;
+    if ((int64_t)d->num_seqs * n_new * d->num_kv_heads > ((int64_t)1 << 33)) return KVD_ERR_SHAPE;
+    if (d->num_seqs == 0 || n_new == 0) return KVD_OK;
+    kvd::AppendParams p{};
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.bt = block_table;
+    p.pos = positions;
+    p.k = static_cast<uint8_t*>(k_cache);
+    p.v = static_cast<uint8_t*>(v_cache);
+    p.scales = scales;
+    p.codebook = codebook;
+    p.sign = sign_pattern;
+    p.k_chunk = k_chunk_bytes(fmt, d->head_dim);
+    p.v_chunk = v_chunk_bytes(fmt, d->head_dim);
+    p.fmt = fmt;
+    p.B = d->num_seqs;
+    p.T = n_new;
+    p.Hkv = d->num_kv_heads;
+    p.D = d->head_dim;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.pool = d->num_pool_blocks;
+    p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    return kvd::launch_append(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KVD_OK
+                                                                                : KVD_ERR_HIP;
+}
+
 const char* kvd_status_str(int status) {
     switch (status) {
         case KVD_OK: return "ok";

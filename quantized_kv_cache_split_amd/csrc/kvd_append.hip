@@ -1,0 +1,176 @@
+// KV append (quantize-on-write) for the paged cache on gfx950: stores new tokens in the layout
+// the decode kernels read (include/kvdecode.h documents both).
+//
+// Formats as in the attention.rs README "KV Cache Formats" table (BF16, FP8 E4M3, Turbo4 and
+// Turbo3 with the Walsh-Hadamard rotation); the rotated-codebook recipe is the one the
+// compressed-cache workload states: sign flip, orthonormal Walsh-Hadamard transform, fp32
+// L2 norm stored per token, nearest Lloyd-Max level per coordinate, little-endian bit packing
+// (turboquant-rs 0.4.1 src/cache/cuda/attention.rs reads exactly these: packed indices, per-
+// token scales, a sign pattern and a codebook).
+//
+// One wavefront per (sequence, new token, KV head); lane l owns elements 2l and 2l + 1
+// (D = 128) or l (D = 64).  Every decision that picks a code is taken exactly:
+//   BF16   round to nearest even on the fp32 bit pattern; NaN -> 0x7FC0;
+//   FP8    q = x / scale in one correctly rounded fp32 division, then round to nearest even
+//          OCP E4M3FN on the bit pattern, saturating to +-448; NaN -> 0x7F;
+//   Turbo  the Hadamard butterflies in fp64 (exact for fp32 inputs: every partial sum of 128
+//          fp32 values with +-1 weights fits the 53-bit significand unless their exponents
+//          differ by more than 2^22), r = y / sqrt(D); the norm is an fp64 sum of the squares
+//          taken as a pairwise tree (adjacent elements, then adjacent lanes by xor shuffles),
+//          its square root rounded to fp32; u = r / norm (fp64) and the index counts the
+//          level midpoints (c_k + c_{k+1}) / 2 strictly below u (a tie takes the lower level).
+// Bytes that hold codes of other tokens (the 4-bit V rows: two tokens per byte) are updated
+// with vector atomics (clear the nibble, then set it), so concurrent tokens never race.
+#include <math.h>
+
+#include "kvd_internal.h"
+#include "kvdecode.h"
+
+namespace kvd {
+namespace {
+
+constexpr int kAppendWaves = 4;
+
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+    const uint32_t b = __float_as_uint(x);
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating to +-448.
+__device__ __forceinline__ uint32_t e4m3fn_rne(float q) {
+    const uint32_t b = __float_as_uint(q);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return 0x7Fu;                  // NaN
+    if (a >= 0x43E00000u) return sign | 0x7Eu;          // |q| >= 448 (and infinity)
+    if (a < 0x3C800000u)                                // |q| < 2^-6: multiples of 2^-9
+        return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // exponent | 3 mantissa bits
+    r -= (127u - 7u) << 3;                                  // rebias
+    return sign | (r < 0x7Eu ? r : 0x7Eu);
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = __shfl_xor((uint32_t)u, m), hi = __shfl_xor((uint32_t)(u >> 32), m);
+    return __longlong_as_double(((uint64_t)hi << 32) | lo);
+}
+
+__global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendParams p) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kAppendWaves + (threadIdx.x >> 6);
+    if (item >= (int64_t)p.B * p.T * p.Hkv) return;
+    const int hk = (int)(item % p.Hkv);
+    const int i = (int)((item / p.Hkv) % p.T);
+    const int b = (int)(item / ((int64_t)p.Hkv * p.T));
+    const int64_t tok = (int64_t)p.pos[b] + i;
+    if (tok < 0 || tok >= (int64_t)kPageTokens * p.max_blocks) return;       // no page for it
+    const int phys = p.bt[(size_t)b * p.max_blocks + tok / kPageTokens];
+    if (phys < 0 || phys >= p.pool) return;                                 // not a pool page
+    const int t = (int)(tok % kPageTokens);
+    const size_t head = (size_t)phys * p.Hkv + hk;
+    const size_t row = ((size_t)b * p.T + i) * p.Hkv + hk;
+
+    for (int which = 0; which < 2; ++which) {
+        const float* src = (which ? p.v_new : p.k_new) + row * p.D;
+        uint8_t* chunk = (which ? p.v : p.k) + head * (which ? p.v_chunk : p.k_chunk);
+        if (p.fmt == KVD_BF16 || p.fmt == KVD_FP8_E4M3) {
+            const float scale = p.fmt == KVD_FP8_E4M3 ? p.scales[which * p.Hkv + hk] : 1.0f;
+            for (int d = lane; d < p.D; d += 64) {
+                const float x = src[d];
+                if (p.fmt == KVD_BF16) {
+                    const uint16_t c = (uint16_t)bf16_rne(x);
+                    uint16_t* c16 = reinterpret_cast<uint16_t*>(chunk);
+                    if (which == 0) c16[((d / 8) * kPageTokens + t) * 8 + d % 8] = c;   // [D/8][16][8]
+                    else c16[d * kPageTokens + t] = c;                                   // [D][16]
+                } else {
+                    const uint8_t c = (uint8_t)e4m3fn_rne(__fdiv_rn(x, scale));
+                    if (which == 0) chunk[((d / 16) * kPageTokens + t) * 16 + d % 16] = c;  // [D/16][16][16]
+                    else chunk[d * kPageTokens + t] = c;                                     // [D][16]
+                }
+            }
+            continue;
+        }
+
+        // ---- rotated codebook (D = 128): lane owns elements e0 = 2 lane, e1 = 2 lane + 1 ----
+        const int e0 = 2 * lane;
+        const float x0 = src[e0], x1 = src[e0 + 1];
+        double y0 = (double)(x0 * p.sign[e0]), y1 = (double)(x1 * p.sign[e0 + 1]);
+        {   // stage h = 1 inside the lane, then h = 2 .. 64 across lanes (partner lane ^ h / 2)
+            const double a = y0, c = y1;
+            y0 = a + c;
+            y1 = a - c;
+        }
+#pragma unroll
+        for (int h = 2; h < 128; h <<= 1) {
+            const int m = h >> 1;
+            const double o0 = shfl_xor_f64(y0, m), o1 = shfl_xor_f64(y1, m);
+            const bool upper = (e0 & h) != 0;
+            y0 = upper ? o0 - y0 : y0 + o0;
+            y1 = upper ? o1 - y1 : y1 + o1;
+        }
+        const double rs = sqrt(128.0);
+        const double r0 = y0 / rs, r1 = y1 / rs;
+        double n2 = (double)x0 * (double)x0 + (double)x1 * (double)x1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) n2 += shfl_xor_f64(n2, m);
+        const float norm = (float)sqrt(n2);
+        const double nd = (double)norm;
+        const double u0 = nd > 0.0 ? r0 / nd : 0.0, u1 = nd > 0.0 ? r1 / nd : 0.0;
+
+        const int kl = 1 << p.kbits;
+        const int nlev = which ? 16 : kl;
+        const float* lv = p.codebook + (which ? kl : 0);
+        uint32_t i0 = 0, i1 = 0;
+        for (int k = 0; k + 1 < nlev; ++k) {
+            const double mid = ((double)lv[k] + (double)lv[k + 1]) / 2.0;
+            i0 += u0 > mid ? 1u : 0u;
+            i1 += u1 > mid ? 1u : 0u;
+        }
+        if (lane == 0)
+            p.scales[(size_t)which * p.pool * p.Hkv * kPageTokens + head * kPageTokens + t] = norm;
+
+        if (which == 1) {   // V [D][8 B]: nibble t of rows e0 and e0 + 1, shared bytes -> atomics
+            uint32_t* words = reinterpret_cast<uint32_t*>(chunk);
+            const int sh = 4 * (t % 8);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int d = e0 + k;
+                uint32_t* w = words + d * 2 + t / 8;
+                atomicAnd(w, ~(0xFu << sh));
+                atomicOr(w, (k ? i1 : i0) << sh);
+            }
+        } else if (p.kbits == 4) {   // K [D/32][16][16 B]: the lane's byte, index pair e0, e0+1
+            const int g = e0 / 32;
+            chunk[(g * kPageTokens + t) * 16 + (e0 % 32) / 2] = (uint8_t)(i0 | (i1 << 4));
+        } else {   // K [D/32][16][12 B]: 32 3-bit indices per group, 6 bits per lane
+            const int g = e0 / 32, pos6 = 6 * (lane % 16);     // bit offset inside the group
+            const uint32_t v6 = i0 | (i1 << 3);
+            uint32_t w[3] = {0u, 0u, 0u};
+            const int wk = pos6 / 32, off = pos6 % 32;
+            w[wk] = v6 << off;
+            if (off > 26) w[wk + 1] = v6 >> (32 - off);
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) w[k] |= __shfl_xor(w[k], m);
+            const int lg = lane % 16;
+            if (lg < 3) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(chunk + (g * kPageTokens + t) * 12);
+                dst[lg] = lg == 0 ? w[0] : (lg == 1 ? w[1] : w[2]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendParams& p, hipStream_t s) {
+    const int64_t items = (int64_t)p.B * p.T * p.Hkv;
+    const int64_t blocks = (items + kAppendWaves - 1) / kAppendWaves;
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64 * kAppendWaves), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace kvd

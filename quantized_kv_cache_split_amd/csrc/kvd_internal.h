@@ -61,9 +61,25 @@ struct GatherParams {
     int32_t fmt, is_v, Hkv, D, max_blocks, pool, seq, kv_head, t0, n, kbits;
 };
 
-// Launchers (kvd_kernels.hip).  Return hipSuccess or the launch error.
+// Arguments of the KV append (quantize-on-write) kernel.
+struct AppendParams {
+    const float* k_new;       // [B][T][Hkv][D] fp32
+    const float* v_new;
+    const int32_t* bt;        // [B][max_blocks]
+    const int32_t* pos;       // [B] token index of each sequence's first new token
+    uint8_t* k;               // K pool
+    uint8_t* v;               // V pool
+    float* scales;            // FP8: [2][Hkv] (read); codebook formats: [2][pool][Hkv][16] (written)
+    const float* codebook;    // codebook formats: K levels then 16 V levels
+    const float* sign;        // codebook formats: [D]
+    int64_t k_chunk, v_chunk;
+    int32_t fmt, B, T, Hkv, D, max_blocks, pool, kbits;
+};
+
+// Launchers (kvd_kernels.hip, kvd_append.hip).  Return hipSuccess or the launch error.
 hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace kvd

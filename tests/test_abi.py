@@ -122,3 +122,25 @@ def test_gather_arg_errors():
     assert g(seq=16) == -2 and g(head=8) == -2 and g(t0=-1) == -2 and g(t0=32768, n=1) == -2
     assert g(fmt=9) == -3
     assert g(n=0) == 0
+
+
+def append_call(d=None, fmt=0, **over):
+    a = dict(k=FAKE, v=FAKE, bt=FAKE, pos=FAKE, n=4, kc=FAKE, vc=FAKE, scales=FAKE, cb=FAKE,
+             sign=FAKE)
+    a.update(over)
+    lib = kvd.load()
+    return lib.kvd_append_kv(ctypes.byref(d or dims()), fmt, a["k"], a["v"], a["bt"], a["pos"],
+                             a["n"], a["kc"], a["vc"], a["scales"], a["cb"], a["sign"], None)
+
+
+def test_append_arg_errors():
+    assert append_call(fmt=5) == -3
+    assert append_call(n=-1) == -2
+    assert append_call(dims(head_dim=96)) == -2
+    for arg in ("k", "v", "bt", "pos", "kc", "vc"):
+        assert append_call(**{arg: None}) == -1, arg
+    assert append_call(fmt=1, scales=None) == -1
+    assert append_call(fmt=2, cb=None) == -1 and append_call(fmt=3, sign=None) == -1
+    assert append_call(fmt=0, scales=None, cb=None, sign=None, n=0) == 0    # BF16 needs neither
+    assert append_call(k=FAKE + 4) == -4 and append_call(kc=FAKE + 8) == -4
+    assert append_call(n=0) == 0 and append_call(dims(num_seqs=0)) == 0    # nothing launched
