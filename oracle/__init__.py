@@ -7,6 +7,7 @@ this package; the GPU library never does, and the two share no code.
 """
 from .attention import (  # noqa: F401
     E4M3FN_TABLE,
+    alibi_bias,
     attend,
     attended_range,
     bf16_to_f64,

@@ -19,6 +19,8 @@ Readings taken where the pages are silent (the header of the library states the 
   * window W: the query sees keys j in [L - W, L) (the W most recent, itself included);
   * softcap c > 0: logit x = scale * q.k is replaced by c * tanh(x / c) before the softmax;
   * GQA: query head h reads KV head floor(h / (Hq / Hkv));
+  * ALiBi (the "ALiBi slopes" feature of the attention.rs README): query head h at position
+    L - 1 adds slope_h * (j - (L - 1)) to its logit for key j, after the softcap;
   * rotated codebook: stored vector = norm * codebook[idx] in the rotated domain; the original
     vector is diag(s) H (that) / sqrt(D), H the Sylvester-order Hadamard matrix;
   * FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN) times one fp32 scale per KV head.
@@ -171,23 +173,31 @@ def attended_range(L: int, W: int) -> tuple[int, int]:
     return (max(0, L - W) if W > 0 else 0), L
 
 
-def logits(q: np.ndarray, k: np.ndarray, softmax_scale, softcap) -> np.ndarray:
-    """z = scale * q K^T, then cap * tanh(z / cap) when cap > 0 (fp64; scale is the fp32
-    value the caller passes, widened)."""
+def logits(q: np.ndarray, k: np.ndarray, softmax_scale, softcap, bias=None) -> np.ndarray:
+    """z = scale * q K^T, then cap * tanh(z / cap) when cap > 0, then + bias [g, n] (the
+    ALiBi term) when given (fp64; scale is the fp32 value the caller passes, widened)."""
     z = float(np.float32(softmax_scale)) * (q @ k.T)
     cap = float(np.float32(softcap))
     if cap > 0:
         z = cap * np.tanh(z / cap)
+    if bias is not None:
+        z = z + bias
     return z
 
 
-def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale, softcap):
+def alibi_bias(slopes, L: int, t0: int, t1: int) -> np.ndarray:
+    """slope_h * (j - (L - 1)) for keys j in [t0, t1): [g, n] fp64 (slopes fp32, widened)."""
+    s = np.asarray(slopes, dtype=np.float32).astype(np.float64)
+    return s[:, None] * (np.arange(t0, t1, dtype=np.float64) - (L - 1))[None, :]
+
+
+def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, softmax_scale, softcap, bias=None):
     """Exact softmax attention of query rows q [g, D] over keys k and values v [n, D].
 
     Returns (m, l, o): the max logit m [g], the sum l = sum_j exp(z_j - m) [g] and the
     normalised output o = sum_j exp(z_j - m) v_j / l [g, D].
     """
-    z = logits(q, k, softmax_scale, softcap)
+    z = logits(q, k, softmax_scale, softcap, bias)
     m = z.max(axis=1)
     p = np.exp(z - m[:, None])
     l = p.sum(axis=1)
@@ -224,11 +234,12 @@ def _q_rows(q_bits, b, h0, g):
 
 def decode_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
                      sign, softmax_scale, window, softcap, num_kv_heads, head_dim,
-                     seqs=None, kv_heads=None, chunk=8192):
+                     seqs=None, kv_heads=None, chunk=8192, alibi=None):
     """out[b, h] = softmax(scale * q_h K^T) V over the attended keys of sequence b, fp64.
 
     q: bf16 bits [B, Hq, D]; caches in the paged layout; context_lens / window int [B]
-    (window None -> no window).  Rows of sequences with context length 0 are zero.
+    (window None -> no window); alibi: per-query-head slopes [Hq] or None.  Rows of sequences
+    with context length 0 are zero.
     ``seqs`` / ``kv_heads`` restrict the work to a sample (other rows are left NaN).
     The keys are processed ``chunk`` tokens at a time and merged with the LSE rule, which is
     the same sum in another order (bounded memory for long contexts).
@@ -254,7 +265,8 @@ def decode_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales
                                codebook=codebook, sign=sign)
                 vv = gather_kv(fmt, "v", v_cache, block_table[b], hk, t0, t1, D, scales=scales,
                                codebook=codebook, sign=sign)
-                parts.append(attend(qr, kk, vv, softmax_scale, softcap))
+                bias = None if alibi is None else alibi_bias(np.asarray(alibi)[rows], L, t0, t1)
+                parts.append(attend(qr, kk, vv, softmax_scale, softcap, bias))
             ms, ls, os_ = zip(*parts)
             out[b, rows] = lse_merge(ms, ls, os_)
     return out
@@ -262,7 +274,7 @@ def decode_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales
 
 def partition_partials(q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
                        sign, softmax_scale, window, softcap, num_kv_heads, head_dim,
-                       partition_size, b, hk, rotated=False):
+                       partition_size, b, hk, rotated=False, alibi=None):
     """Per-partition triples for one (sequence, KV head): list of (lo, hi, m [g], l [g], o [g, D]).
 
     rotated=True returns o in the storage (rotated) domain for the codebook formats, which is
@@ -278,7 +290,10 @@ def partition_partials(q, k_cache, v_cache, block_table, context_lens, fmt, scal
                        codebook=codebook, sign=sign)
         vv = gather_kv(fmt, "v", v_cache, block_table[b], hk, lo, hi, head_dim, scales=scales,
                        codebook=codebook, sign=sign)
-        m, l, o = attend(qr, kk, vv, softmax_scale, softcap)
+        bias = None
+        if alibi is not None:
+            bias = alibi_bias(np.asarray(alibi)[hk * g: hk * g + g], int(context_lens[b]), lo, hi)
+        m, l, o = attend(qr, kk, vv, softmax_scale, softcap, bias)
         if rotated and fmt.startswith("turbo"):
             d = head_dim
             h = sylvester_hadamard(d).astype(np.float64)

@@ -98,8 +98,8 @@ def _tanh(x: Decimal) -> Decimal:
 
 def brute_decode_attention(q_bits, k_cache, v_cache, block_table, context_lens, fmt, scales,
                            codebook, sign, softmax_scale, window, softcap, num_kv_heads,
-                           head_dim):
-    """Nested lists out[b][h][d] of Decimal."""
+                           head_dim, alibi=None):
+    """Nested lists out[b][h][d] of Decimal.  ``alibi``: per-query-head slopes or None."""
     B, Hq, D = len(q_bits), len(q_bits[0]), head_dim
     g = Hq // num_kv_heads
     kc = k_cache.reshape(-1)
@@ -132,6 +132,8 @@ def brute_decode_attention(q_bits, k_cache, v_cache, block_table, context_lens, 
                 x = scale * sum(qv[d] * keys[hk, j][d] for d in range(D))
                 if cap > 0:
                     x = cap * _tanh(x / cap)
+                if alibi is not None:
+                    x += _f32(alibi[h]) * (j - (L - 1))
                 z[j] = x
             m = max(z.values())
             p = {j: (z[j] - m).exp() for j in z}

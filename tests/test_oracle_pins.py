@@ -270,7 +270,7 @@ def test_planted_window_off_by_one(monkeypatch):
 
 
 def test_planted_cap_before_scale(monkeypatch):
-    def bad(q, k, scale, cap):
+    def bad(q, k, scale, cap, bias=None):
         z = q @ k.T
         c = float(np.float32(cap))
         if c > 0:
@@ -278,6 +278,27 @@ def test_planted_cap_before_scale(monkeypatch):
         return float(np.float32(scale)) * z
     monkeypatch.setattr(oa, "logits", bad)
     assert _brute_mismatch(_tiny("bf16", context=40, softmax_scale=0.25, softcap=5.0))
+
+
+def test_planted_alibi_before_cap_or_flipped(monkeypatch):
+    """The ALiBi term added before the cap, or with the distance's sign flipped, is caught
+    by the brute force."""
+    inp = _tiny("bf16", num_q_heads=4, num_kv_heads=2, context=30, softcap=2.0)
+    sl = _slopes(4)
+    want = brute_as_array(brute_decode_attention(*oracle_args(inp), alibi=sl))
+    good = oa.logits
+
+    def before_cap(q, k, scale, cap, bias=None):
+        return good(q, k, scale, 0.0, None) if bias is None else \
+            float(np.float32(cap)) * np.tanh((good(q, k, scale, 0.0, None) + bias) / float(np.float32(cap)))
+    monkeypatch.setattr(oa, "logits", before_cap)
+    assert np.abs(oracle.decode_attention(*oracle_args(inp), alibi=sl) - want).max() > 1e-6
+    monkeypatch.setattr(oa, "logits", good)
+    monkeypatch.setattr(oa, "alibi_bias", lambda s, L, t0, t1: -good_bias(s, L, t0, t1))
+    assert np.abs(oracle.decode_attention(*oracle_args(inp), alibi=sl) - want).max() > 1e-6
+
+
+good_bias = oa.alibi_bias
 
 
 def test_planted_gqa_mapping(monkeypatch):
@@ -314,3 +335,45 @@ def test_planted_fnuz_decode():
     lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
     ok = ~np.isnan(lib)
     assert (fnuz[ok] != lib[ok]).any()
+
+
+# --------------------------------------------------------------------------------------------
+# ALiBi (the "ALiBi slopes" feature of the attention.rs README)
+# --------------------------------------------------------------------------------------------
+def _slopes(h, base=8.0):
+    """The usual geometric ALiBi slopes 2^(-base (i+1) / h), as fp32."""
+    return (2.0 ** (-base * (np.arange(h) + 1) / h)).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4"])
+def test_brute_alibi(fmt):
+    inp = _tiny(fmt, num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None, ctx_range=(3, 40),
+                window=11, window_frac=0.5, softcap=2.0 if fmt == "bf16" else 0.0)
+    sl = _slopes(4)
+    o = oracle.decode_attention(*oracle_args(inp), alibi=sl)
+    b = brute_as_array(brute_decode_attention(*oracle_args(inp), alibi=sl))
+    assert np.abs(o - b).max() <= 1e-12
+
+
+@pytest.mark.parametrize("L,W", [(300, 0), (300, 40), (17, 0)])
+def test_alibi_closed_form(L, W):
+    """K = 0: the logits are the ALiBi terms alone, slope * (j - (L - 1)); with V[j][d] = bit
+    d of j the output is the exp-weighted share of keys with that bit set."""
+    D = 64
+
+    def kv(seq, n):
+        j = np.arange(n)
+        v = ((j[None, :, None] >> np.arange(D)[None, None, :]) & 1).astype(np.float32)
+        return np.zeros((1, n, D), np.float32), v
+
+    inp = kvgen.make_inputs(kvgen.spec("c1", pool_total=None), lengths=[L], windows=[W],
+                            kv_override=kv)
+    sl = _slopes(4, base=5.0)
+    o = oracle.decode_attention(*oracle_args(inp), alibi=sl)[0]
+    lo = max(0, L - W) if W else 0
+    j = np.arange(lo, L)
+    bits = (j[:, None] >> np.arange(D)[None, :]) & 1
+    for h in range(4):
+        w = np.exp(np.float64(sl[h]) * (j - (L - 1)))
+        want = (w[:, None] * bits).sum(axis=0) / w.sum()
+        assert np.abs(o[h] - want).max() < 1e-14, h
