@@ -7,19 +7,22 @@
  *
  *     z_j   = softmax_scale * <q[b,h], k_j>            j in [lo, L)
  *     z_j   = softcap * tanh(z_j / softcap)             only when softcap > 0
+ *     z_j  += alibi_slopes[h] * (j - (L - 1))           only when alibi_slopes != NULL
  *     out[b,h] = sum_j exp(z_j - max z) v_j / sum_j exp(z_j - max z)
  *
  * with k_j, v_j the dequantised key/value vectors of KV head floor(h / (Hq / Hkv)) (GQA/MQA).
  * Sources: attention.rs README ("KV Cache Formats": BF16, FP8 E4M3, Turbo4 and Turbo3 caches,
  * each with decode and Split-K decode kernels sharing one float reduce, Split-K from 1024
- * tokens; "Features": softcapping, sliding window, GQA/MQA, paged block tables, causal mask)
+ * tokens; "Features": softcapping, sliding window, GQA/MQA, paged block tables, causal mask;
+ * the paged-attention bullet list adds "ALiBi slopes")
  * and turboquant-rs 0.4.1 src/cache/cuda/attention.rs (two phases, partitioned attention then
  * a reduce; 512-token partitions, ceil(kv_len / 512) of them; fp32 per-partition max, sum and
  * output; the compressed cache is read directly with a sign pattern and a codebook; an empty
  * context yields an all-zero fp32 output).
  *
  * Readings where those pages are silent: the window holds the W most recent keys including
- * the query's own position; the cap acts on the scaled logit before the max; an empty context
+ * the query's own position; the cap acts on the scaled logit before the max; the ALiBi term
+ * (per query head, the query at position L - 1) is added after the cap; an empty context
  * gives zero rows; partitions sit at absolute multiples of the partition size.
  *
  * Conventions for every entry point.
@@ -91,7 +94,9 @@ typedef enum kvd_status {
 } kvd_status;
 
 /* Shapes.  Supported: block_size == 16; head_dim 64 or 128 for BF16/FP8, 128 for the Turbo
- * formats; num_q_heads a multiple of num_kv_heads with num_q_heads / num_kv_heads <= 16. */
+ * formats; num_q_heads a multiple of num_kv_heads.  A query group larger than 16 (MQA-like
+ * shapes) is processed in tiles of 16 query heads, each tile reading its KV head's pages
+ * again. */
 typedef struct kvd_dims {
     int32_t num_seqs;            /* B */
     int32_t num_q_heads;         /* Hq */
@@ -135,6 +140,7 @@ size_t kvd_workspace_bytes(const kvd_dims* dims);
  *   softmax_scale  logit scale (e.g. 1/sqrt(D))
  *   window       int32 [B] sliding-window widths (0 = none), or NULL for no window at all
  *   softcap      tanh cap on the scaled logits; 0 = off
+ *   alibi_slopes fp32 [Hq] per-query-head ALiBi slopes, or NULL for none
  *   out          fp32 [B][Hq][D]; must not alias any input
  *   workspace    >= kvd_workspace_bytes(dims) bytes, 256-byte aligned; contents on entry do
  *                not matter; on return it holds the partials of split sequences
@@ -144,7 +150,8 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,
                           const float* codebook, const float* sign_pattern, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* workspace,
+                          const int32_t* window, float softcap, const float* alibi_slopes,
+                          float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
@@ -158,7 +165,8 @@ int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cac
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,
                           const float* codebook, const float* sign_pattern, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* workspace,
+                          const int32_t* window, float softcap, const float* alibi_slopes,
+                          float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /* Phase 2 alone (same arguments; reads the workspace phase 1 filled).  For each split
@@ -168,7 +176,8 @@ int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cac
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,
                           const float* codebook, const float* sign_pattern, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* workspace,
+                          const int32_t* window, float softcap, const float* alibi_slopes,
+                          float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
 /* Test export: dequantised cache values of tokens [token_begin, token_begin + n_tokens) of

@@ -45,7 +45,7 @@ def library_path() -> str:
 _ATTN_ARGS = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
               ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
-              ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
 
 def load() -> ctypes.CDLL:
@@ -107,13 +107,13 @@ def workspace_bytes(dims: Dims) -> int:
 
 
 def _attn(name, dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
-          sign_pattern, softmax_scale, window, softcap, out, workspace, stream):
+          sign_pattern, softmax_scale, window, softcap, out, workspace, stream, alibi_slopes):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(load(), name)(ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(block_table), _ptr(context_lens), _fmt(fmt), _ptr(scales),
                                _ptr(codebook), _ptr(sign_pattern), float(softmax_scale),
-                               _ptr(window), float(softcap), _ptr(out), _ptr(workspace),
-                               ws_bytes, _stream(stream))
+                               _ptr(window), float(softcap), _ptr(alibi_slopes), _ptr(out),
+                               _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise KvdError(st, name)
     return out
@@ -121,29 +121,29 @@ def _attn(name, dims, q, k_cache, v_cache, block_table, context_lens, fmt, scale
 
 def decode_attn_paged(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
                       codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
-                      stream=None):
+                      stream=None, alibi_slopes=None):
     """Both phases; see kvd_decode_attn_paged in include/kvdecode.h."""
     return _attn("kvd_decode_attn_paged", dims, q, k_cache, v_cache, block_table, context_lens,
                  fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
-                 workspace, stream)
+                 workspace, stream, alibi_slopes)
 
 
 def decode_partitions(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
                       codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
-                      stream=None):
+                      stream=None, alibi_slopes=None):
     """Phase 1 (partition kernel) only."""
     return _attn("kvd_decode_partitions", dims, q, k_cache, v_cache, block_table, context_lens,
                  fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
-                 workspace, stream)
+                 workspace, stream, alibi_slopes)
 
 
 def reduce_partitions(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
                       codebook, sign_pattern, softmax_scale, window, softcap, out, workspace,
-                      stream=None):
+                      stream=None, alibi_slopes=None):
     """Phase 2 (reduce kernel) only."""
     return _attn("kvd_reduce_partitions", dims, q, k_cache, v_cache, block_table, context_lens,
                  fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
-                 workspace, stream)
+                 workspace, stream, alibi_slopes)
 
 
 def dequant_gather(dims, fmt, is_v, cache, scales, codebook, block_table, seq, kv_head,

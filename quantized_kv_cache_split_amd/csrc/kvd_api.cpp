@@ -36,6 +36,12 @@ struct Plan {
     size_t off_l, off_o, bytes;
 };
 
+// Query tiles per KV head: groups of up to kMaxGroup query heads share one MFMA tile.
+int query_tiles(const kvd_dims* d) {
+    const int g = d->num_q_heads / d->num_kv_heads;
+    return (g + kvd::kMaxGroup - 1) / kvd::kMaxGroup;
+}
+
 // Compute units of the current device (256 on MI355X when the query fails).
 int device_cus() {
     int dev = 0, cus = 0;
@@ -58,13 +64,15 @@ int choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return 1;
     int64_t r = d->partitions_per_wave;
     if (r == 0) {
-        const int64_t waves = (int64_t)pl.P * d->num_kv_heads * d->num_seqs;
+        const int64_t tiles = query_tiles(d);
+        const int64_t waves = (int64_t)pl.P * d->num_kv_heads * tiles * d->num_seqs;
         const int64_t slots = (int64_t)device_cus() * kvd::kWavesPerCU;
         r = (waves + slots - 1) / slots;
         if (r > kvd::kMaxRun) r = kvd::kMaxRun;
     }
     if (fmt < KVD_TURBO4) {   // BF16 / FP8 stage the run's triples in LDS
-        const int64_t cap = kvd::stage_rows(d->head_dim) / (d->num_q_heads / d->num_kv_heads);
+        const int g = d->num_q_heads / d->num_kv_heads;
+        const int64_t cap = kvd::stage_rows(d->head_dim) / (g < kvd::kMaxGroup ? g : kvd::kMaxGroup);
         if (r > cap) r = cap;
     }
     if (r > pl.P) r = pl.P;
@@ -77,7 +85,6 @@ int check_dims(const kvd_dims* d, int fmt) {
     if (fmt >= 0 && (fmt < KVD_BF16 || fmt > KVD_TURBO3)) return KVD_ERR_FORMAT;
     if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return KVD_ERR_SHAPE;
     if (d->num_q_heads % d->num_kv_heads != 0) return KVD_ERR_SHAPE;
-    if (d->num_q_heads / d->num_kv_heads > kvd::kMaxGroup) return KVD_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return KVD_ERR_SHAPE;
     if (fmt >= KVD_TURBO4 && d->head_dim != 128) return KVD_ERR_SHAPE;
     if (d->block_size != kvd::kPageTokens) return KVD_ERR_SHAPE;
@@ -121,7 +128,7 @@ enum Phases { kPhase1 = 1, kPhase2 = 2 };
 int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const void* v_cache,
         const int32_t* block_table, const int32_t* context_lens, int fmt, const float* scales,
         const float* codebook, const float* sign_pattern, float softmax_scale,
-        const int32_t* window, float softcap, float* out, void* workspace,
+        const int32_t* window, float softcap, const float* alibi, float* out, void* workspace,
         size_t workspace_bytes, void* stream) {
     int st = check_dims(d, fmt);
     if (st != KVD_OK) return st;
@@ -131,7 +138,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(block_table, 4) || !aligned(context_lens, 4) || (window && !aligned(window, 4)) ||
         (scales && !aligned(scales, 16)) || (codebook && !aligned(codebook, 4)) ||
-        (sign_pattern && !aligned(sign_pattern, 4)))
+        (sign_pattern && !aligned(sign_pattern, 4)) || (alibi && !aligned(alibi, 4)))
         return KVD_ERR_ALIGN;
     if (!(softcap >= 0.0f) || !(softmax_scale == softmax_scale)) return KVD_ERR_SHAPE;
     const Plan pl = make_plan(d);
@@ -152,6 +159,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.scales = scales;
     p.codebook = codebook;
     p.sign = sign_pattern;
+    p.alibi = alibi;
     p.out = out;
     char* ws = static_cast<char*>(workspace);
     p.ws_m = pl.bytes ? reinterpret_cast<float*>(ws) : nullptr;
@@ -163,6 +171,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.Hq = d->num_q_heads;
     p.Hkv = d->num_kv_heads;
     p.g = d->num_q_heads / d->num_kv_heads;
+    p.qt = query_tiles(d);
     p.D = d->head_dim;
     p.max_blocks = d->max_blocks_per_seq;
     p.pool = d->num_pool_blocks;
@@ -184,7 +193,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     if (phases & kPhase1) {
         // `waves` waves per workgroup, p.run partitions per wave
         const int px = pl.P ? (pl.P + waves * p.run - 1) / (waves * p.run) : 1;
-        const int64_t wgs = (int64_t)px * d->num_kv_heads * d->num_seqs;
+        const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qt * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);
         e = kvd::launch_partitions(fmt, p, grid, s);
@@ -209,28 +218,28 @@ size_t kvd_workspace_bytes(const kvd_dims* dims) {
 int kvd_decode_attn_paged(const kvd_dims* d, const void* q, const void* k, const void* v,
                           const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
                           const float* codebook, const float* sign, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const int32_t* window, float softcap, const float* alibi, float* out,
+                          void* ws, size_t ws_bytes, void* stream) {
     return run(kPhase1 | kPhase2, d, q, k, v, bt, ctx, fmt, scales, codebook, sign,
-               softmax_scale, window, softcap, out, ws, ws_bytes, stream);
+               softmax_scale, window, softcap, alibi, out, ws, ws_bytes, stream);
 }
 
 int kvd_decode_partitions(const kvd_dims* d, const void* q, const void* k, const void* v,
                           const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
                           const float* codebook, const float* sign, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const int32_t* window, float softcap, const float* alibi, float* out,
+                          void* ws, size_t ws_bytes, void* stream) {
     return run(kPhase1, d, q, k, v, bt, ctx, fmt, scales, codebook, sign, softmax_scale,
-               window, softcap, out, ws, ws_bytes, stream);
+               window, softcap, alibi, out, ws, ws_bytes, stream);
 }
 
 int kvd_reduce_partitions(const kvd_dims* d, const void* q, const void* k, const void* v,
                           const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
                           const float* codebook, const float* sign, float softmax_scale,
-                          const int32_t* window, float softcap, float* out, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          const int32_t* window, float softcap, const float* alibi, float* out,
+                          void* ws, size_t ws_bytes, void* stream) {
     return run(kPhase2, d, q, k, v, bt, ctx, fmt, scales, codebook, sign, softmax_scale,
-               window, softcap, out, ws, ws_bytes, stream);
+               window, softcap, alibi, out, ws, ws_bytes, stream);
 }
 
 int kvd_dequant_gather(const kvd_dims* d, int fmt, int is_v, const void* cache,

@@ -11,7 +11,7 @@ namespace kvd {
 constexpr int kPageTokens = 16;     // tokens per page (block_size)
 constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
-constexpr int kMaxGroup = 16;       // query heads per KV head one workgroup handles
+constexpr int kMaxGroup = 16;       // query heads one MFMA tile (one wave) handles
 constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
 constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
@@ -34,6 +34,7 @@ struct LaunchParams {
     const float* scales;      // fp8 [2][Hkv]; turbo norms [2][pool][Hkv][16]
     const float* codebook;    // turbo levels (K then V)
     const float* sign;        // turbo [D]
+    const float* alibi;       // [Hq] ALiBi slopes or nullptr
     float* out;               // [B][Hq][D]
     float* ws_m;              // [B][Hq][P]
     float* ws_l;              // [B][Hq][P]
@@ -41,6 +42,7 @@ struct LaunchParams {
     int64_t k_chunk;          // bytes per (page, KV head), K
     int64_t v_chunk;          // bytes per (page, KV head), V
     int32_t B, Hq, Hkv, g, D;
+    int32_t qt;               // query tiles per KV head: ceil(g / kMaxGroup)
     int32_t max_blocks, pool, max_ctx;
     int32_t part_mode;        // PartMode
     int32_t part_size;        // tokens per partition (split sequences)

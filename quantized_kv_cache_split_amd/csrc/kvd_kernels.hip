@@ -358,13 +358,19 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     // handed to the eight XCDs round-robin by linear id, so this order spreads every
     // sequence's work over the XCDs (with 8 KV heads each XCD gets one head of every
     // sequence); x fastest would pile the short sequences' work onto the XCDs of small x.
+    // A query group larger than kMaxGroup is split into p.qt tiles ("virtual heads") of up to
+    // kMaxGroup query heads, each processed like a KV head of its own (its pages are read once
+    // per tile).
     const int wg = blockIdx.x;
-    const int hk = wg % p.Hkv, b = (wg / p.Hkv) % p.B, xb = wg / (p.Hkv * p.B);
+    const int nvh = p.Hkv * p.qt;
+    const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = wg / (nvh * p.B);
+    const int hk = vh / p.qt, qtile = vh - hk * p.qt;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int g = p.g;
+    const int qbase = hk * p.g + qtile * kMaxGroup;               // first query head of the tile
+    const int g = min(kMaxGroup, p.g - qtile * kMaxGroup);        // query heads in the tile
     const SeqInfo si = seq_info(p, b);
-    float* out_rows = p.out + ((size_t)b * p.Hq + (size_t)hk * g) * D;
+    float* out_rows = p.out + ((size_t)b * p.Hq + (size_t)qbase) * D;
 
     if (si.bad || si.L == 0) {
         if (xb == 0) {
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
         for (int i = tid; i < g * D; i += kThr) {
             const int r = i / D, d = i % D;
-            const uint16_t qb = p.q[((size_t)b * p.Hq + (size_t)hk * g + r) * D + d];
+            const uint16_t qb = p.q[((size_t)b * p.Hq + (size_t)qbase + r) * D + d];
             lds.row[i] = bf16_bits_to_f32(qb) * p.sign[d];
         }
         __syncthreads();
@@ -474,7 +480,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
         oscale = 1.0f / vsc;
     } else {
-        const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)hk * g + qn) * D;
+        const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)qbase + qn) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = (FMT == KVD_BF16) ? 32 * s + 8 * j : 64 * (s / 2) + 16 * j + 8 * (s % 2);
@@ -489,6 +495,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     }
     const float cap_l2 = CAP ? p.softcap * kLog2e : 0.0f;      // cap in base-2 units
     const float inv_cap_l2 = CAP ? 1.0f / cap_l2 : 0.0f;
+    // ALiBi slope of this lane's query head, in base-2 units (0 without ALiBi)
+    const bool alibi = p.alibi != nullptr;
+    const float slope_l2 = alibi ? p.alibi[qbase + qn] * kLog2e : 0.0f;
 
     // ---- state -------------------------------------------------------------------------
     f32x4 oacc[VT];
@@ -588,6 +597,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 const float t = fast_exp2(2.0f * kLog2e * (z[e] * inv_cap_l2));
                 z[e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
             }
+        }
+        if (alibi) {   // + slope * (j - (L - 1)) for the lane's tokens j = tok0 .. tok0 + 7
+            const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
+            const float base = slope_l2 * (float)(tok0 - (si.L - 1));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[e] += base + slope_l2 * (float)e;
         }
         float vn[8];   // V norms (codebook formats)
         if constexpr (kTurbo) {
@@ -715,7 +730,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         }
     };
 
-    const size_t row0 = (size_t)b * p.Hq + (size_t)hk * g;
+    const size_t row0 = (size_t)b * p.Hq + (size_t)qbase;
 
     // ---- split sequences: close a partition after its last pair ------------------------
     // Writes the partition's triple (m = the exact max logit in base-2 units, l = the sum

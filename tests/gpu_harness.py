@@ -14,13 +14,16 @@ REL_TOL = 1e-2     # max over rows of max_d |gpu - oracle| / max_d |oracle|
 class GpuBatch:
     """Device copy of one batch plus output and workspace buffers."""
 
-    def __init__(self, inp, partition_size=None, device="cuda:0", partitions_per_wave=0):
+    def __init__(self, inp, partition_size=None, device="cuda:0", partitions_per_wave=0,
+                 alibi=None):
         import torch
         import quantized_kv_cache_split_amd as kvd
         self.kvd = kvd
         self.inp = inp
         self.dims = kvd.Dims(**dims_kwargs(inp, partition_size, partitions_per_wave))
         self.t = to_torch(inp, device)
+        self.alibi = None if alibi is None else torch.from_numpy(
+            np.asarray(alibi, dtype=np.float32)).to(device)
         s = inp.spec
         self.out = torch.full((s.num_seqs, s.num_q_heads, s.head_dim), float("nan"),
                               dtype=torch.float32, device=device)
@@ -37,13 +40,13 @@ class GpuBatch:
                 float(self.inp.softcap), self.out, self.ws if self.kvd.workspace_bytes(self.dims) else None)
 
     def run(self, window=True):
-        self.kvd.decode_attn_paged(*self._args(window))
+        self.kvd.decode_attn_paged(*self._args(window), alibi_slopes=self.alibi)
         import torch
         torch.cuda.synchronize()
         return self.out.double().cpu().numpy()
 
     def run_phase1(self):
-        self.kvd.decode_partitions(*self._args())
+        self.kvd.decode_partitions(*self._args(), alibi_slopes=self.alibi)
         import torch
         torch.cuda.synchronize()
 

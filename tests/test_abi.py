@@ -57,19 +57,19 @@ FAKE = 1 << 20   # a 16-byte aligned, never dereferenced address
 
 def call(d=None, fmt=0, **over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, ctx=FAKE, scales=FAKE, cb=FAKE, sign=FAKE,
-             scale=0.1, win=None, cap=0.0, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+             scale=0.1, win=None, cap=0.0, alibi=None, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
     a.update(over)
     lib = kvd.load()
     return lib.kvd_decode_attn_paged(ctypes.byref(d or dims()), a["q"], a["k"], a["v"], a["bt"],
                                      a["ctx"], fmt, a["scales"], a["cb"], a["sign"], a["scale"],
-                                     a["win"], a["cap"], a["out"], a["ws"], a["ws_bytes"], None)
+                                     a["win"], a["cap"], a["alibi"], a["out"], a["ws"],
+                                     a["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("field,value", [("num_q_heads", 60), ("num_kv_heads", 0),
                                          ("head_dim", 96), ("block_size", 32),
                                          ("max_context_len", 0), ("max_context_len", 1 << 20),
-                                         ("partition_size", 100), ("num_q_heads", 8 * 17),
-                                         ("partitions_per_wave", -1)])
+                                         ("partition_size", 100), ("partitions_per_wave", -1)])
 def test_shape_errors(field, value):
     assert call(dims(**{field: value})) == -2
 
@@ -92,6 +92,12 @@ def test_fp8_and_turbo_need_their_arrays():
     assert call(fmt=2, cb=None) == -1
     assert call(fmt=3, sign=None) == -1
     assert call(fmt=0, scales=None, cb=None, sign=None, ws_bytes=0) == -5
+
+
+def test_alibi_alignment_and_large_groups():
+    assert call(alibi=FAKE + 2) == -4
+    # query groups above 16 (here 64 query heads on one KV head) are accepted
+    assert kvd.workspace_bytes(dims(num_q_heads=64, num_kv_heads=1)) > 0
 
 
 def test_alignment_errors():

@@ -264,3 +264,85 @@ def test_context_above_bound_gives_nan():
     gb.t["context_lens"][1] = 10 ** 6
     gpu = gb.run()
     assert np.isnan(gpu[1]).all() and np.isfinite(gpu[0]).all()
+
+
+# --------------------------------------------------------------------------------------------
+# ALiBi slopes and query groups above 16 (MQA-like shapes)
+# --------------------------------------------------------------------------------------------
+def _slopes(h, base=8.0):
+    return (2.0 ** (-base * (np.arange(h) + 1) / h)).astype(np.float32)
+
+
+@pytest.mark.parametrize("ps", [0, 128, -1])
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_alibi_ragged_window(fmt, ps):
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=6, num_q_heads=8, num_kv_heads=2,
+                                       ctx_range=(1, 4000), window=1500,
+                                       softcap=50.0 if fmt == "bf16" else 0.0),
+                            poison_before_window=True)
+    sl = _slopes(8)
+    gpu = GpuBatch(inp, partition_size=ps, alibi=sl).run()
+    ref = oracle.decode_attention(*oracle_args(inp), alibi=sl)
+    assert_close(gpu, ref, f"{fmt} alibi ps={ps}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_alibi_position_coded_v(fmt):
+    """K = 0: the logits are the ALiBi terms; with V[j][d] = bit d of j the output is the
+    exp-weighted share of keys with bit d set (closed form), here split into 512-token parts."""
+    D, L = 128, 3000
+
+    def kv(seq, n):
+        j = np.arange(n)
+        return (np.zeros((1, n, D), np.float32),
+                ((j[None, :, None] >> np.arange(D)[None, None, :]) & 1).astype(np.float32))
+
+    inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=D, pool_total=None), lengths=[L],
+                            kv_override=kv, fp8_scale=np.ones((2, 1), np.float32))
+    sl = _slopes(4, base=9.0)
+    gpu = GpuBatch(inp, alibi=sl).run()[0]
+    j = np.arange(L)
+    bits = (j[:, None] >> np.arange(D)[None, :]) & 1
+    for h in range(4):
+        w = np.exp(np.float64(sl[h]) * (j - (L - 1)))
+        want = (w[:, None] * bits).sum(axis=0) / w.sum()
+        assert np.abs(gpu[h] - want).max() < 2e-6, h
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "turbo4"])
+def test_alibi_partials_match_oracle(fmt):
+    inp = _small(fmt, context=None, ctx_range=(200, 700), num_seqs=2)
+    sl = _slopes(inp.spec.num_q_heads)
+    gb = GpuBatch(inp, partition_size=128, alibi=sl)
+    gb.run_phase1()
+    m, l, o = gb.partials()
+    s = inp.spec
+    for b in range(s.num_seqs):
+        for hk in range(s.num_kv_heads):
+            for lo_, hi_, pm, pl, po in oracle.partition_partials(*oracle_args(inp), 128, b, hk,
+                                                                  rotated=True, alibi=sl):
+                p = lo_ // 128
+                rows = slice(hk * s.group, hk * s.group + s.group)
+                lse = m[b, rows, p].astype(np.float64) * np.log(2.0) + np.log(l[b, rows, p].astype(np.float64))
+                assert np.abs(lse - (pm + np.log(pl))).max() < 5e-3
+                assert_close(o[b, rows, p].astype(np.float64), po, f"{fmt} alibi partial b{b} p{p}")
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("hq,hkv", [(32, 1), (64, 1), (48, 2), (20, 1)])
+def test_large_query_groups(fmt, hq, hkv):
+    """Groups of 20..64 query heads per KV head run as tiles of 16 (the last tile ragged)."""
+    inp = _small(fmt, num_q_heads=hq, num_kv_heads=hkv, context=None, ctx_range=(1, 2600),
+                 num_seqs=3)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} g={hq // hkv}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "turbo3"])
+def test_large_group_alibi_runs(fmt):
+    inp = _small(fmt, num_q_heads=40, num_kv_heads=1, context=None, ctx_range=(900, 5000),
+                 num_seqs=3)
+    sl = _slopes(40)
+    ref = oracle.decode_attention(*oracle_args(inp), alibi=sl)
+    for run in (1, 3):
+        assert_close(GpuBatch(inp, partitions_per_wave=run, alibi=sl).run(), ref,
+                     f"{fmt} g=40 alibi run={run}")
