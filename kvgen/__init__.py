@@ -10,7 +10,8 @@ no rotation of the query, no softmax.  The oracle (``oracle/``) and the GPU libr
 implement those on their own; this is the only module both sides share.
 
 Workload shapes follow the attention.rs README (page "guoqingbao/attention.rs", section
-"KV Cache Formats": BF16, FP8 E4M3, Turbo4 = 4-bit K + 4-bit V, Turbo3 = 3-bit K + 4-bit V)
+"KV Cache Formats": BF16, FP8 E4M3, Turbo8 = FP8 K + 4-bit V, Turbo4 = 4-bit K + 4-bit V,
+Turbo3 = 3-bit K + 4-bit V)
 and the turboquant-rs fused attention wrapper (page "turboquant-rs 0.4.1
 src/cache/cuda/attention.rs": 512-token partitions, sign pattern, codebook, per-token scales).
 """
@@ -26,9 +27,19 @@ from dataclasses import dataclass, field
 import numpy as np
 
 BLOCK_SIZE = 16          # tokens per page
-FORMATS = ("bf16", "fp8", "turbo4", "turbo3")
-FORMAT_CODE = {"bf16": 0, "fp8": 1, "turbo4": 2, "turbo3": 3}
-KV_BITS = {"turbo4": (4, 4), "turbo3": (3, 4)}   # (K bits, V bits)
+FORMATS = ("bf16", "fp8", "turbo4", "turbo3", "turbo8")
+FORMAT_CODE = {"bf16": 0, "fp8": 1, "turbo4": 2, "turbo3": 3, "turbo8": 4}
+KV_BITS = {"turbo4": (4, 4), "turbo3": (3, 4)}   # (K bits, V bits) of the all-codebook formats
+
+
+def k_is_fp8(fmt: str) -> bool:
+    """K stored as E4M3FN codes with one fp32 scale per KV head (FP8 and Turbo8)."""
+    return fmt in ("fp8", "turbo8")
+
+
+def v_is_codebook(fmt: str) -> bool:
+    """V stored as 4-bit rotated-codebook indices with per-token norms (the Turbo formats)."""
+    return fmt in ("turbo4", "turbo3", "turbo8")
 
 BF16_POISON = np.uint16(0x7FC0)   # quiet NaN
 FP8_POISON = np.uint8(0x7F)       # E4M3FN NaN (S.1111.111)
@@ -89,6 +100,8 @@ SPECS: dict[str, Spec] = {
     "m-bf16": Spec("bf16-L32768-gqa8", 16, 64, 8, 128, "bf16", context=32768),
     "m-t4": Spec("turbo4-L32768", 8, 32, 8, 128, "turbo4", context=32768),
     "m-t3": Spec("turbo3-L32768", 8, 32, 8, 128, "turbo3", context=32768),
+    "m-t8": Spec("turbo8-L32768", 8, 32, 8, 128, "turbo8", context=32768),
+    "c5-t8": Spec("turbo8-L65536", 8, 32, 8, 128, "turbo8", context=65536),
 }
 
 
@@ -102,17 +115,17 @@ def spec(name: str, **overrides) -> Spec:
 # --------------------------------------------------------------------------------------------
 def k_chunk_bytes(fmt: str, d: int) -> int:
     """Bytes of one (page, KV head) chunk of the K cache."""
-    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 6 * d}[fmt]
+    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 6 * d, "turbo8": 16 * d}[fmt]
 
 
 def v_chunk_bytes(fmt: str, d: int) -> int:
     """Bytes of one (page, KV head) chunk of the V cache (Turbo V is always 4-bit)."""
-    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 8 * d}[fmt]
+    return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 8 * d, "turbo8": 8 * d}[fmt]
 
 
 def kv_bytes_per_token_head(fmt: str, d: int) -> int:
     """Algorithmic cache bytes the method must read per (token, KV head), K + V (+ norms)."""
-    norms = 8 if fmt.startswith("turbo") else 0
+    norms = 8 if fmt in KV_BITS else (4 if fmt == "turbo8" else 0)
     return (k_chunk_bytes(fmt, d) + v_chunk_bytes(fmt, d)) // BLOCK_SIZE + norms
 
 
@@ -272,7 +285,7 @@ def pack_k_pages(fmt: str, elems: np.ndarray) -> np.ndarray:
     if fmt == "bf16":      # [D/8][16][8] bf16
         c = elems.astype(np.uint16).reshape(n, h, t, d // 8, 8).transpose(0, 1, 3, 2, 4)
         return np.ascontiguousarray(c).view(np.uint8).reshape(n, h, -1)
-    if fmt == "fp8":       # [D/16][16][16] bytes
+    if k_is_fp8(fmt):      # [D/16][16][16] bytes
         c = elems.astype(np.uint8).reshape(n, h, t, d // 16, 16).transpose(0, 1, 3, 2, 4)
         return np.ascontiguousarray(c).reshape(n, h, -1)
     groups = elems.reshape(n, h, t, d // 32, 32).transpose(0, 1, 3, 2, 4)   # [D/32][16][32]
@@ -302,8 +315,11 @@ class Inputs:
     q: np.ndarray                 # uint16 [B, Hq, D] bf16 bits
     k_cache: np.ndarray           # uint8 [pool, Hkv, k_chunk_bytes]
     v_cache: np.ndarray           # uint8 [pool, Hkv, v_chunk_bytes]
-    scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo: f32 [2, pool, Hkv, 16]; bf16: None
-    codebook: np.ndarray | None   # turbo: f32 [2^kbits + 16] (K levels then V levels)
+    scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo4/3: f32 [2, pool, Hkv, 16];
+                                  # turbo8: f32 [pool*Hkv*16 + Hkv] (V norms, then K scales);
+                                  # bf16: None
+    codebook: np.ndarray | None   # turbo4/3: f32 [2^kbits + 16] (K levels then V levels);
+                                  # turbo8: f32 [16] (V levels)
     sign: np.ndarray | None       # turbo: f32 [D] of +-1
     block_table: np.ndarray       # int32 [B, max_blocks_per_seq]
     context_lens: np.ndarray      # int32 [B]
@@ -353,13 +369,13 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
     """Build one batch.
 
     poison: spare pages and tail slots past each context length hold NaN (bf16 0x7FC0,
-        fp8 0x7F, Turbo norm NaN), so any read that reaches the arithmetic shows up.
+        fp8 0x7F, codebook norm NaN), so any read that reaches the arithmetic shows up.
     poison_before_window: also poison pages that lie wholly before a window's start.
     unused_fill: block-table entries past a sequence's last page -> 'spare' (a poisoned spare
         page) or -1.
     kv_override: callable(seq, L) -> (K [Hkv, L, D], V [Hkv, L, D]) float32 logical values,
         replacing the Gaussian draws (identity tests).
-    fp8_scale: optional f32 [2, Hkv] replacing amax/448.
+    fp8_scale: optional f32 [2, Hkv] replacing amax/448 (Turbo8 uses the K row).
     lengths / windows: optional explicit context lengths / window widths per sequence.
     """
     assert s.fmt in FORMATS and s.num_q_heads % s.num_kv_heads == 0
@@ -407,27 +423,27 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
     k_cache = np.empty((pool, Hkv, kb), dtype=np.uint8)
     v_cache = np.empty((pool, Hkv, vb), dtype=np.uint8)
     scales = codebook_arr = sgn = None
-    if fmt.startswith("turbo"):
-        kbits, vbits = KV_BITS[fmt]
-        cb_k, cb_v = codebook(1 << kbits, D), codebook(1 << vbits, D)
-        codebook_arr = np.concatenate([cb_k, cb_v]).astype(np.float32)
+    k_fp8, v_cb, k_cb = k_is_fp8(fmt), v_is_codebook(fmt), fmt in KV_BITS
+    knorm = vnorm = kscale = None
+    nan_or_0 = np.float32(np.nan if poison else 0.0)
+    if v_cb:
+        cb_v = codebook(16, D)
         sgn = sign_pattern(r["sign"], D)
-        scales = np.full((2, pool, Hkv, BLOCK_SIZE), np.nan if poison else 0.0, dtype=np.float32)
+        vnorm = np.full((pool, Hkv, BLOCK_SIZE), nan_or_0, dtype=np.float32)
+        if k_cb:
+            cb_k = codebook(1 << KV_BITS[fmt][0], D)
+            codebook_arr = np.concatenate([cb_k, cb_v]).astype(np.float32)
+            knorm = np.full((pool, Hkv, BLOCK_SIZE), nan_or_0, dtype=np.float32)
+        else:
+            codebook_arr = cb_v.copy()
 
     # poison everything first; real pages are overwritten below
-    if poison:
-        if fmt == "bf16":
-            k_cache.view(np.uint16)[...] = BF16_POISON
-            v_cache.view(np.uint16)[...] = BF16_POISON
-        elif fmt == "fp8":
-            k_cache[...] = FP8_POISON
-            v_cache[...] = FP8_POISON
-        else:
-            k_cache[...] = 0x5A
-            v_cache[...] = 0xA5
-    else:
-        k_cache[...] = 0
-        v_cache[...] = 0
+    k_poison = BF16_POISON if fmt == "bf16" else (FP8_POISON if k_fp8 else np.uint8(0x5A))
+    v_poison = BF16_POISON if fmt == "bf16" else (FP8_POISON if fmt == "fp8" else np.uint8(0xA5))
+    kview = k_cache.view(np.uint16) if fmt == "bf16" else k_cache
+    vview = v_cache.view(np.uint16) if fmt == "bf16" else v_cache
+    kview[...] = k_poison if poison else 0
+    vview[...] = v_poison if poison else 0
 
     # K and V of sequence b come from child b of the K / V stream, so sequences can be drawn and
     # encoded in parallel threads with a result that does not depend on the thread count.
@@ -444,7 +460,8 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
     starts = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int64)
     workers = max(1, min(16, os.cpu_count() or 1, B))
     drawn = {}
-    if fmt == "fp8":
+    fp8_scales = None
+    if k_fp8:
         # one fp32 scale per (K|V, KV head) = amax / 448 over the whole batch: draw first
         def first(b):
             kk, vv = draw(b)
@@ -456,10 +473,13 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
             amaxes = list(ex.map(first, range(B)))
         if fp8_scale is None:
             amax = np.max(np.stack(amaxes), axis=0).astype(np.float32)
-            scales = (amax / np.float32(448.0)).astype(np.float32)
-            scales[scales == 0] = np.float32(1.0)
+            fp8_scales = (amax / np.float32(448.0)).astype(np.float32)
+            fp8_scales[fp8_scales == 0] = np.float32(1.0)
         else:
-            scales = np.asarray(fp8_scale, dtype=np.float32).reshape(2, Hkv)
+            fp8_scales = np.asarray(fp8_scale, dtype=np.float32).reshape(2, Hkv)
+        kscale = fp8_scales[0]
+        if fmt == "fp8":
+            scales = fp8_scales
 
     def fill_seq(b):
         Lb, npg = int(L[b]), int(n_pages[b])
@@ -468,25 +488,28 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         if npg == 0:
             return
         pad = npg * BLOCK_SIZE - Lb
+
+        def put_norms(plane, nrm):
+            nrm = np.concatenate([nrm, np.full((Hkv, pad), nan_or_0, np.float32)], axis=1)
+            plane[phys] = nrm.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
+
         if fmt == "bf16":
             ke, ve = bf16_bits(kk), bf16_bits(vv)
-            fill = BF16_POISON if poison else np.uint16(0)
-        elif fmt == "fp8":
-            ke = e4m3fn_encode(kk / scales[0][:, None, None])
-            ve = e4m3fn_encode(vv / scales[1][:, None, None])
-            fill = FP8_POISON if poison else np.uint8(0)
+        elif k_fp8:
+            ke = e4m3fn_encode(kk / kscale[:, None, None])
         else:
             ke, kn = turbo_encode(kk, sgn, cb_k)
+            put_norms(knorm, kn)
+        if fmt == "fp8":
+            ve = e4m3fn_encode(vv / fp8_scales[1][:, None, None])
+        elif v_cb:
             ve, vn = turbo_encode(vv, sgn, cb_v)
-            fill = np.uint8(0)
-            nfill = np.float32(np.nan if poison else 0.0)
-            kn = np.concatenate([kn, np.full((Hkv, pad), nfill, np.float32)], axis=1)
-            vn = np.concatenate([vn, np.full((Hkv, pad), nfill, np.float32)], axis=1)
-            scales[0, phys] = kn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
-            scales[1, phys] = vn.reshape(Hkv, npg, BLOCK_SIZE).transpose(1, 0, 2)
+            put_norms(vnorm, vn)
+        kfill = k_poison if (poison and (fmt == "bf16" or k_fp8)) else np.zeros((), ke.dtype)
+        vfill = v_poison if (poison and not v_cb) else np.zeros((), ve.dtype)
         del kk, vv
-        ke = np.concatenate([ke, np.full((Hkv, pad, D), fill, ke.dtype)], axis=1)
-        ve = np.concatenate([ve, np.full((Hkv, pad, D), fill, ve.dtype)], axis=1)
+        ke = np.concatenate([ke, np.full((Hkv, pad, D), kfill, ke.dtype)], axis=1)
+        ve = np.concatenate([ve, np.full((Hkv, pad, D), vfill, ve.dtype)], axis=1)
         ke = ke.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
         ve = ve.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
         k_cache[phys] = pack_k_pages(fmt, ke)
@@ -494,18 +517,22 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         if poison_before_window and W[b] > 0 and Lb > W[b]:
             first_live = (Lb - int(W[b])) // BLOCK_SIZE
             dead = phys[:first_live]
-            if fmt == "bf16":
-                k_cache.view(np.uint16)[dead] = BF16_POISON
-                v_cache.view(np.uint16)[dead] = BF16_POISON
-            elif fmt == "fp8":
-                k_cache[dead] = FP8_POISON
-                v_cache[dead] = FP8_POISON
+            if fmt == "bf16" or k_fp8:
+                kview[dead] = k_poison
             else:
-                scales[:, dead] = np.nan
+                knorm[dead] = np.nan
+            if v_cb:
+                vnorm[dead] = np.nan
+            else:
+                vview[dead] = v_poison
 
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(fill_seq, range(B)))
 
+    if fmt in KV_BITS:
+        scales = np.stack([knorm, vnorm])
+    elif fmt == "turbo8":
+        scales = np.concatenate([vnorm.reshape(-1), kscale]).astype(np.float32)
     return Inputs(spec=s, q=q, k_cache=k_cache, v_cache=v_cache, scales=scales,
                   codebook=codebook_arr, sign=sgn, block_table=bt, context_lens=L, window=W,
                   softmax_scale=s.scale, softcap=np.float32(s.softcap), max_context_len=max_ctx)
@@ -524,6 +551,12 @@ def relayout(inp: Inputs, seed: int) -> Inputs:
     if sc is not None and sc.ndim == 4:
         sc = np.empty_like(inp.scales)
         sc[:, new_of_old] = inp.scales
+    elif inp.spec.fmt == "turbo8":
+        hkv = inp.spec.num_kv_heads
+        vn = inp.scales[:-hkv].reshape(pool, hkv, BLOCK_SIZE)
+        moved = np.empty_like(vn)
+        moved[new_of_old] = vn
+        sc = np.concatenate([moved.reshape(-1), inp.scales[-hkv:]])
     bt = inp.block_table.copy()
     ok = bt >= 0
     bt[ok] = new_of_old[bt[ok]]

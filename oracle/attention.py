@@ -6,8 +6,9 @@ library: it reads the paged layout, decodes FP8 and the rotated codebook format,
 and computes softmax(q K^T * scale) V on its own, in float64.
 
 What it follows (page titles and sections of the source pages):
-  * attention.rs README, "KV Cache Formats": the formats BF16, FP8 (E4M3), Turbo4 (4-bit K +
-    4-bit V, Walsh-Hadamard) and Turbo3 (3-bit K + 4-bit V); the Split-K paragraph below that
+  * attention.rs README, "KV Cache Formats": the formats BF16, FP8 (E4M3), Turbo8 (FP8 K +
+    4-bit V, Walsh-Hadamard), Turbo4 (4-bit K + 4-bit V, Walsh-Hadamard) and Turbo3 (3-bit K +
+    4-bit V); the Split-K paragraph below that
     table: long contexts are split (from 1024 tokens on) and the pieces are merged by a float
     reduce; "Features": softcapping, sliding window, GQA/MQA, paged block tables, causal mask.
   * turboquant-rs 0.4.1 src/cache/cuda/attention.rs: ``PARTITION_SIZE = 512`` and
@@ -23,7 +24,10 @@ Readings taken where the pages are silent (the header of the library states the 
     L - 1 adds slope_h * (j - (L - 1)) to its logit for key j, after the softcap;
   * rotated codebook: stored vector = norm * codebook[idx] in the rotated domain; the original
     vector is diag(s) H (that) / sqrt(D), H the Sylvester-order Hadamard matrix;
-  * FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN) times one fp32 scale per KV head.
+  * FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN) times one fp32 scale per KV head;
+  * Turbo8 = K exactly as the FP8 format stores it (one scale per KV head, not rotated) and V
+    exactly as Turbo4 stores it (rotated 4-bit codebook with per-token norms).  Its scale array
+    is [pool][Hkv][16] V norms followed by the [Hkv] K scales; its codebook is the 16 V levels.
 
 Everything here is fp64; bf16 / fp8 / codebook values are widened exactly.
 """
@@ -34,7 +38,33 @@ import math
 import numpy as np
 
 BLOCK = 16
-_FMT_BITS = {"turbo4": (4, 4), "turbo3": (3, 4)}
+_FMT_BITS = {"turbo4": (4, 4), "turbo3": (3, 4)}   # codebook K and V bits
+
+
+def elem_kind(fmt: str, which: str) -> str:
+    """How K or V of a format is stored: 'bf16', 'fp8' (E4M3FN code, per-head scale) or 'cb'
+    (rotated-codebook index, per-token norm)."""
+    if fmt == "bf16":
+        return "bf16"
+    if fmt == "fp8" or (fmt == "turbo8" and which == "k"):
+        return "fp8"
+    return "cb"
+
+
+def fp8_scale(fmt: str, scales, which: str, hk: int, hkv: int):
+    """The fp32 dequantisation scale of an FP8-stored K or V of KV head hk (of hkv)."""
+    sc = np.asarray(scales)
+    if fmt == "turbo8":                      # the last hkv floats are the K scales
+        return sc.reshape(-1)[sc.size - hkv + hk]
+    return sc[0 if which == "k" else 1, hk]
+
+
+def norm_plane(fmt: str, scales, which: str, pool: int, hkv: int) -> np.ndarray:
+    """The [pool][Hkv][16] per-token norms of a codebook-stored K or V."""
+    sc = np.asarray(scales)
+    if fmt == "turbo8":
+        return sc.reshape(-1)[: pool * hkv * BLOCK].reshape(pool, hkv, BLOCK)
+    return sc[0 if which == "k" else 1]
 
 
 # --------------------------------------------------------------------------------------------
@@ -88,7 +118,7 @@ def _page_elems_k(fmt: str, chunk: np.ndarray, d: int) -> np.ndarray:
     if fmt == "bf16":     # [D/8][16 tokens][8] bf16
         x = chunk.view(np.uint16).reshape(d // 8, BLOCK, 8)
         return x.transpose(1, 0, 2).reshape(BLOCK, d)
-    if fmt == "fp8":      # [D/16][16 tokens][16] bytes
+    if elem_kind(fmt, "k") == "fp8":   # [D/16][16 tokens][16] bytes
         x = chunk.reshape(d // 16, BLOCK, 16)
         return x.transpose(1, 0, 2).reshape(BLOCK, d)
     kbits = _FMT_BITS[fmt][0]
@@ -127,17 +157,6 @@ def gather_norms(norms: np.ndarray, block_table_row: np.ndarray, hk: int, t0: in
     return norms[phys, hk, j % BLOCK].astype(np.float64)
 
 
-def dequant(fmt: str, which: str, stored: np.ndarray, *, scale=None, codebook=None,
-            norms=None) -> np.ndarray:
-    """Stored elements -> values in the storage domain (fp64).  For the rotated formats that
-    is norm * codebook[idx], still rotated."""
-    if fmt == "bf16":
-        return bf16_to_f64(stored)
-    if fmt == "fp8":
-        return E4M3FN_TABLE[stored] * np.float64(np.float32(scale))
-    return norms[:, None] * np.asarray(codebook, dtype=np.float64)[stored]
-
-
 def unrotate(x_rot: np.ndarray, sign: np.ndarray) -> np.ndarray:
     """x = diag(s) H x_rot / sqrt(D): the inverse of x_rot = H diag(s) x / sqrt(D)."""
     d = x_rot.shape[-1]
@@ -146,8 +165,11 @@ def unrotate(x_rot: np.ndarray, sign: np.ndarray) -> np.ndarray:
 
 
 def codebooks(fmt: str, codebook: np.ndarray):
-    kbits, _ = _FMT_BITS[fmt]
+    """(K levels or None, V levels) of a codebook format, fp32."""
     cb = np.asarray(codebook, dtype=np.float32)
+    if fmt == "turbo8":
+        return None, cb[:16]
+    kbits, _ = _FMT_BITS[fmt]
     return cb[: 1 << kbits], cb[1 << kbits: (1 << kbits) + 16]
 
 
@@ -155,14 +177,15 @@ def gather_kv(fmt: str, which: str, cache, block_table_row, hk, t0, t1, d, *, sc
               codebook=None, sign=None) -> np.ndarray:
     """Logical (original-domain) K or V vectors of tokens [t0, t1): fp64 [n, D]."""
     stored = gather_stored(fmt, which, cache, block_table_row, hk, t0, t1, d)
-    wi = 0 if which == "k" else 1
-    if fmt == "bf16":
-        return dequant(fmt, which, stored)
-    if fmt == "fp8":
-        return dequant(fmt, which, stored, scale=np.asarray(scales)[wi, hk])
-    norms = gather_norms(np.asarray(scales)[wi], block_table_row, hk, t0, t1)
-    cb = codebooks(fmt, codebook)[wi]
-    return unrotate(dequant(fmt, which, stored, codebook=cb, norms=norms), sign)
+    kind = elem_kind(fmt, which)
+    pool, hkv = cache.shape[0], cache.shape[1]
+    if kind == "bf16":
+        return bf16_to_f64(stored)
+    if kind == "fp8":
+        return E4M3FN_TABLE[stored] * np.float64(np.float32(fp8_scale(fmt, scales, which, hk, hkv)))
+    norms = gather_norms(norm_plane(fmt, scales, which, pool, hkv), block_table_row, hk, t0, t1)
+    cb = codebooks(fmt, codebook)[0 if which == "k" else 1]
+    return unrotate(norms[:, None] * cb.astype(np.float64)[stored], sign)
 
 
 # --------------------------------------------------------------------------------------------
@@ -307,13 +330,15 @@ def dequant_gather(fmt, which, cache, scales, codebook, block_table_row, hk, t0,
     export defines them: bf16 widened; fp8 value * scale rounded to fp32; codebook formats
     norm * level rounded to fp32 (still rotated)."""
     stored = gather_stored(fmt, which, cache, block_table_row, hk, t0, t0 + n, d)
-    wi = 0 if which == "k" else 1
-    if fmt == "bf16":
+    kind = elem_kind(fmt, which)
+    pool, hkv = cache.shape[0], cache.shape[1]
+    if kind == "bf16":
         return bf16_to_f64(stored).astype(np.float32)
-    if fmt == "fp8":
-        return (E4M3FN_TABLE[stored].astype(np.float32) * np.float32(np.asarray(scales)[wi, hk]))
-    norms = np.asarray(scales)[wi]
+    if kind == "fp8":
+        sc = np.float32(fp8_scale(fmt, scales, which, hk, hkv))
+        return E4M3FN_TABLE[stored].astype(np.float32) * sc
+    norms = norm_plane(fmt, scales, which, pool, hkv)
     j = np.arange(t0, t0 + n)
     nrm = norms[np.asarray(block_table_row)[j // BLOCK], hk, j % BLOCK].astype(np.float32)
-    cb = codebooks(fmt, codebook)[wi].astype(np.float32)
+    cb = codebooks(fmt, codebook)[0 if which == "k" else 1].astype(np.float32)
     return nrm[:, None] * cb[stored]

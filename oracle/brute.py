@@ -48,7 +48,7 @@ def _k_elem(fmt, kc, phys, hk, nkv, slot, d, D):
         base = (phys * nkv + hk) * 32 * D
         off = base + (((d // 8) * BLOCK + slot) * 8 + d % 8) * 2
         return ("v", _bf16(int(kc[off]), int(kc[off + 1])))
-    if fmt == "fp8":
+    if fmt in ("fp8", "turbo8"):               # Turbo8 K is stored exactly as FP8 K
         base = (phys * nkv + hk) * 16 * D
         return ("v", _e4m3(int(kc[base + ((d // 16) * BLOCK + slot) * 16 + d % 16])))
     bits = 4 if fmt == "turbo4" else 3
@@ -81,10 +81,18 @@ def _token_vector(fmt, which, cache_flat, phys, hk, nkv, slot, D, scales, codebo
     if fmt == "fp8":
         s = _f32(scales[wi][hk])
         return [x * s for _, x in raw]
-    kbits = 4 if fmt == "turbo4" else 3
+    flat = [float(x) for x in scales.reshape(-1)] if fmt == "turbo8" else None
+    if fmt == "turbo8" and which == "k":       # K scale of head hk: the last nkv floats
+        s = _f32(flat[len(flat) - nkv + hk])
+        return [x * s for _, x in raw]
     levels = [_f32(c) for c in codebook]
-    table = levels[: 1 << kbits] if which == "k" else levels[1 << kbits: (1 << kbits) + 16]
-    norm = _f32(scales[wi][phys][hk][slot])
+    if fmt == "turbo8":                        # 16 V levels; V norms [pool][nkv][16] first
+        table = levels[:16]
+        norm = _f32(flat[(phys * nkv + hk) * BLOCK + slot])
+    else:
+        kbits = 4 if fmt == "turbo4" else 3
+        table = levels[: 1 << kbits] if which == "k" else levels[1 << kbits: (1 << kbits) + 16]
+        norm = _f32(scales[wi][phys][hk][slot])
     rot = [norm * table[i] for _, i in raw]
     root = Decimal(D).sqrt()
     return [_f32(sign[d]) * sum(_hadamard_entry(d, e) * rot[e] for e in range(D)) / root

@@ -8,7 +8,8 @@ written out here on their own.
 
 What it follows (page titles and sections of the source pages):
   * attention.rs README, "KV Cache Formats": BF16, FP8 (E4M3) and the Walsh-Hadamard formats
-    Turbo4 (4-bit K + 4-bit V) and Turbo3 (3-bit K + 4-bit V) are cache storage formats.
+    Turbo8 (FP8 K + 4-bit V), Turbo4 (4-bit K + 4-bit V) and Turbo3 (3-bit K + 4-bit V) are
+    cache storage formats.
   * turboquant-rs 0.4.1 src/cache/cuda/attention.rs: the compressed cache holds packed indices
     and per-token scales, read back with a sign pattern and a codebook.
   * The recipe the compressed-cache workload states: each K and V token vector is multiplied
@@ -33,7 +34,7 @@ import math
 
 import numpy as np
 
-from .attention import BLOCK, _FMT_BITS, _page_elems_k, _page_elems_v
+from .attention import BLOCK, _FMT_BITS, _page_elems_k, _page_elems_v, elem_kind, fp8_scale
 
 
 # --------------------------------------------------------------------------------------------
@@ -146,7 +147,7 @@ def _pack_k_chunk(fmt: str, elems: np.ndarray, d: int) -> np.ndarray:
     if fmt == "bf16":     # [D/8][16][8] bf16
         x = np.asarray(elems, dtype=np.uint16).reshape(BLOCK, d // 8, 8).transpose(1, 0, 2)
         return np.ascontiguousarray(x).view(np.uint8).reshape(-1)
-    if fmt == "fp8":      # [D/16][16][16] bytes
+    if elem_kind(fmt, "k") == "fp8":      # [D/16][16][16] bytes (FP8 and Turbo8)
         x = np.asarray(elems, dtype=np.uint8).reshape(BLOCK, d // 16, 16).transpose(1, 0, 2)
         return np.ascontiguousarray(x).reshape(-1)
     kbits = _FMT_BITS[fmt][0]
@@ -164,18 +165,23 @@ def _pack_v_chunk(fmt: str, elems: np.ndarray, d: int) -> np.ndarray:
     return np.ascontiguousarray(pack_le(t, 4)).reshape(-1)
 
 
-def encode_tokens(fmt: str, which: str, x: np.ndarray, *, hk=None, scales=None, codebook=None,
-                  sign=None):
-    """Token vectors x [n, D] of one KV head -> (stored elements [n, D], norms [n] or None)."""
-    if fmt == "bf16":
+def encode_tokens(fmt: str, which: str, x: np.ndarray, *, hk=None, hkv=None, scales=None,
+                  codebook=None, sign=None):
+    """Token vectors x [n, D] of one KV head hk (of hkv) -> (stored elements [n, D], norms [n]
+    or None)."""
+    kind = elem_kind(fmt, which)
+    if kind == "bf16":
         return bf16_encode(x).astype(np.int64), None
-    wi = 0 if which == "k" else 1
-    if fmt == "fp8":
-        return fp8_encode(x, np.asarray(scales, dtype=np.float32)[wi, hk]).astype(np.int64), None
-    kbits = _FMT_BITS[fmt][wi]
+    if kind == "fp8":
+        sc = np.float32(fp8_scale(fmt, np.asarray(scales, dtype=np.float32), which, hk, hkv))
+        return fp8_encode(x, sc).astype(np.int64), None
     cb = np.asarray(codebook, dtype=np.float32)
+    if fmt == "turbo8":                   # the codebook is the 16 V levels
+        return turbo_encode(x, sign, cb[:16])
+    wi = 0 if which == "k" else 1
+    bits = _FMT_BITS[fmt][wi]
     kl = 1 << _FMT_BITS[fmt][0]
-    levels = cb[:kl] if which == "k" else cb[kl: kl + (1 << kbits)]
+    levels = cb[:kl] if which == "k" else cb[kl: kl + (1 << bits)]
     return turbo_encode(x, sign, levels)
 
 
@@ -186,8 +192,9 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
     k_new, v_new: fp32 [B][T][Hkv][D]; new token i of sequence b is token positions[b] + i,
     stored in page block_table[b][(positions[b] + i) // 16], slot (positions[b] + i) % 16.
     Tokens whose page index lies past the block table row, or whose page id lies outside the
-    pool, are skipped.  Returns (k_cache, v_cache, scales);
-    for the rotated formats the per-token norms go to scales [2][pool][Hkv][16]."""
+    pool, are skipped.  Returns (k_cache, v_cache, scales); for the rotated formats the
+    per-token norms go to scales [2][pool][Hkv][16] (Turbo8: V norms to the [pool][Hkv][16]
+    head of its flat scale array)."""
     k_cache = np.array(k_cache, copy=True)
     v_cache = np.array(v_cache, copy=True)
     scales = None if scales is None else np.array(scales, copy=True)
@@ -207,13 +214,16 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
             for hk in range(Hkv):
                 for which, src, cache in (("k", k_new, k_cache), ("v", v_new, v_cache)):
                     el, norm = encode_tokens(fmt, which, src[b, i, hk][None, :], hk=hk,
-                                             scales=scales, codebook=codebook, sign=sign)
+                                             hkv=Hkv, scales=scales, codebook=codebook,
+                                             sign=sign)
                     chunk = np.ascontiguousarray(cache[phys, hk])
                     read = _page_elems_k if which == "k" else _page_elems_v
                     pack = _pack_k_chunk if which == "k" else _pack_v_chunk
                     elems = np.array(read(fmt, chunk, d), dtype=np.int64)
                     elems[slot] = el[0]
                     cache[phys, hk] = pack(fmt, elems, d)
-                    if norm is not None:
+                    if norm is not None and fmt == "turbo8":
+                        scales[(phys * Hkv + hk) * BLOCK + slot] = norm[0]
+                    elif norm is not None:
                         scales[0 if which == "k" else 1, phys, hk, slot] = norm[0]
     return k_cache, v_cache, scales

@@ -107,10 +107,10 @@ def test_pack_unpack_random(bits, rng):
 
 def test_layout_sizes():
     for fmt, kb, vb in [("bf16", 4096, 4096), ("fp8", 2048, 2048), ("turbo4", 1024, 1024),
-                        ("turbo3", 768, 1024)]:
+                        ("turbo3", 768, 1024), ("turbo8", 2048, 1024)]:
         assert kvgen.k_chunk_bytes(fmt, 128) == kb and kvgen.v_chunk_bytes(fmt, 128) == vb
-    # bytes per (token, KV head): 512 / 256 / 136 / 120
-    assert [kvgen.kv_bytes_per_token_head(f, 128) for f in kvgen.FORMATS] == [512, 256, 136, 120]
+    # bytes per (token, KV head): 512 / 256 / 136 / 120 / 196 (Turbo8: 128 K + 64 V + 4 norm)
+    assert [kvgen.kv_bytes_per_token_head(f, 128) for f in kvgen.FORMATS] == [512, 256, 136, 120, 196]
 
 
 def test_config_shapes():
@@ -122,13 +122,30 @@ def test_config_shapes():
     assert s.softcap == 50.0
 
 
-def test_relayout_same_logical_cache():
-    inp = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo4", head_dim=128, context=100))
+@pytest.mark.parametrize("fmt", ["turbo4", "turbo8"])
+def test_relayout_same_logical_cache(fmt):
+    inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=128, context=100))
     other = kvgen.relayout(inp, 5)
     assert not (other.block_table == inp.block_table).all()
     a = oracle.decode_attention(*oracle_args(inp))
     b = oracle.decode_attention(*oracle_args(other))
     assert (a == b).all()
+
+
+def test_turbo8_scales_layout():
+    """Turbo8: K bytes and K scales exactly as the FP8 format writes them for the same draws,
+    V bytes and V norms exactly as Turbo4 writes them; scales = V norms, then K scales."""
+    kw = dict(head_dim=128, num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None,
+              ctx_range=(3, 70))
+    t8 = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo8", **kw))
+    f8 = kvgen.make_inputs(kvgen.spec("c1", fmt="fp8", **kw))
+    t4 = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo4", **kw))
+    pool = t8.num_pool_blocks
+    assert t8.scales.shape == (pool * 2 * 16 + 2,)
+    assert np.array_equal(t8.k_cache, f8.k_cache) and np.array_equal(t8.scales[-2:], f8.scales[0])
+    assert np.array_equal(t8.v_cache, t4.v_cache)
+    assert np.array_equal(t8.scales[:-2].reshape(pool, 2, 16), t4.scales[1], equal_nan=True)
+    assert np.array_equal(t8.codebook, t4.codebook[16:])
 
 
 def test_poison_spare_and_tail():

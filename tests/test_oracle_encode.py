@@ -15,6 +15,7 @@ import pytest
 
 import kvgen
 import oracle
+import oracle.attention as oa
 from oracle import encode as enc
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -173,13 +174,15 @@ def test_append_then_gather(fmt, rng):
         for hk in range(2):
             for which, new, cache, old in (("k", kn, k2, inp.k_cache), ("v", vn, v2, inp.v_cache)):
                 got = oracle.gather_stored(fmt, which, cache, inp.block_table[b], hk, pos[b], pos[b] + T, 128)
-                want, norm = enc.encode_tokens(fmt, which, new[b, :, hk], hk=hk, scales=inp.scales,
-                                               codebook=inp.codebook, sign=inp.sign)
+                want, norm = enc.encode_tokens(fmt, which, new[b, :, hk], hk=hk, hkv=2,
+                                               scales=inp.scales, codebook=inp.codebook,
+                                               sign=inp.sign)
                 assert np.array_equal(got, want)
                 if norm is not None:
                     j = np.arange(pos[b], pos[b] + T)
                     phys = inp.block_table[b][j // 16]
-                    assert np.array_equal(sc2[0 if which == "k" else 1, phys, hk, j % 16], norm)
+                    plane = oa.norm_plane(fmt, sc2, which, inp.num_pool_blocks, 2)
+                    assert np.array_equal(plane[phys, hk, j % 16], norm)
                 before = oracle.gather_stored(fmt, which, old, inp.block_table[b], hk, 0, pos[b], 128)
                 after = oracle.gather_stored(fmt, which, cache, inp.block_table[b], hk, 0, pos[b], 128)
                 assert np.array_equal(before, after)

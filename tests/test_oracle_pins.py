@@ -69,7 +69,7 @@ def test_brute_large_logits_cap_order():
     _vs_brute(inp)
 
 
-@pytest.mark.parametrize("fmt", ["turbo4", "turbo3"])
+@pytest.mark.parametrize("fmt", ["turbo4", "turbo3", "turbo8"])
 def test_brute_turbo_window(fmt):
     inp = _tiny(fmt, num_seqs=2, context=None, ctx_range=(5, 24), window=7, window_frac=0.5,
                 num_q_heads=2)
@@ -254,6 +254,22 @@ def test_planted_missing_sign(monkeypatch):
     assert _brute_mismatch(_tiny("turbo4", context=9, num_q_heads=2))
 
 
+def test_planted_turbo8_scale_of_wrong_head(monkeypatch):
+    """Turbo8 with two KV heads: the K scale of head 0 used for both heads, or the V norms
+    read from a [2][pool][Hkv][16]-style second plane, is caught by the brute force."""
+    inp = _tiny("turbo8", num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None,
+                ctx_range=(3, 30))
+    good = oa.fp8_scale
+    monkeypatch.setattr(oa, "fp8_scale", lambda f, sc, w, hk, hkv: good(f, sc, w, 0, hkv))
+    assert _brute_mismatch(inp)
+    monkeypatch.setattr(oa, "fp8_scale", good)
+    pool = inp.num_pool_blocks
+    flat = np.asarray(inp.scales)
+    monkeypatch.setattr(oa, "norm_plane", lambda f, sc, w, p, h: np.roll(
+        flat[: pool * 2 * 16], 2).reshape(pool, 2, 16))
+    assert _brute_mismatch(inp)
+
+
 def test_planted_window_off_by_one(monkeypatch):
     monkeypatch.setattr(oa, "attended_range", lambda L, W: ((max(0, L - W + 1) if W > 0 else 0), L))
     D = 64
@@ -345,7 +361,7 @@ def _slopes(h, base=8.0):
     return (2.0 ** (-base * (np.arange(h) + 1) / h)).astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
 def test_brute_alibi(fmt):
     inp = _tiny(fmt, num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None, ctx_range=(3, 40),
                 window=11, window_frac=0.5, softcap=2.0 if fmt == "bf16" else 0.0)
