@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention: effective KV GB/s (% of HBM peak) at 32K context"
 HBM_PEAK_GBS = 8000.0
 KV_NAMES = {"bf16": "bf16", "fp8": "fp8_e4m3", "turbo4": "turbo4 (K4/V4 rotated codebook)",
-            "turbo3": "turbo3 (K3/V4 rotated codebook)"}
+            "turbo3": "turbo3 (K3/V4 rotated codebook)",
+            "turbo8": "turbo8 (FP8 K + V4 rotated codebook)"}
 
 
 def parse():
@@ -37,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4",
-                    help="c1 c2 c3 c4 c5-t4 c5-t3 m-bf16 m-t4 m-t3 (see kvgen.SPECS)")
+                    help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 m-bf16 m-t4 m-t3 m-t8 (see kvgen.SPECS)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--partitions-per-wave", type=int, default=0,
                     help="launch tuning of the partition kernel (0 = the library's choice)")

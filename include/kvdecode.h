@@ -11,7 +11,8 @@
  *     out[b,h] = sum_j exp(z_j - max z) v_j / sum_j exp(z_j - max z)
  *
  * with k_j, v_j the dequantised key/value vectors of KV head floor(h / (Hq / Hkv)) (GQA/MQA).
- * Sources: attention.rs README ("KV Cache Formats": BF16, FP8 E4M3, Turbo4 and Turbo3 caches,
+ * Sources: attention.rs README ("KV Cache Formats": BF16, FP8 E4M3, Turbo8, Turbo4 and Turbo3
+ * caches,
  * each with decode and Split-K decode kernels sharing one float reduce, Split-K from 1024
  * tokens; "Features": softcapping, sliding window, GQA/MQA, paged block tables, causal mask;
  * the paged-attention bullet list adds "ALiBi slopes")
@@ -62,6 +63,10 @@
  *                         Stored value in the rotated domain: norm[t] * codebook[index];
  *                         the original vector is  x = diag(s) H x_rot / sqrt(D), H the
  *                         Sylvester-order D x D Hadamard matrix, s = sign_pattern.
+ *   TURBO8 (KVD_TURBO8)   FP8 K + 4-bit V ("FP8 K + 4-bit V (Walsh-Hadamard)" in the formats
+ *                         table; reading: K exactly as the FP8 format stores it -- not
+ *                         rotated, one fp32 scale per KV head -- and V exactly as the Turbo
+ *                         formats store it).  k_chunk = 16*D, v_chunk = 8*D bytes.
  *
  * Query q: bf16 [num_seqs][num_q_heads][D].  Output out: fp32 [num_seqs][num_q_heads][D], in
  * the original (un-rotated) domain for every format.
@@ -80,7 +85,8 @@ typedef enum kvd_format {
     KVD_BF16 = 0,       /* unquantised bfloat16 K and V */
     KVD_FP8_E4M3 = 1,   /* OCP E4M3FN codes, fp32 scale per KV head */
     KVD_TURBO4 = 2,     /* rotated codebook: 4-bit K, 4-bit V, fp32 per-token norms */
-    KVD_TURBO3 = 3      /* rotated codebook: 3-bit K, 4-bit V, fp32 per-token norms */
+    KVD_TURBO3 = 3,     /* rotated codebook: 3-bit K, 4-bit V, fp32 per-token norms */
+    KVD_TURBO8 = 4      /* FP8 K (fp32 scale per KV head) + rotated 4-bit V (per-token norms) */
 } kvd_format;
 
 typedef enum kvd_status {
@@ -134,8 +140,11 @@ size_t kvd_workspace_bytes(const kvd_dims* dims);
  *   context_lens int32 [B]; 0 gives an all-zero output row
  *   fmt          a kvd_format
  *   scales       KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv], K scales then V;
- *                Turbo: fp32 per-token norms [2][num_pool_blocks][Hkv][16], K then V
- *   codebook     Turbo: fp32 levels, 2^kbits for K then 16 for V (kbits 4 or 3); else unused
+ *                KVD_TURBO4/3: fp32 per-token norms [2][num_pool_blocks][Hkv][16], K then V;
+ *                KVD_TURBO8: fp32 V norms [num_pool_blocks][Hkv][16] followed by the [Hkv]
+ *                K scales (num_pool_blocks * Hkv * 16 + Hkv floats)
+ *   codebook     KVD_TURBO4/3: fp32 levels, 2^kbits for K then 16 for V (kbits 4 or 3);
+ *                KVD_TURBO8: the 16 V levels; else unused
  *   sign_pattern Turbo: fp32 [D] of +1.0 / -1.0; else unused
  *   softmax_scale  logit scale (e.g. 1/sqrt(D))
  *   window       int32 [B] sliding-window widths (0 = none), or NULL for no window at all
@@ -195,7 +204,7 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
 
 /* KV append (quantize-on-write): stores n_new new tokens of every sequence in the paged cache,
  * in the layout above, so the decode entry points read them back.  Sources: the attention.rs
- * README "KV Cache Formats" table (the four storage formats) and the compressed-cache recipe
+ * README "KV Cache Formats" table (the storage formats) and the compressed-cache recipe
  * (each token vector is flipped by the +-1 sign pattern, transformed by the orthonormal
  * Walsh-Hadamard transform, normalised by its fp32 L2 norm, stored per token, and each
  * coordinate replaced by the index of the nearest codebook level, indices bit-packed
@@ -208,7 +217,9 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
  *   n_new         tokens per sequence in this call (>= 0; 0 does nothing)
  *   k_cache, v_cache  the pools, updated in place (other tokens' bytes are preserved)
  *   scales        KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv] per-head scales
- *                 (read); Turbo: fp32 per-token norms [2][num_pool_blocks][Hkv][16] (written)
+ *                 (read); KVD_TURBO4/3: fp32 per-token norms [2][num_pool_blocks][Hkv][16]
+ *                 (written); KVD_TURBO8: the V norms (written) and K scales (read), laid out
+ *                 as for kvd_decode_attn_paged
  *   codebook, sign_pattern  Turbo: as for kvd_decode_attn_paged; else unused
  * Codes, decided exactly (readings where the pages are silent):
  *   BF16  round to nearest even; NaN stored as 0x7FC0.

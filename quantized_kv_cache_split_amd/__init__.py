@@ -12,21 +12,44 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "FORMATS",
+__all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "TURBO8", "FORMATS",
            "workspace_bytes", "decode_attn_paged", "decode_partitions", "reduce_partitions",
-           "dequant_gather", "status_str", "library_path", "load"]
+           "dequant_gather", "append_kv", "status_str", "library_path", "load",
+           "hip_runtimes_mapped"]
 
-BF16, FP8_E4M3, TURBO4, TURBO3 = 0, 1, 2, 3
-FORMATS = {"bf16": BF16, "fp8": FP8_E4M3, "turbo4": TURBO4, "turbo3": TURBO3}
+BF16, FP8_E4M3, TURBO4, TURBO3, TURBO8 = 0, 1, 2, 3, 4
+FORMATS = {"bf16": BF16, "fp8": FP8_E4M3, "turbo4": TURBO4, "turbo3": TURBO3, "turbo8": TURBO8}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkvdecode.so")
 _lib = None
 
 
+KVD_ERR_HIP = -6
+
+
+def _hip_error() -> str:
+    """Name and text of the HIP runtime's pending error on this thread (a failed launch leaves
+    its error there), or '' when there is none.  Reading it clears it."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipGetLastError.restype = ctypes.c_int
+        hip.hipGetErrorName.argtypes = [ctypes.c_int]
+        hip.hipGetErrorName.restype = ctypes.c_char_p
+        hip.hipGetErrorString.argtypes = [ctypes.c_int]
+        hip.hipGetErrorString.restype = ctypes.c_char_p
+        e = hip.hipGetLastError()
+        if e == 0:
+            return ""
+        return f" [{hip.hipGetErrorName(e).decode()} ({e}): {hip.hipGetErrorString(e).decode()}]"
+    except (OSError, AttributeError):
+        return ""
+
+
 class KvdError(RuntimeError):
     def __init__(self, status: int, where: str):
-        super().__init__(f"{where}: {status_str(status)} (status {status})")
+        detail = _hip_error() if status == KVD_ERR_HIP else ""
+        super().__init__(f"{where}: {status_str(status)} (status {status}){detail}")
         self.status = status
 
 
@@ -48,13 +71,37 @@ _ATTN_ARGS = [ctypes.POINTER(Dims), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_v
               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
 
 
+def hip_runtimes_mapped() -> list[str]:
+    """Files of the HIP runtime (libamdhip64) mapped into this process."""
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6 and os.path.basename(parts[5]).startswith("libamdhip64"):
+                paths.add(os.path.realpath(parts[5]))
+    return sorted(paths)
+
+
 def load() -> ctypes.CDLL:
-    """Load the built library (raises if it is missing)."""
+    """Load the built library (raises if it is missing).
+
+    torch ships its own HIP runtime.  The library links the system one by soname, so it is
+    loaded after torch, whose runtime then satisfies that dependency: one HIP runtime per
+    process.  Loaded first, it would bring in the system runtime and torch a second one, and
+    the two would not share streams or memory (launches fail, later calls crash)."""
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        try:
+            import torch  # noqa: F401  (its HIP runtime must be loaded first)
+        except ImportError:
+            pass
         lib = ctypes.CDLL(_LIB_PATH)
+        runtimes = hip_runtimes_mapped()
+        if len(runtimes) > 1:
+            raise RuntimeError("two HIP runtimes are loaded in this process (" + ", ".join(runtimes)
+                               + "); import torch before anything that loads a HIP runtime")
         lib.kvd_workspace_bytes.argtypes = [ctypes.POINTER(Dims)]
         lib.kvd_workspace_bytes.restype = ctypes.c_size_t
         for name in ("kvd_decode_attn_paged", "kvd_decode_partitions", "kvd_reduce_partitions"):

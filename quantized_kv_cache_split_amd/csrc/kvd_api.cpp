@@ -20,7 +20,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t k_chunk_bytes(int fmt, int d) {
     switch (fmt) {
         case KVD_BF16: return 32LL * d;
-        case KVD_FP8_E4M3: return 16LL * d;
+        case KVD_FP8_E4M3:
+        case KVD_TURBO8: return 16LL * d;   // Turbo8 K is stored as FP8 K
         case KVD_TURBO4: return 8LL * d;
         default: return 6LL * d;
     }
@@ -82,7 +83,7 @@ int choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
 // Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
 int check_dims(const kvd_dims* d, int fmt) {
     if (!d) return KVD_ERR_NULL;
-    if (fmt >= 0 && (fmt < KVD_BF16 || fmt > KVD_TURBO3)) return KVD_ERR_FORMAT;
+    if (fmt >= 0 && (fmt < KVD_BF16 || fmt > KVD_TURBO8)) return KVD_ERR_FORMAT;
     if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return KVD_ERR_SHAPE;
     if (d->num_q_heads % d->num_kv_heads != 0) return KVD_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return KVD_ERR_SHAPE;

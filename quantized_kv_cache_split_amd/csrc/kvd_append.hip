@@ -1,8 +1,9 @@
 // KV append (quantize-on-write) for the paged cache on gfx950: stores new tokens in the layout
 // the decode kernels read (include/kvdecode.h documents both).
 //
-// Formats as in the attention.rs README "KV Cache Formats" table (BF16, FP8 E4M3, Turbo4 and
-// Turbo3 with the Walsh-Hadamard rotation); the rotated-codebook recipe is the one the
+// Formats as in the attention.rs README "KV Cache Formats" table (BF16, FP8 E4M3, and Turbo8,
+// Turbo4 and Turbo3 with the Walsh-Hadamard rotation; Turbo8 writes K as FP8 and V as Turbo4
+// does); the rotated-codebook recipe is the one the
 // compressed-cache workload states: sign flip, orthonormal Walsh-Hadamard transform, fp32
 // L2 norm stored per token, nearest Lloyd-Max level per coordinate, little-endian bit packing
 // (turboquant-rs 0.4.1 src/cache/cuda/attention.rs reads exactly these: packed indices, per-
@@ -72,11 +73,16 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendP
     const size_t head = (size_t)phys * p.Hkv + hk;
     const size_t row = ((size_t)b * p.T + i) * p.Hkv + hk;
 
+    const size_t norm_plane = (size_t)p.pool * p.Hkv * kPageTokens;   // floats per norm plane
+    const bool t8 = p.fmt == KVD_TURBO8;
     for (int which = 0; which < 2; ++which) {
         const float* src = (which ? p.v_new : p.k_new) + row * p.D;
         uint8_t* chunk = (which ? p.v : p.k) + head * (which ? p.v_chunk : p.k_chunk);
-        if (p.fmt == KVD_BF16 || p.fmt == KVD_FP8_E4M3) {
-            const float scale = p.fmt == KVD_FP8_E4M3 ? p.scales[which * p.Hkv + hk] : 1.0f;
+        const bool fp8 = p.fmt == KVD_FP8_E4M3 || (t8 && which == 0);   // Turbo8 K is FP8 K
+        if (p.fmt == KVD_BF16 || fp8) {
+            // FP8: scales [2][Hkv]; Turbo8: the K scales follow the V norms
+            const float scale = !fp8 ? 1.0f
+                              : t8 ? p.scales[norm_plane + hk] : p.scales[which * p.Hkv + hk];
             for (int d = lane; d < p.D; d += 64) {
                 const float x = src[d];
                 if (p.fmt == KVD_BF16) {
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendP
         const double nd = (double)norm;
         const double u0 = nd > 0.0 ? r0 / nd : 0.0, u1 = nd > 0.0 ? r1 / nd : 0.0;
 
-        const int kl = 1 << p.kbits;
+        const int kl = t8 ? 0 : 1 << p.kbits;   // K levels ahead of the 16 V levels
         const int nlev = which ? 16 : kl;
         const float* lv = p.codebook + (which ? kl : 0);
         uint32_t i0 = 0, i1 = 0;
@@ -128,8 +134,8 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendP
             i0 += u0 > mid ? 1u : 0u;
             i1 += u1 > mid ? 1u : 0u;
         }
-        if (lane == 0)
-            p.scales[(size_t)which * p.pool * p.Hkv * kPageTokens + head * kPageTokens + t] = norm;
+        if (lane == 0)   // norm planes K then V (Turbo8: the V plane only)
+            p.scales[(which && !t8 ? norm_plane : 0) + head * kPageTokens + t] = norm;
 
         if (which == 1) {   // V [D][8 B]: nibble t of rows e0 and e0 + 1, shared bytes -> atomics
             uint32_t* words = reinterpret_cast<uint32_t*>(chunk);
@@ -169,8 +175,7 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendP
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
     const int64_t items = (int64_t)p.B * p.T * p.Hkv;
     const int64_t blocks = (items + kAppendWaves - 1) / kAppendWaves;
-    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(64 * kAppendWaves), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(append_kernel, dim3((unsigned)blocks), dim3(64 * kAppendWaves), s, p);
 }
 
 }  // namespace kvd

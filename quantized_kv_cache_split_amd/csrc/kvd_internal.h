@@ -15,7 +15,8 @@ constexpr int kMaxGroup = 16;       // query heads one MFMA tile (one wave) hand
 constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
 constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
-// the codebook formats (one per CU, sharing 128 KB of conflict-free codebook tables).
+// the codebook formats (sharing conflict-free codebook tables: 128 KB for Turbo4 / Turbo3, one
+// workgroup per CU; 64 KB for Turbo8, two per CU).
 constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
 // (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
 // a wave's run of partitions is capped at stage_rows(D) / group (BF16 / FP8).
@@ -31,8 +32,9 @@ struct LaunchParams {
     const int32_t* bt;        // [B][max_blocks]
     const int32_t* ctx;       // [B]
     const int32_t* win;       // [B] or nullptr
-    const float* scales;      // fp8 [2][Hkv]; turbo norms [2][pool][Hkv][16]
-    const float* codebook;    // turbo levels (K then V)
+    const float* scales;      // fp8 [2][Hkv]; turbo4/3 norms [2][pool][Hkv][16];
+                              // turbo8 [pool][Hkv][16] V norms then [Hkv] K scales
+    const float* codebook;    // turbo levels (K then V; turbo8: V only)
     const float* sign;        // turbo [D]
     const float* alibi;       // [Hq] ALiBi slopes or nullptr
     float* out;               // [B][Hq][D]
@@ -71,12 +73,24 @@ struct AppendParams {
     const int32_t* pos;       // [B] token index of each sequence's first new token
     uint8_t* k;               // K pool
     uint8_t* v;               // V pool
-    float* scales;            // FP8: [2][Hkv] (read); codebook formats: [2][pool][Hkv][16] (written)
-    const float* codebook;    // codebook formats: K levels then 16 V levels
+    float* scales;            // FP8: [2][Hkv] (read); Turbo4/3: [2][pool][Hkv][16] (written);
+                              // Turbo8: [pool][Hkv][16] V norms (written), then [Hkv] K scales (read)
+    const float* codebook;    // codebook formats: K levels then 16 V levels (Turbo8: V levels)
     const float* sign;        // codebook formats: [D]
     int64_t k_chunk, v_chunk;
     int32_t fmt, B, T, Hkv, D, max_blocks, pool, kbits;
 };
+
+// Launches `kernel` (which takes one parameter struct by value) and returns the status of this
+// launch alone.  hipGetLastError() after a triple-chevron launch would also report an error
+// left pending by any earlier, unrelated runtime call on the thread (the caller's, or another
+// library's) and blame this launch for it.
+template <typename Params>
+inline hipError_t launch_kernel(void (*kernel)(Params), dim3 grid, dim3 block, hipStream_t s,
+                                const Params& p) {
+    void* args[] = {const_cast<Params*>(&p)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s);
+}
 
 // Launchers (kvd_kernels.hip, kvd_append.hip).  Return hipSuccess or the launch error.
 hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStream_t s);

@@ -60,21 +60,20 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 constexpr int kLutCopies = 32;   // copies of each codebook pair table (one per LDS bank pair)
 constexpr float kLog2e = 1.4426950408889634f;
 
+// How K and V of each format are stored:
+//   K codebook (Turbo4, Turbo3): rotated-codebook indices with per-token norms;
+//   K FP8 (FP8, Turbo8): E4M3FN codes with one scale per KV head, not rotated;
+//   V codebook (Turbo4, Turbo3, Turbo8): rotated 4-bit codebook indices with per-token norms.
 template <int FMT>
-constexpr bool is_turbo() { return FMT == KVD_TURBO4 || FMT == KVD_TURBO3; }
+constexpr bool k_codebook() { return FMT == KVD_TURBO4 || FMT == KVD_TURBO3; }
+template <int FMT>
+constexpr bool k_fp8() { return FMT == KVD_FP8_E4M3 || FMT == KVD_TURBO8; }
+template <int FMT>
+constexpr bool v_codebook() { return k_codebook<FMT>() || FMT == KVD_TURBO8; }
 template <int FMT, int D>
-constexpr int k_chunk() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
+constexpr int k_chunk() { return FMT == KVD_BF16 ? 32 * D : k_fp8<FMT>() ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
 template <int FMT, int D>
 constexpr int v_chunk() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : 8 * D; }
-// Vector memory instructions load_pair issues for one page pair.
-template <int FMT, int D>
-constexpr int loads_per_pair() {
-    return FMT == KVD_BF16 ? D / 16 + D / 16 : FMT == KVD_FP8_E4M3 ? D / 32 + D / 16
-         : FMT == KVD_TURBO4 ? 2 + 8 + 4 : 2 + 8 + 4;
-}
-// s_waitcnt immediate that waits until at most n vector memory loads are outstanding (gfx9
-// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their maxima).
-constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 
 // ------------------------------------------------------------------------------------------
 // small helpers
@@ -242,6 +241,11 @@ template <> struct PairRaw<KVD_TURBO3, 128> {       // K [4][16][12 B], V [128][
     uint32_t v[8];
     f32x4 kn0, kn1, vn0, vn1;
 };
+template <> struct PairRaw<KVD_TURBO8, 128> {       // K [8][16][16] bytes, V [128][8 B], V norms
+    u32x4 kx[2], ky[2];
+    uint32_t v[8];
+    f32x4 vn0, vn1;
+};
 
 // Per-lane placement of the pair's tokens (see the header comment).
 struct LaneMap {
@@ -275,6 +279,19 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 #pragma unroll
         for (int i = 0; i < D / 16; ++i)
             r.v[i] = *reinterpret_cast<const u32x2*>(vch + (16 * i + ln.n) * 16 + ln.v_pos0);
+    } else if constexpr (FMT == KVD_TURBO8) {   // K as FP8, V and its norms as Turbo4
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const uint8_t* base = kch + 1024 * i + 256 * ln.j + 16 * ln.a_pos;
+            r.kx[i] = *reinterpret_cast<const u32x4*>(base);
+            r.ky[i] = *reinterpret_cast<const u32x4*>(base + 64);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r.v[i] = *reinterpret_cast<const uint32_t*>(vch + (16 * i + ln.n) * 8 + ln.v_pos0 / 2);
+        const size_t nb = (ln.v_sel ? headB : headA) * kPageTokens + ln.v_pos0;   // V norms first
+        r.vn0 = *reinterpret_cast<const f32x4*>(p.scales + nb);
+        r.vn1 = *reinterpret_cast<const f32x4*>(p.scales + nb + 4);
     } else {
         if constexpr (FMT == KVD_TURBO4) {   // 32-index group j of the lane's tokens
             const uint8_t* base = kch + 256 * ln.j + 16 * ln.a_pos;
@@ -312,12 +329,14 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // partitions.
 template <int FMT, int D, bool CAP, int PF>
 __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel(const LaunchParams p) {
-    constexpr bool kTurbo = is_turbo<FMT>();
+    constexpr bool kKcb = k_codebook<FMT>();   // rotated query, K table, K norms
+    constexpr bool kVcb = v_codebook<FMT>();   // V table, V norms, output in the rotated domain
+    constexpr int kTables = kKcb ? 2 : 1;      // codebook pair tables in LDS (V table last)
     constexpr int kW = waves_per_group(FMT);   // waves per workgroup
     constexpr int kThr = 64 * kW;
     constexpr int KS = D / 32;   // QK MFMA steps (k = 32 head elements each)
     constexpr int VT = D / 16;   // PV MFMA tiles (16 head elements each)
-    static_assert(!kTurbo || D == 128, "codebook formats are built for head_dim 128");
+    static_assert(!kVcb || D == 128, "codebook formats are built for head_dim 128");
     using Raw = PairRaw<FMT, D>;
 
     // LDS.  BF16 / FP8 (4 waves, two workgroups per CU): per-wave staging of finished (m, l, o)
@@ -325,10 +344,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     // the r-th partition of its run, query n) and copies them to the workspace after its walk,
     // so no global store joins the in-order stream of its loads; the unsplit merge uses rows
     // 0..g-1.  Rows are D + 4 floats apart so the 16 query rows a ds_write_b128 touches start
-    // in different banks.  Codebook formats (8 waves, one workgroup per CU): the two
-    // conflict-free pair tables (128 KB, at LDS address 0), reused for the unsplit merge once
-    // every wave has finished its walk; these compute-bound waves write partials directly.
-    constexpr int SR = kTurbo ? kMaxGroup : stage_rows(D);
+    // in different banks.  Codebook-V formats (8 waves): the conflict-free pair tables at LDS
+    // address 0 (K and V, 128 KB, one workgroup per CU for Turbo4 / Turbo3; V only, 64 KB, two
+    // per CU for Turbo8), reused for the unsplit merge once every wave has finished its walk;
+    // these waves write partials directly.
+    constexpr int SR = kVcb ? kMaxGroup : stage_rows(D);
     constexpr int SD = D + 4;
     struct Merge {
         float m[kW][SR];
@@ -340,15 +360,15 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     };
     struct LdsTurbo {
         union {
-            u32x4 lut[2][256 * kLutCopies / 2];   // K table at byte 0, V table at byte 65536
+            u32x4 lut[kTables][256 * kLutCopies / 2];   // [K table,] V table (64 KB each)
             Merge st;
         } u;
         float row[kMaxGroup * D];                 // query rotation / output rotation
         float rowscale[kMaxGroup];
     };
-    using Lds = typename std::conditional<kTurbo, LdsTurbo, LdsStage>::type;
+    using Lds = typename std::conditional<kVcb, LdsTurbo, LdsStage>::type;
     __shared__ Lds lds;
-    Merge& stg = [&]() -> Merge& { if constexpr (kTurbo) return lds.u.st; else return lds.st; }();
+    Merge& stg = [&]() -> Merge& { if constexpr (kVcb) return lds.u.st; else return lds.st; }();
     auto& sm_m = stg.m;
     auto& sm_l = stg.l;
     float (&sm_o)[kW][SR * SD] = *reinterpret_cast<float (*)[kW][SR * SD]>(&stg.o);
@@ -409,41 +429,53 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     ln.v_pos0 = 8 * (ln.j & 1);
     const int n = ln.n, j = ln.j;
     const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;   // copy of this lane
-    const uint32_t kbase = lut_lane, vbase = lut_lane | 0x10000u;       // K / V table
+    const uint32_t kbase = lut_lane;                                      // K table (byte 0)
+    const uint32_t vbase = lut_lane | (kKcb ? 0x10000u : 0u);             // V table
 
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
-    u32x4 qop[KS];                      // BF16 / FP8: q (bf16) for step s
-    u32x4 qdup[kTurbo ? KS : 1][2];     // codebook formats: q hi, each pair repeated
-    u32x4 qlo0[kTurbo ? KS : 1][2];     // codebook formats: q lo pairs interleaved with zeros
+    u32x4 qop[KS];                      // BF16 / FP8 K: q (bf16) for step s
+    u32x4 qdup[kKcb ? KS : 1][2];       // codebook K: q hi, each pair repeated
+    u32x4 qlo0[kKcb ? KS : 1][2];       // codebook K: q lo pairs interleaved with zeros
     float zscale;           // logit -> base-2 softmax argument (without per-token factors)
     float oscale = 1.0f;    // accumulator -> output units (FP8 V scale / codebook scales)
+    float ksc = 1.0f;       // K table normaliser (codebook K)
 
-    if constexpr (kTurbo) {
+    if constexpr (kVcb) {
         // codebook pair tables (levels scaled by a power of two so the largest magnitude is in
-        // [0.5, 1)); thread t builds entry t of both tables
-        const int kl = 1 << p.kbits;
+        // [0.5, 1)); the levels are 2^kbits K levels then 16 V levels, or (Turbo8) 16 V levels
+        const int kl = kKcb ? 1 << p.kbits : 0;
         float kmax = 0.0f, vmax = 0.0f;
         for (int i = 0; i < kl; ++i) kmax = fmaxf(kmax, fabsf(p.codebook[i]));
         for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
-        const float ksc = pow2_normaliser(kmax), vsc = pow2_normaliser(vmax);
+        ksc = pow2_normaliser(kmax);
+        const float vsc = pow2_normaliser(vmax);
         {
-            // 512 threads: thread t fills half the copies of entry t / 2 of both tables
+            // 512 threads: thread t fills half the copies of entry t / 2 of every table
             static_assert(kThr == 2 * 256, "one thread pair per table entry");
             const int e = tid >> 1, c0 = (tid & 1) * (kLutCopies / 2);
-            const int ki0 = e % kl, ki1 = (e / kl) % kl;
             uint32_t h, l;
-            f16_hilo(p.codebook[ki0] * ksc, p.codebook[ki1] * ksc, h, l);
-            const u32x4 kv = {h, l, h, l};
+            u32x4 kv = {0u, 0u, 0u, 0u};
+            if constexpr (kKcb) {
+                const int ki0 = e % kl, ki1 = (e / kl) % kl;
+                f16_hilo(p.codebook[ki0] * ksc, p.codebook[ki1] * ksc, h, l);
+                kv = u32x4{h, l, h, l};
+            }
             f16_hilo(p.codebook[kl + (e & 15)] * vsc, p.codebook[kl + (e >> 4)] * vsc, h, l);
             const u32x4 vv = {h, l, h, l};
 #pragma unroll
             for (int c = 0; c < kLutCopies / 2; c += 2) {
-                lds.u.lut[0][(e * kLutCopies + c0 + c) / 2] = kv;
-                lds.u.lut[1][(e * kLutCopies + c0 + c) / 2] = vv;
+                if constexpr (kKcb) lds.u.lut[0][(e * kLutCopies + c0 + c) / 2] = kv;
+                lds.u.lut[kTables - 1][(e * kLutCopies + c0 + c) / 2] = vv;
             }
         }
+        oscale = 1.0f / vsc;
+        // the tables are complete before any wave's walk reads them (codebook K: the query
+        // rotation's barriers below do the same)
+        if constexpr (!kKcb) __syncthreads();
+    }
+    if constexpr (kKcb) {
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
         for (int i = tid; i < g * D; i += kThr) {
             const int r = i / D, d = i % D;
@@ -478,7 +510,6 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             qlo0[s][1] = u32x4{l[2], 0u, l[3], 0u};
         }
         zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
-        oscale = 1.0f / vsc;
     } else {
         const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)qbase + qn) * D;
 #pragma unroll
@@ -488,9 +519,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             qop[s] = qlive ? w : u32x4{0u, 0u, 0u, 0u};
         }
         zscale = p.softmax_scale * kLog2e;
-        if constexpr (FMT == KVD_FP8_E4M3) {
+        if constexpr (FMT == KVD_FP8_E4M3) {   // scales [2][Hkv]: K then V
             zscale *= p.scales[hk];
             oscale = p.scales[p.Hkv + hk];
+        } else if constexpr (FMT == KVD_TURBO8) {   // K scales after the [pool][Hkv][16] V norms
+            zscale *= p.scales[(size_t)p.pool * p.Hkv * kPageTokens + hk];
         }
     }
     const float cap_l2 = CAP ? p.softcap * kLog2e : 0.0f;      // cap in base-2 units
@@ -550,7 +583,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 sx = mfma_bf16(r.kx[s], qop[s], sx);
                 sy = mfma_bf16(r.ky[s], qop[s], sy);
             }
-        } else if constexpr (FMT == KVD_FP8_E4M3) {
+        } else if constexpr (k_fp8<FMT>()) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const int i = s / 2, h = s % 2;
@@ -587,7 +620,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         float z[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) { z[e] = sx[e] * zscale; z[4 + e] = sy[e] * zscale; }
-        if constexpr (kTurbo) {
+        if constexpr (kKcb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) { z[e] *= r.kn0[e]; z[4 + e] *= r.kn1[e]; }
         }
@@ -604,8 +637,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
 #pragma unroll
             for (int e = 0; e < 8; ++e) z[e] += base + slope_l2 * (float)e;
         }
-        float vn[8];   // V norms (codebook formats)
-        if constexpr (kTurbo) {
+        float vn[8];   // V norms (codebook V)
+        if constexpr (kVcb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) { vn[e] = r.vn0[e]; vn[4 + e] = r.vn1[e]; }
         }
@@ -622,7 +655,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 vmask |= (ok ? 1u : 0u) << e;
                 z[e] = ok ? z[e] : -INFINITY;
             }
-            if constexpr (kTurbo) {
+            if constexpr (kVcb) {
                 // table levels are always finite, so zero norms (possibly NaN in unused slots)
                 // make the masked P' exactly 0
 #pragma unroll
@@ -661,7 +694,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         // the accumulator rescale is skipped on almost every pair.  The choice is wave-uniform.
         bool grow = mloc > m_run + kLazyLog2;
         float vloc = 0.0f;
-        if constexpr (kTurbo) {
+        if constexpr (kVcb) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vloc = fmaxf(vloc, vn[e]);
             vloc = max_over_groups(vloc);
@@ -671,7 +704,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             const float m_new = fmaxf(m_run, mloc);
             float f = fast_exp2(m_run - m_new);
             l_run *= f;
-            if constexpr (kTurbo) {
+            if constexpr (kVcb) {
                 const float sig_new = fmaxf(sig_run, vloc);
                 inv_sig = __builtin_amdgcn_rcpf(sig_new);
                 f *= sig_run * inv_sig;
@@ -686,7 +719,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_run); psum += pe[e]; }
         l_run += psum;
 
-        if constexpr (kTurbo) {
+        if constexpr (kVcb) {
             // P' = p * vnorm / sigma, rounded once to fp16 (each value repeated to match the
             // interleaved hi/lo V operand); the V levels keep their hi + lo precision
             uint32_t ph[4];
@@ -743,10 +776,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         if (k < npairs && tend >= part_end) {
             float lt = l_run + __shfl_xor(l_run, 16);
             lt += __shfl_xor(lt, 32);
-            const float osc = kTurbo ? oscale * sig_run : oscale;
+            const float osc = kVcb ? oscale * sig_run : oscale;
             const float sc = bad_ids ? __builtin_nanf("") : osc / lt;
             const float lx = lt * fast_exp2(m_run - m_true);   // the sum relative to the exact max
-            if constexpr (kTurbo) {
+            if constexpr (kVcb) {
                 if (qlive) {
                     const size_t slot = (row0 + n) * p.P + part;
 #pragma unroll
@@ -824,7 +857,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
 
     // ---- results ---------------------------------------------------------------------------
     if (si.split) {
-        if (kTurbo || !live) return;   // codebook formats wrote their triples directly
+        if (kVcb || !live) return;   // codebook-V formats wrote their triples directly
         // copy the run's staged triples to the workspace (this wave's own LDS rows: a
         // wavefront-scope fence orders the other lanes' writes before the reads)
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -849,11 +882,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
-    if constexpr (kTurbo) oscale *= sig_run;
+    if constexpr (kVcb) oscale *= sig_run;
 
     // unsplit: merge the waves through LDS, then write the final rows (the codebook formats'
     // merge rows reuse the tables, so every wave must have finished its walk first)
-    if constexpr (kTurbo) __syncthreads();
+    if constexpr (kVcb) __syncthreads();
     if (qlive) {
         if (j == 0) {
             sm_m[wave][n] = m_run;
@@ -879,10 +912,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         }
         float o = acc / wsum;
         if (wg_bad) o = __builtin_nanf("");
-        if constexpr (kTurbo) lds.row[i] = o;
+        if constexpr (kVcb) lds.row[i] = o;
         else out_rows[i] = o;
     }
-    if constexpr (kTurbo) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
+    if constexpr (kVcb) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
         __syncthreads();
         fwht_rows<D>(lds.row, g, tid, kThr);
         const float rs = 1.0f / sqrtf((float)D);
@@ -900,7 +933,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
 // blocks after the first rescale the running sums to the new maximum (online LSE).
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
-    constexpr bool kTurbo = is_turbo<FMT>();
+    constexpr bool kVcb = v_codebook<FMT>();   // partial outputs are in the rotated domain
     constexpr int E = D / 64;
     constexpr int kBlock = 64;
     const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
@@ -953,7 +986,7 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] *= inv;
 
-    if constexpr (kTurbo) {   // diag(s) H o / sqrt(D): butterflies in registers, then lanes
+    if constexpr (kVcb) {   // diag(s) H o / sqrt(D): butterflies in registers, then lanes
         static_assert(E == 2, "codebook formats are built for head_dim 128");
         const float a0 = acc[0], a1 = acc[1];
         acc[0] = a0 + a1;
@@ -991,17 +1024,20 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     const size_t head = (size_t)phys * p.Hkv + p.kv_head;
     const uint8_t* ch = p.cache + head * p.chunk;
     float val;
+    const size_t norm_plane = (size_t)p.pool * p.Hkv * kPageTokens;   // floats per norm plane
     if (p.fmt == KVD_BF16) {
         const size_t off = p.is_v ? (size_t)d * 16 + pos : ((size_t)(d / 8) * 16 + pos) * 8 + d % 8;
         val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(ch)[off]);
-    } else if (p.fmt == KVD_FP8_E4M3) {
+    } else if (p.fmt == KVD_FP8_E4M3 || (p.fmt == KVD_TURBO8 && !p.is_v)) {
         const size_t off = p.is_v ? (size_t)d * 16 + pos : ((size_t)(d / 16) * 16 + pos) * 16 + d % 16;
         const uint32_t w = reinterpret_cast<const uint32_t*>(ch)[off / 4];
         const u32x2 bf = fp8x4_to_bf16(w);
         const int e = off % 4;
         const uint32_t pair = bf[e / 2];
         val = bf16_bits_to_f32((e & 1) ? (pair >> 16) : (pair & 0xFFFFu));
-        val *= p.scales[(p.is_v ? p.Hkv : 0) + p.kv_head];
+        // FP8: scales [2][Hkv]; Turbo8: the K scales follow the V norms
+        val *= p.fmt == KVD_TURBO8 ? p.scales[norm_plane + p.kv_head]
+                                   : p.scales[(p.is_v ? p.Hkv : 0) + p.kv_head];
     } else {
         uint32_t idx;
         if (p.is_v) {
@@ -1015,9 +1051,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
             const int e = d % 32;
             idx = (tri_field(g3[0], g3[1], g3[2], e / 8) >> (3 * (e % 8))) & 7u;
         }
-        const int kl = 1 << p.kbits;
+        // levels: 2^kbits K then 16 V (Turbo8: the 16 V levels); norm planes K then V
+        // (Turbo8: the V plane only)
+        const bool t8 = p.fmt == KVD_TURBO8;
+        const int kl = t8 ? 0 : 1 << p.kbits;
         const float lvl = p.codebook[(p.is_v ? kl : 0) + idx];
-        const size_t nb = (size_t)(p.is_v ? p.pool : 0) * p.Hkv * kPageTokens + head * kPageTokens + pos;
+        const size_t nb = (p.is_v && !t8 ? norm_plane : 0) + head * kPageTokens + pos;
         val = p.scales[nb] * lvl;
     }
     p.out[i] = val;
@@ -1033,16 +1072,13 @@ constexpr int prefetch_depth() { return 2; }
 template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
     constexpr int PF = prefetch_depth<FMT>();
-    if (p.softcap > 0.0f)
-        hipLaunchKernelGGL((partition_kernel<FMT, D, true, PF>), grid, dim3(64 * waves_per_group(FMT)), 0, s, p);
-    else
-        hipLaunchKernelGGL((partition_kernel<FMT, D, false, PF>), grid, dim3(64 * waves_per_group(FMT)), 0, s, p);
-    return hipGetLastError();
+    const dim3 block(64 * waves_per_group(FMT));
+    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF>, grid, block, s, p)
+                            : launch_kernel(partition_kernel<FMT, D, false, PF>, grid, block, s, p);
 }
 template <int FMT, int D>
 hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
-    hipLaunchKernelGGL((reduce_kernel<FMT, D>), dim3(p.Hq, p.B), dim3(64), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(reduce_kernel<FMT, D>, dim3(p.Hq, p.B), dim3(64), s, p);
 }
 
 }  // namespace
@@ -1054,6 +1090,7 @@ hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStrea
         case KVD_FP8_E4M3: return p.D == 64 ? launch_partitions_t<KVD_FP8_E4M3, 64>(p, grid, s)
                                             : launch_partitions_t<KVD_FP8_E4M3, 128>(p, grid, s);
         case KVD_TURBO4: return launch_partitions_t<KVD_TURBO4, 128>(p, grid, s);
+        case KVD_TURBO8: return launch_partitions_t<KVD_TURBO8, 128>(p, grid, s);
         default: return launch_partitions_t<KVD_TURBO3, 128>(p, grid, s);
     }
 }
@@ -1065,14 +1102,14 @@ hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s) {
         case KVD_FP8_E4M3: return p.D == 64 ? launch_reduce_t<KVD_FP8_E4M3, 64>(p, s)
                                             : launch_reduce_t<KVD_FP8_E4M3, 128>(p, s);
         case KVD_TURBO4: return launch_reduce_t<KVD_TURBO4, 128>(p, s);
+        case KVD_TURBO8: return launch_reduce_t<KVD_TURBO8, 128>(p, s);
         default: return launch_reduce_t<KVD_TURBO3, 128>(p, s);
     }
 }
 
 hipError_t launch_gather(const GatherParams& p, hipStream_t s) {
     const int total = p.n * p.D;
-    hipLaunchKernelGGL(gather_kernel, dim3((total + 255) / 256), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(gather_kernel, dim3((total + 255) / 256), dim3(256), s, p);
 }
 
 }  // namespace kvd

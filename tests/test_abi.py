@@ -26,6 +26,19 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_one_hip_runtime_per_process():
+    """Loading the library leaves exactly one HIP runtime mapped: torch's, when torch is
+    installed (the library binds to it instead of loading the system copy beside it)."""
+    kvd.load()
+    maps = kvd.hip_runtimes_mapped()
+    assert len(maps) == 1, maps
+    try:
+        import torch
+    except ImportError:
+        return
+    assert os.path.dirname(maps[0]) == os.path.realpath(os.path.join(os.path.dirname(torch.__file__), "lib"))
+
+
 def dims(**kw):
     base = dict(num_seqs=16, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
                 max_blocks_per_seq=2048, num_pool_blocks=33792, max_context_len=32768,
@@ -76,6 +89,7 @@ def test_shape_errors(field, value):
 
 def test_turbo_needs_d128():
     assert call(dims(head_dim=64), fmt=2) == -2
+    assert call(dims(head_dim=64), fmt=4) == -2      # Turbo8 (codebook V)
 
 
 def test_format_error():
@@ -91,6 +105,8 @@ def test_fp8_and_turbo_need_their_arrays():
     assert call(fmt=1, scales=None) == -1
     assert call(fmt=2, cb=None) == -1
     assert call(fmt=3, sign=None) == -1
+    assert call(fmt=4, scales=None) == -1 and call(fmt=4, cb=None) == -1
+    assert call(fmt=4, sign=None) == -1
     assert call(fmt=0, scales=None, cb=None, sign=None, ws_bytes=0) == -5
 
 
@@ -147,6 +163,7 @@ def test_append_arg_errors():
         assert append_call(**{arg: None}) == -1, arg
     assert append_call(fmt=1, scales=None) == -1
     assert append_call(fmt=2, cb=None) == -1 and append_call(fmt=3, sign=None) == -1
+    assert append_call(fmt=4, scales=None) == -1 and append_call(fmt=4, cb=None) == -1
     assert append_call(fmt=0, scales=None, cb=None, sign=None, n=0) == 0    # BF16 needs neither
     assert append_call(k=FAKE + 4) == -4 and append_call(kc=FAKE + 8) == -4
     assert append_call(n=0) == 0 and append_call(dims(num_seqs=0)) == 0    # nothing launched

@@ -104,6 +104,15 @@ def test_append_fp8_saturation_and_nan():
     _assert_same(gpu, ref, "fp8 saturation")
 
 
+def test_append_turbo8_k_saturation():
+    """Turbo8 K goes through the FP8 encoder with the per-head K scale stored after the V
+    norms: saturation, infinities, NaN and signed zero as for FP8."""
+    def mutate(kn, vn, pos, bt, inp):
+        kn[0, 0, 1, :8] = [1e9, -1e9, np.inf, -np.inf, np.nan, 0.0, -0.0, 1e-30]
+    inp, gpu, ref = _append_case("turbo8", [2, 9], 3, seed=11, mutate=mutate)
+    _assert_same(gpu, ref, "turbo8 K saturation")
+
+
 def test_append_bf16_nan_inf():
     def mutate(kn, vn, pos, bt, inp):
         kn[0, 0, 0, :4] = [np.nan, np.inf, -np.inf, 3.4e38]
@@ -111,7 +120,7 @@ def test_append_bf16_nan_inf():
     _assert_same(gpu, ref, "bf16 nan/inf")
 
 
-@pytest.mark.parametrize("fmt", ["turbo4", "turbo3"])
+@pytest.mark.parametrize("fmt", ["turbo4", "turbo3", "turbo8"])
 def test_append_turbo_zero_and_scaled_vectors(fmt):
     def mutate(kn, vn, pos, bt, inp):
         kn[0, 0, 0] = 0.0

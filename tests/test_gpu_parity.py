@@ -83,6 +83,28 @@ def test_fp8_all_codes_decode_exactly():
         assert len(set(cache[phys, 0].tolist())) == 256
 
 
+def test_turbo8_k_all_codes_decode_exactly():
+    """Every E4M3FN code as Turbo8 K, whose per-head scales sit after the V norms."""
+    import torch
+    inp = _small("turbo8", num_seqs=1, context=16, num_kv_heads=2, num_q_heads=4)
+    phys = int(inp.block_table[0, 0])
+    codes = (np.arange(inp.k_cache.shape[-1]) * 7 % 256).astype(np.uint8)
+    inp.k_cache[phys, 1] = codes
+    inp.scales[-2:] = np.array([0.5, 0.37], np.float32)
+    gb = GpuBatch(inp)
+    out = torch.empty((16, 128), device="cuda:0")
+    gb.kvd.dequant_gather(gb.dims, "turbo8", False, gb.t["k_cache"], gb.t["scales"],
+                          gb.t["codebook"], gb.t["block_table"], 0, 1, 0, 16, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.dequant_gather("turbo8", "k", inp.k_cache, inp.scales, inp.codebook,
+                                 inp.block_table[0], 1, 0, 16, 128)
+    assert (np.isnan(got) == np.isnan(want)).all()
+    ok = ~np.isnan(want)
+    assert (got[ok].view(np.uint32) == want[ok].view(np.uint32)).all()
+    assert np.nanmax(np.abs(want)) == np.float32(448) * np.float32(0.37)   # head 1's scale
+
+
 # --------------------------------------------------------------------------------------------
 # the tiny config: single partition, explicit 3-way split (128), forced single, auto
 # --------------------------------------------------------------------------------------------
@@ -233,7 +255,7 @@ def test_partials_match_oracle(fmt, run):
                 # feed fp16 operands (query and level each rounded to 11 significant bits), so
                 # |dz| <= 2^-10 * scale * |q| * max_t |k_t|  (Cauchy-Schwarz).
                 tol = 1e-4
-                if fmt.startswith("turbo"):
+                if fmt in ("turbo4", "turbo3"):   # codebook K (Turbo8 K is FP8: exact products)
                     kk = oracle.gather_kv(fmt, "k", inp.k_cache, inp.block_table[b], hk, lo_, hi_,
                                           s.head_dim, scales=inp.scales, codebook=inp.codebook,
                                           sign=inp.sign)
@@ -309,7 +331,7 @@ def test_alibi_position_coded_v(fmt):
         assert np.abs(gpu[h] - want).max() < 2e-6, h
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "turbo4"])
+@pytest.mark.parametrize("fmt", ["bf16", "turbo4", "turbo8"])
 def test_alibi_partials_match_oracle(fmt):
     inp = _small(fmt, context=None, ctx_range=(200, 700), num_seqs=2)
     sl = _slopes(inp.spec.num_q_heads)
