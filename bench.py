@@ -293,7 +293,8 @@ def main():
             "window": spec.window, "softcap": spec.softcap,
             "kv_format": KV_NAMES[spec.fmt], "block_size": 16,
             "partition_size": ps if ps else 512, "kv_bytes_per_step": kv_bytes,
-            "mfma_operands": "bf16 (bf16/fp8 caches), fp16 (codebook caches); fp32 accumulate",
+            "mfma_operands": "bf16 for BF16/FP8 K and V, fp16 for codebook K and V (Turbo8: "
+                             "bf16 QK, fp16 PV); fp32 accumulate",
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(spec.num_seqs / mean_call, 1),
