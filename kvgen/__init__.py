@@ -67,6 +67,7 @@ class Spec:
     pool_total: int | None = None         # explicit pool size (overrides pool_spare)
     partition_size: int = 0               # 0 = auto (512, split at >= 1024 tokens)
     seed: int = 0
+    queries_per_seq: int = 1              # > 1: a chunk of queries at the last positions
 
     @property
     def group(self) -> int:
@@ -312,7 +313,7 @@ def pack_v_pages(fmt: str, elems: np.ndarray) -> np.ndarray:
 class Inputs:
     """One synthetic batch, host-side, exactly as the C ABI consumes it."""
     spec: Spec
-    q: np.ndarray                 # uint16 [B, Hq, D] bf16 bits
+    q: np.ndarray                 # uint16 [B, Hq, D] bf16 bits ([B, n_q, Hq, D] for n_q > 1)
     k_cache: np.ndarray           # uint8 [pool, Hkv, k_chunk_bytes]
     v_cache: np.ndarray           # uint8 [pool, Hkv, v_chunk_bytes]
     scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo4/3: f32 [2, pool, Hkv, 16];
@@ -338,10 +339,11 @@ class Inputs:
         return self.block_table.shape[1]
 
     def spans(self) -> np.ndarray:
-        """Attended tokens per sequence: min(L, W) if windowed, else L."""
+        """Keys any query of a sequence attends to: min(L, W + n_q - 1) if windowed, else L
+        (n_q = 1 for decode)."""
         L = self.context_lens.astype(np.int64)
         W = self.window.astype(np.int64)
-        return np.where(W > 0, np.minimum(L, W), L)
+        return np.where(W > 0, np.minimum(L, W + self.spec.queries_per_seq - 1), L)
 
     def kv_bytes(self) -> int:
         """Algorithmic cache bytes one call must read."""
@@ -416,8 +418,9 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         else:
             bt[b, n_pages[b]:] = -1
 
-    # query
-    q = bf16_bits(r["q"].standard_normal((B, s.num_q_heads, D), dtype=np.float32))
+    # query: [B, Hq, D], or [B, n_q, Hq, D] for a chunk of n_q queries per sequence
+    qshape = (B, s.num_q_heads, D) if s.queries_per_seq == 1 else (B, s.queries_per_seq, s.num_q_heads, D)
+    q = bf16_bits(r["q"].standard_normal(qshape, dtype=np.float32))
 
     kb, vb = k_chunk_bytes(fmt, D), v_chunk_bytes(fmt, D)
     k_cache = np.empty((pool, Hkv, kb), dtype=np.uint8)

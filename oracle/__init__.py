@@ -1,7 +1,8 @@
 """Oracle for paged decode attention -- TEST INFRASTRUCTURE ONLY.
 
-Plain fp64 CPU definition of decode attention (``attention``), a 40-digit ``decimal`` brute
-force (``brute``) and the cache writer that stores new tokens (``encode``).
+Plain fp64 CPU definition of decode attention (``attention``), of multi-query (chunked-prefill)
+attention over the same cache (``multiquery``), a 40-digit ``decimal`` brute force (``brute``)
+and the cache writer that stores new tokens (``encode``).
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
 this package; the GPU library never does, and the two share no code.
 """
@@ -24,3 +25,4 @@ from .attention import (  # noqa: F401
     unrotate,
 )
 from . import encode  # noqa: F401,E402
+from .multiquery import multi_query_attention, multi_query_partials  # noqa: F401,E402

@@ -149,3 +149,59 @@ def brute_decode_attention(q_bits, k_cache, v_cache, block_table, context_lens, 
             rows.append([sum(p[j] * vals[hk, j][d] for j in z) / den for d in range(D)])
         out.append(rows)
     return out
+
+
+def brute_multi_query(q_bits, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
+                      sign, softmax_scale, window, softcap, num_kv_heads, head_dim, alibi=None):
+    """Chunk of n_q queries per sequence (q_bits nested [B][n_q][Hq][D]): query i at position
+    p = L - n_q + i takes the keys j with lo <= j <= p, lo = p + 1 - W under a window W (else 0),
+    and adds alibi[h] * (j - p) after the cap.  Nested lists out[b][i][h][d] of Decimal."""
+    B, n_q, Hq, D = len(q_bits), len(q_bits[0]), len(q_bits[0][0]), head_dim
+    g = Hq // num_kv_heads
+    kc = k_cache.reshape(-1)
+    vc = v_cache.reshape(-1)
+    scale = _f32(softmax_scale)
+    cap = _f32(softcap)
+    out = []
+    for b in range(B):
+        L = int(context_lens[b])
+        W = 0 if window is None else int(window[b])
+        cache_k, cache_v = {}, {}
+
+        def key(hk, j):
+            if (hk, j) not in cache_k:
+                phys = int(block_table[b][j // BLOCK])
+                cache_k[hk, j] = _token_vector(fmt, "k", kc, phys, hk, num_kv_heads, j % BLOCK, D,
+                                               scales, codebook, sign)
+                cache_v[hk, j] = _token_vector(fmt, "v", vc, phys, hk, num_kv_heads, j % BLOCK, D,
+                                               scales, codebook, sign)
+            return cache_k[hk, j], cache_v[hk, j]
+
+        seq = []
+        for i in range(n_q):
+            rows = []
+            for h in range(Hq):
+                if L == 0:
+                    rows.append([Decimal(0)] * D)
+                    continue
+                hk = h // g
+                pos = L - n_q + i
+                lo = max(0, pos + 1 - W) if W > 0 else 0
+                qv = [_bf16(int(q_bits[b][i][h][d]) & 0xFF, int(q_bits[b][i][h][d]) >> 8)
+                      for d in range(D)]
+                z = {}
+                for j in range(lo, pos + 1):
+                    kj = key(hk, j)[0]
+                    x = scale * sum(qv[d] * kj[d] for d in range(D))
+                    if cap > 0:
+                        x = cap * _tanh(x / cap)
+                    if alibi is not None:
+                        x += _f32(alibi[h]) * (j - pos)
+                    z[j] = x
+                m = max(z.values())
+                p = {j: (z[j] - m).exp() for j in z}
+                den = sum(p.values())
+                rows.append([sum(p[j] * key(hk, j)[1][d] for j in z) / den for d in range(D)])
+            seq.append(rows)
+        out.append(seq)
+    return out
