@@ -26,6 +26,14 @@
  * (per query head, the query at position L - 1) is added after the cap; an empty context
  * gives zero rows; partitions sit at absolute multiples of the partition size.
  *
+ * A chunk of queries per sequence (kvd_dims.queries_per_seq = n_q > 1; the README's "Chunked
+ * Prefill" and "causal masking" over the same paged, possibly compressed cache): the n_q
+ * queries occupy the last n_q positions of the context (their K and V are already in the
+ * cache).  Query i sits at position p = L - n_q + i and attends causally exactly like the
+ * decode query of the context prefix that ends there: keys [lo_i, p] with lo_i = max(0, p + 1 -
+ * window[b]) under a window, else 0; the ALiBi term is alibi_slopes[h] * (j - p).  A sequence
+ * with 0 < L < n_q gets NaN rows (its query positions would be negative).
+ *
  * Conventions for every entry point.
  *   - All array pointers are DEVICE pointers owned by the caller.  The library never
  *     allocates, frees or synchronises; it keeps no state between calls.
@@ -68,8 +76,8 @@
  *                         rotated, one fp32 scale per KV head -- and V exactly as the Turbo
  *                         formats store it).  k_chunk = 16*D, v_chunk = 8*D bytes.
  *
- * Query q: bf16 [num_seqs][num_q_heads][D].  Output out: fp32 [num_seqs][num_q_heads][D], in
- * the original (un-rotated) domain for every format.
+ * Query q: bf16 [num_seqs][n_q][num_q_heads][D] (n_q = 1: [num_seqs][num_q_heads][D]).
+ * Output out: fp32 with the same shape, in the original (un-rotated) domain for every format.
  */
 #ifndef KVDECODE_H
 #define KVDECODE_H
@@ -121,19 +129,24 @@ typedef struct kvd_dims {
                                     walks (it writes every partition's triple).  0: auto
                                     (about one wavefront per resident slot of the device when
                                     every sequence had max_context_len tokens, at most 4);
-                                    > 0: that many.  Capped at 4096 / (head_dim * Hq / Hkv)
-                                    and treated as 1 when the partition size is not a
-                                    multiple of 32.  Must be >= 0. */
+                                    > 0: that many.  Capped at 4096 / (head_dim * rows),
+                                    rows = min(16, n_q * Hq / Hkv), and treated as 1 when the
+                                    partition size is not a multiple of 32.  Must be >= 0. */
+    int32_t queries_per_seq;     /* n_q: queries per sequence, a chunk at the last n_q positions
+                                    (above); 0 or 1: single-query decode.  The n_q * Hq / Hkv
+                                    query rows of a KV head share one pass over its pages per
+                                    16 rows.  Requires n_q <= max_context_len and
+                                    num_seqs * n_q <= 65535. */
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: the per-partition fp32 triples
- * m [B][Hq][P], l [B][Hq][P] and o [B][Hq][P][D], P = ceil(max_context_len / partition size),
- * each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
+ * m [B][n_q][Hq][P], l [B][n_q][Hq][P] and o [B][n_q][Hq][P][D], P = ceil(max_context_len /
+ * partition size), each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
 size_t kvd_workspace_bytes(const kvd_dims* dims);
 
 /* Decode attention, both phases (partition kernel, then the reduce kernel when any sequence
  * is split).
- *   q            bf16 [B][Hq][D]
+ *   q            bf16 [B][n_q][Hq][D]
  *   k_cache      K pool in `fmt`'s layout (above);  v_cache  V pool
  *   block_table  int32 [B][max_blocks_per_seq]; entries for the pages holding the attended
  *                range [lo, L) must be valid pool indices (others are never read)
@@ -150,7 +163,7 @@ size_t kvd_workspace_bytes(const kvd_dims* dims);
  *   window       int32 [B] sliding-window widths (0 = none), or NULL for no window at all
  *   softcap      tanh cap on the scaled logits; 0 = off
  *   alibi_slopes fp32 [Hq] per-query-head ALiBi slopes, or NULL for none
- *   out          fp32 [B][Hq][D]; must not alias any input
+ *   out          fp32 [B][n_q][Hq][D]; must not alias any input
  *   workspace    >= kvd_workspace_bytes(dims) bytes, 256-byte aligned; contents on entry do
  *                not matter; on return it holds the partials of split sequences
  *   stream       hipStream_t
@@ -166,10 +179,12 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
 /* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
  * partitions_per_wave partitions, four wavefronts per workgroup.  For a split sequence,
  * partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and its triple goes to the
- * workspace at (b, h, p):  m = max_j z_j * log2(e)  (base-2 units),
+ * workspace at (b, i, h, p):  m = max_j z_j * log2(e)  (base-2 units),
  * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
- * rotated domain for the Turbo formats.  Empty partitions are not written.  Sequences that are
- * not split get their final output row written here. */
+ * rotated domain for the Turbo formats; the keys j are those of the partition that query i
+ * sees, and a query that sees none of them gets m = -inf, l = 0, o = 0.  Partitions outside
+ * the sequence's range are not written.  Sequences that are not split get their final output
+ * row written here. */
 int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,

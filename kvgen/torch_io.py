@@ -11,7 +11,7 @@ def dims_kwargs(inp, partition_size: int | None = None, partitions_per_wave: int
                 head_dim=s.head_dim, block_size=16, max_blocks_per_seq=inp.max_blocks_per_seq,
                 num_pool_blocks=inp.num_pool_blocks, max_context_len=inp.max_context_len,
                 partition_size=s.partition_size if partition_size is None else partition_size,
-                partitions_per_wave=partitions_per_wave)
+                partitions_per_wave=partitions_per_wave, queries_per_seq=s.queries_per_seq)
 
 
 def to_torch(inp, device) -> dict:

@@ -58,7 +58,8 @@ class Dims(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_pool_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
-                ("partition_size", ctypes.c_int32), ("partitions_per_wave", ctypes.c_int32)]
+                ("partition_size", ctypes.c_int32), ("partitions_per_wave", ctypes.c_int32),
+                ("queries_per_seq", ctypes.c_int32)]
 
 
 def library_path() -> str:

@@ -37,10 +37,15 @@ struct Plan {
     size_t off_l, off_o, bytes;
 };
 
-// Query tiles per KV head: groups of up to kMaxGroup query heads share one MFMA tile.
+// Queries per sequence (a chunk at the last positions; 0 means 1).
+int queries(const kvd_dims* d) { return d->queries_per_seq > 1 ? d->queries_per_seq : 1; }
+
+// Query rows per KV head (queries x group) and the MFMA tiles of up to kMaxGroup rows they fill.
+int64_t query_rows(const kvd_dims* d) {
+    return (int64_t)queries(d) * (d->num_q_heads / d->num_kv_heads);
+}
 int query_tiles(const kvd_dims* d) {
-    const int g = d->num_q_heads / d->num_kv_heads;
-    return (g + kvd::kMaxGroup - 1) / kvd::kMaxGroup;
+    return (int)((query_rows(d) + kvd::kMaxGroup - 1) / kvd::kMaxGroup);
 }
 
 // Compute units of the current device (256 on MI355X when the query fails).
@@ -72,8 +77,8 @@ int choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         if (r > kvd::kMaxRun) r = kvd::kMaxRun;
     }
     if (fmt < KVD_TURBO4) {   // BF16 / FP8 stage the run's triples in LDS
-        const int g = d->num_q_heads / d->num_kv_heads;
-        const int64_t cap = kvd::stage_rows(d->head_dim) / (g < kvd::kMaxGroup ? g : kvd::kMaxGroup);
+        const int64_t rows = query_rows(d);
+        const int64_t cap = kvd::stage_rows(d->head_dim) / (rows < kvd::kMaxGroup ? rows : kvd::kMaxGroup);
         if (r > cap) r = cap;
     }
     if (r > pl.P) r = pl.P;
@@ -97,6 +102,9 @@ int check_dims(const kvd_dims* d, int fmt) {
     if (!(ps == 0 || ps == -1 || (ps > 0 && ps % kvd::kPageTokens == 0))) return KVD_ERR_SHAPE;
     if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return KVD_ERR_SHAPE;   // grid limits
     if (d->partitions_per_wave < 0) return KVD_ERR_SHAPE;
+    if (d->queries_per_seq < 0 || d->queries_per_seq > 65535) return KVD_ERR_SHAPE;
+    if ((int64_t)d->num_seqs * queries(d) > 65535) return KVD_ERR_SHAPE;   // reduce grid rows
+    if ((int64_t)queries(d) > d->max_context_len) return KVD_ERR_SHAPE;   // positions >= 0
     return KVD_OK;
 }
 
@@ -116,7 +124,7 @@ Plan make_plan(const kvd_dims* d) {
         pl.part_size = d->partition_size;
         pl.P = (d->max_context_len + pl.part_size - 1) / pl.part_size;
     }
-    const size_t rows = (size_t)d->num_seqs * d->num_q_heads * pl.P;
+    const size_t rows = (size_t)d->num_seqs * queries(d) * d->num_q_heads * pl.P;
     const size_t ml = round_up(rows * sizeof(float), 256);
     pl.off_l = ml;
     pl.off_o = 2 * ml;
@@ -172,6 +180,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.Hq = d->num_q_heads;
     p.Hkv = d->num_kv_heads;
     p.g = d->num_q_heads / d->num_kv_heads;
+    p.nq = queries(d);
     p.qt = query_tiles(d);
     p.D = d->head_dim;
     p.max_blocks = d->max_blocks_per_seq;

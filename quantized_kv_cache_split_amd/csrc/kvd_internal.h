@@ -44,7 +44,8 @@ struct LaunchParams {
     int64_t k_chunk;          // bytes per (page, KV head), K
     int64_t v_chunk;          // bytes per (page, KV head), V
     int32_t B, Hq, Hkv, g, D;
-    int32_t qt;               // query tiles per KV head: ceil(g / kMaxGroup)
+    int32_t nq;               // queries per sequence (a chunk at the last positions; 1 = decode)
+    int32_t qt;               // query tiles per KV head: ceil(nq * g / kMaxGroup)
     int32_t max_blocks, pool, max_ctx;
     int32_t part_mode;        // PartMode
     int32_t part_size;        // tokens per partition (split sequences)

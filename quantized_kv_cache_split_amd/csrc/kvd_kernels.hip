@@ -38,6 +38,7 @@
 //   (page m/8, slot 8*((m/4)%2) + m%4), tile Y the slot 4 higher; after the QK product lane
 //   (n, j) then holds query n's logits for tokens (page j/2, slots 8*(j%2) + e), e = 0..7,
 //   which is also the k-slot order of group j in the PV product.
+#include <float.h>
 #include <math.h>
 
 #include <type_traits>
@@ -199,20 +200,26 @@ __device__ void fwht_rows(float* buf, int rows, int tid, int nthreads) {
 }
 
 struct SeqInfo {
-    int L, lo;
+    int L, lo, W;
     bool bad, split;
 };
 
-// Attended range [lo, L) of sequence b and whether it is split into partitions.
+// Range [lo, L) of the keys any query of sequence b attends to and whether it is split into
+// partitions.  With a chunk of nq queries (the last nq positions), query i at position
+// L - nq + i sees [max(0, L - nq + i + 1 - W), L - nq + i] under a window W, so the sequence's
+// range starts at query 0's window.  MQ = false: one query per sequence (nq = 1).
+template <bool MQ>
 __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
     SeqInfo s;
+    const int nq = MQ ? p.nq : 1;
     // one value per workgroup: keep it in scalar registers so loops over it stay uniform
     int L = __builtin_amdgcn_readfirstlane(p.ctx[b]);
     const int W = p.win ? __builtin_amdgcn_readfirstlane(p.win[b]) : 0;
-    s.bad = (L < 0) || (L > p.max_ctx) || (W < 0);
+    s.bad = (L < 0) || (L > p.max_ctx) || (W < 0) || (MQ && L > 0 && L < nq);
     if (s.bad) L = 0;
     s.L = L;
-    s.lo = (W > 0 && L > W) ? L - W : 0;
+    s.W = W;
+    s.lo = W > 0 ? max(0, L - nq + 1 - W) : 0;
     const int span = L - s.lo;
     s.split = p.part_mode == kPartFixed ? true
             : (p.part_mode == kPartNever ? false : span >= kAutoSplitMin);
@@ -327,7 +334,7 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
 // partitions.
-template <int FMT, int D, bool CAP, int PF>
+template <int FMT, int D, bool CAP, int PF, bool MQ>
 __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel(const LaunchParams p) {
     constexpr bool kKcb = k_codebook<FMT>();   // rotated query, K table, K norms
     constexpr bool kVcb = v_codebook<FMT>();   // V table, V norms, output in the rotated domain
@@ -378,24 +385,33 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     // handed to the eight XCDs round-robin by linear id, so this order spreads every
     // sequence's work over the XCDs (with 8 KV heads each XCD gets one head of every
     // sequence); x fastest would pile the short sequences' work onto the XCDs of small x.
-    // A query group larger than kMaxGroup is split into p.qt tiles ("virtual heads") of up to
-    // kMaxGroup query heads, each processed like a KV head of its own (its pages are read once
-    // per tile).
+    // The query rows of one KV head are (query i of the chunk, head of the group), i-major:
+    // p.nq * p.g rows (p.g for single-query decode).  More rows than kMaxGroup are split into
+    // p.qt tiles ("virtual heads") of up to kMaxGroup rows, each processed like a KV head of its
+    // own (its pages are read once per tile).
     const int wg = blockIdx.x;
     const int nvh = p.Hkv * p.qt;
     const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = wg / (nvh * p.B);
     const int hk = vh / p.qt, qtile = vh - hk * p.qt;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qbase = hk * p.g + qtile * kMaxGroup;               // first query head of the tile
-    const int g = min(kMaxGroup, p.g - qtile * kMaxGroup);        // query heads in the tile
-    const SeqInfo si = seq_info(p, b);
-    float* out_rows = p.out + ((size_t)b * p.Hq + (size_t)qbase) * D;
+    const int rbase = qtile * kMaxGroup;                          // first row of the tile
+    const int g = min(kMaxGroup, (MQ ? p.nq : 1) * p.g - rbase);  // rows in the tile
+    const SeqInfo si = seq_info<MQ>(p, b);
+    // q / out / workspace row (b, i, h) of tile row t (q and out are [B][nq][Hq][D]): row
+    // rbase + t of the KV head is query i = (rbase + t) / g, head hk * g + (rbase + t) - i * g,
+    // i.e. row0 + t + i * (Hq - g).  MQ = false: one query per sequence (p.nq == 1, i = 0).
+    const size_t row0 = (size_t)b * (MQ ? p.nq : 1) * p.Hq + (size_t)hk * p.g + rbase;
+    auto row_index = [&](int t) -> size_t {
+        if constexpr (!MQ) return row0 + t;
+        const int i = (rbase + t) / p.g;
+        return row0 + t + (size_t)i * (p.Hq - p.g);
+    };
 
     if (si.bad || si.L == 0) {
         if (xb == 0) {
             const float v = si.bad ? __builtin_nanf("") : 0.0f;
-            for (int i = tid; i < g * D; i += kThr) out_rows[i] = v;
+            for (int i = tid; i < g * D; i += kThr) p.out[row_index(i / D) * D + i % D] = v;
         }
         return;
     }
@@ -435,6 +451,16 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
+    // the lane's query: index in the chunk, position, and the keys [row_lo, row_hi) it sees;
+    // the keys every row of the tile sees: [tile_lo, tile_hi) (the unmasked fast path).  One
+    // query per sequence: every row sees the sequence's whole range.
+    const int q_i = MQ ? (rbase + qn) / p.g : 0;
+    const int q_pos = MQ ? si.L - p.nq + q_i : si.L - 1;
+    const int row_hi = MQ ? q_pos + 1 : si.L;
+    const int row_lo = MQ ? (si.W > 0 ? max(0, row_hi - si.W) : 0) : si.lo;
+    const int tile_hi = MQ ? si.L - p.nq + rbase / p.g + 1 : si.L;
+    const int tile_lo = MQ ? (si.W > 0 ? max(0, si.L - p.nq + (rbase + g - 1) / p.g + 1 - si.W) : 0)
+                           : si.lo;
     u32x4 qop[KS];                      // BF16 / FP8 K: q (bf16) for step s
     u32x4 qdup[kKcb ? KS : 1][2];       // codebook K: q hi, each pair repeated
     u32x4 qlo0[kKcb ? KS : 1][2];       // codebook K: q lo pairs interleaved with zeros
@@ -479,7 +505,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         // q_rot = H (s * q): rows of the group in LDS, then the butterfly
         for (int i = tid; i < g * D; i += kThr) {
             const int r = i / D, d = i % D;
-            const uint16_t qb = p.q[((size_t)b * p.Hq + (size_t)qbase + r) * D + d];
+            const uint16_t qb = p.q[row_index(r) * D + d];
             lds.row[i] = bf16_bits_to_f32(qb) * p.sign[d];
         }
         __syncthreads();
@@ -511,11 +537,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         }
         zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
     } else {
-        const uint16_t* qrow = p.q + ((size_t)b * p.Hq + (size_t)qbase + qn) * D;
+        const uint16_t* qptr = p.q + row_index(qn) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const int d0 = (FMT == KVD_BF16) ? 32 * s + 8 * j : 64 * (s / 2) + 16 * j + 8 * (s % 2);
-            const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(qptr + d0);
             qop[s] = qlive ? w : u32x4{0u, 0u, 0u, 0u};
         }
         zscale = p.softmax_scale * kLog2e;
@@ -530,7 +556,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     const float inv_cap_l2 = CAP ? 1.0f / cap_l2 : 0.0f;
     // ALiBi slope of this lane's query head, in base-2 units (0 without ALiBi)
     const bool alibi = p.alibi != nullptr;
-    const float slope_l2 = alibi ? p.alibi[qbase + qn] * kLog2e : 0.0f;
+    const float slope_l2 = alibi ? p.alibi[hk * p.g + (rbase + qn - q_i * p.g)] * kLog2e : 0.0f;
 
     // ---- state -------------------------------------------------------------------------
     f32x4 oacc[VT];
@@ -573,7 +599,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         const int pgA = pg0 + 2 * min(k, npairs - 1);
         const bool hasB = pgA + 1 < pg1;
         const int hi_k = k < npairs ? hi : lo;
-        const bool full = (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
+        const bool full = MQ ? (pgA * kPageTokens >= max(lo, tile_lo)) && hasB &&
+                                   ((pgA + 2) * kPageTokens <= min(hi_k, tile_hi))
+                             : (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
 
         f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
         f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
@@ -631,9 +659,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 z[e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
             }
         }
-        if (alibi) {   // + slope * (j - (L - 1)) for the lane's tokens j = tok0 .. tok0 + 7
+        if (alibi) {   // + slope * (j - q_pos) for the lane's tokens j = tok0 .. tok0 + 7
             const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
-            const float base = slope_l2 * (float)(tok0 - (si.L - 1));
+            const float base = slope_l2 * (float)(tok0 - q_pos);
 #pragma unroll
             for (int e = 0; e < 8; ++e) z[e] += base + slope_l2 * (float)e;
         }
@@ -643,8 +671,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             for (int e = 0; e < 4; ++e) { vn[e] = r.vn0[e]; vn[4 + e] = r.vn1[e]; }
         }
         // Tokens outside [lo, hi) (and a missing second page) are selected out, never
-        // multiplied: their logits become -inf and their V values zero.  Only the first and
-        // last pair of a range can be partial; the test is uniform over the wave.
+        // multiplied: their logits become -inf and their V values zero.  A query of a chunk
+        // also drops the keys outside its own causal window (logits only: those tokens hold
+        // real data).  Only pairs at the ends of a range can be partial; the test is uniform
+        // over the wave.
         if (!full) {
             const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
             uint32_t vmask = 0;
@@ -653,7 +683,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 const int t = tok0 + e;
                 const bool ok = (t >= lo) && (t < hi_k) && (ln.v_sel == 0 || hasB);
                 vmask |= (ok ? 1u : 0u) << e;
-                z[e] = ok ? z[e] : -INFINITY;
+                z[e] = (ok && (!MQ || (t >= row_lo && t < row_hi))) ? z[e] : -INFINITY;
             }
             if constexpr (kVcb) {
                 // table levels are always finite, so zero norms (possibly NaN in unused slots)
@@ -700,9 +730,13 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             vloc = max_over_groups(vloc);
             grow = grow || (vloc > sig_run * kLazySig);
         }
+        // (chunks of queries: maxima are clamped to -FLT_MAX where they enter a difference: a
+        // query row that has not seen a key yet keeps m = -inf, and -inf - -inf would be NaN;
+        // with one query per sequence every computed pair holds a key of the range)
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float m_new = fmaxf(m_run, mloc);
-            float f = fast_exp2(m_run - m_new);
+            float f = MQ ? fast_exp2(fmaxf(m_run, -FLT_MAX) - fmaxf(m_new, -FLT_MAX))
+                         : fast_exp2(m_run - m_new);
             l_run *= f;
             if constexpr (kVcb) {
                 const float sig_new = fmaxf(sig_run, vloc);
@@ -715,8 +749,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             m_run = m_new;
         }
         float pe[8], psum = 0.0f;
+        const float m_ref = MQ ? fmaxf(m_run, -FLT_MAX) : m_run;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_run); psum += pe[e]; }
+        for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_ref); psum += pe[e]; }
         l_run += psum;
 
         if constexpr (kVcb) {
@@ -763,8 +798,6 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         }
     };
 
-    const size_t row0 = (size_t)b * p.Hq + (size_t)qbase;
-
     // ---- split sequences: close a partition after its last pair ------------------------
     // Writes the partition's triple (m = the exact max logit in base-2 units, l = the sum
     // taken relative to it, o = O / l in output units, which no reference choice affects) and
@@ -777,11 +810,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             float lt = l_run + __shfl_xor(l_run, 16);
             lt += __shfl_xor(lt, 32);
             const float osc = kVcb ? oscale * sig_run : oscale;
-            const float sc = bad_ids ? __builtin_nanf("") : osc / lt;
-            const float lx = lt * fast_exp2(m_run - m_true);   // the sum relative to the exact max
+            // a query row that saw no key of this partition: m = -inf, l = 0, o = 0
+            const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
+            const float lx = lt > 0.0f ? lt * fast_exp2(m_run - m_true) : 0.0f;   // relative to the exact max
             if constexpr (kVcb) {
                 if (qlive) {
-                    const size_t slot = (row0 + n) * p.P + part;
+                    const size_t slot = row_index(n) * p.P + part;
 #pragma unroll
                     for (int t = 0; t < VT; ++t)
                         *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
@@ -868,13 +902,13 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         for (int i = lane; i < nrows * C; i += 64) {
             const int row = i / C, c = i % C;
             const int r = row / g, qn_ = row - r * g;
-            const size_t slot = (row0 + qn_) * p.P + part_first + r;
+            const size_t slot = row_index(qn_) * p.P + part_first + r;
             *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 4 * c) =
                 *reinterpret_cast<const f32x4*>(&sm_o[wave][row * SD + 4 * c]);
         }
         for (int row = lane; row < nrows; row += 64) {
             const int r = row / g, qn_ = row - r * g;
-            const size_t slot = (row0 + qn_) * p.P + part_first + r;
+            const size_t slot = row_index(qn_) * p.P + part_first + r;
             p.ws_m[slot] = sm_m[wave][row];
             p.ws_l[slot] = sm_l[wave][row];
         }
@@ -913,20 +947,22 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         float o = acc / wsum;
         if (wg_bad) o = __builtin_nanf("");
         if constexpr (kVcb) lds.row[i] = o;
-        else out_rows[i] = o;
+        else p.out[row_index(r) * D + d] = o;
     }
     if constexpr (kVcb) {   // inverse rotation of the final rows: diag(s) H o / sqrt(D)
         __syncthreads();
         fwht_rows<D>(lds.row, g, tid, kThr);
         const float rs = 1.0f / sqrtf((float)D);
-        for (int i = tid; i < g * D; i += kThr) out_rows[i] = lds.row[i] * p.sign[i % D] * rs;
+        for (int i = tid; i < g * D; i += kThr)
+            p.out[row_index(i / D) * D + i % D] = lds.row[i] * p.sign[i % D] * rs;
     }
 }
 
 // ------------------------------------------------------------------------------------------
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
-// One wave per (query head, sequence); lane l owns output elements E*l .. E*l + E - 1
+// One wave per (query head, sequence x query of the chunk); lane l owns output elements
+// E*l .. E*l + E - 1
 // (E = D / 64).  Partitions are taken 64 at a time: each lane loads the (m, l) of one of them
 // and then every lane loads its slice of all 64 partition outputs, so a block costs one memory
 // round trip.  The block's weights are computed lane-parallel and broadcast with v_readlane;
@@ -936,12 +972,12 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     constexpr bool kVcb = v_codebook<FMT>();   // partial outputs are in the rotated domain
     constexpr int E = D / 64;
     constexpr int kBlock = 64;
-    const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-    const SeqInfo si = seq_info(p, b);
+    const int hq = blockIdx.x, bi = blockIdx.y, b = bi / p.nq, lane = threadIdx.x;
+    const SeqInfo si = seq_info<true>(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
     const int p0 = si.lo / p.part_size, p1 = (si.L - 1) / p.part_size;
     const int n = p1 - p0 + 1;
-    const size_t row = (size_t)b * p.Hq + hq;
+    const size_t row = (size_t)bi * p.Hq + hq;   // out / workspace row (b, query, head)
     const float* ms = p.ws_m + row * p.P + p0;
     const float* ls = p.ws_l + row * p.P + p0;
     const float* os = p.ws_o + (row * p.P + p0) * D + E * lane;
@@ -967,8 +1003,10 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o));
         const float Mn = fmaxf(M, mb);
-        const float sc = fast_exp2(M - Mn);   // 0 on the first block (M = -inf)
-        const float w = in ? lq * fast_exp2(mq - Mn) : 0.0f;
+        // 0 on the first block (M = -inf); the clamp keeps a block in which this query row
+        // has no key yet (m = -inf everywhere) from producing -inf - -inf
+        const float sc = fast_exp2(fmaxf(M, -FLT_MAX) - fmaxf(Mn, -FLT_MAX));
+        const float w = (in && lq > 0.0f) ? lq * fast_exp2(mq - Mn) : 0.0f;   // l = 0: no key
         wsum = wsum * sc + w;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] *= sc;
@@ -1073,12 +1111,15 @@ template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
     constexpr int PF = prefetch_depth<FMT>();
     const dim3 block(64 * waves_per_group(FMT));
-    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF>, grid, block, s, p)
-                            : launch_kernel(partition_kernel<FMT, D, false, PF>, grid, block, s, p);
+    if (p.nq > 1)
+        return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true>, grid, block, s, p)
+                                : launch_kernel(partition_kernel<FMT, D, false, PF, true>, grid, block, s, p);
+    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, false>, grid, block, s, p)
+                            : launch_kernel(partition_kernel<FMT, D, false, PF, false>, grid, block, s, p);
 }
 template <int FMT, int D>
 hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
-    return launch_kernel(reduce_kernel<FMT, D>, dim3(p.Hq, p.B), dim3(64), s, p);
+    return launch_kernel(reduce_kernel<FMT, D>, dim3(p.Hq, p.B * p.nq), dim3(64), s, p);
 }
 
 }  // namespace

@@ -25,8 +25,8 @@ class GpuBatch:
         self.alibi = None if alibi is None else torch.from_numpy(
             np.asarray(alibi, dtype=np.float32)).to(device)
         s = inp.spec
-        self.out = torch.full((s.num_seqs, s.num_q_heads, s.head_dim), float("nan"),
-                              dtype=torch.float32, device=device)
+        self.out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32,
+                              device=device)
         nbytes = kvd.workspace_bytes(self.dims)
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         if nbytes:
@@ -51,17 +51,19 @@ class GpuBatch:
         torch.cuda.synchronize()
 
     def partials(self):
-        """Workspace triples (m, l, o) as numpy arrays [B, Hq, P], [B, Hq, P], [B, Hq, P, D]."""
+        """Workspace triples (m, l, o) as numpy arrays [B, Hq, P], [B, Hq, P], [B, Hq, P, D]
+        (with a chunk of n_q queries: [B, n_q, Hq, P] ...)."""
         s = self.inp.spec
-        B, Hq, D = s.num_seqs, s.num_q_heads, s.head_dim
+        B, Hq, D, nq = s.num_seqs, s.num_q_heads, s.head_dim, s.queries_per_seq
         ps = self.dims.partition_size or 512     # partitions as the header defines them
         P = -(-self.dims.max_context_len // ps)
-        rows = B * Hq * P
+        lead = (B, Hq) if nq == 1 else (B, nq, Hq)
+        rows = B * nq * Hq * P
         ml = -(-rows * 4 // 256) * 256
         ws = self.ws.cpu().numpy()
-        m = ws[:rows * 4].view(np.float32).reshape(B, Hq, P)
-        l = ws[ml:ml + rows * 4].view(np.float32).reshape(B, Hq, P)
-        o = ws[2 * ml:2 * ml + rows * D * 4].view(np.float32).reshape(B, Hq, P, D)
+        m = ws[:rows * 4].view(np.float32).reshape(*lead, P)
+        l = ws[ml:ml + rows * 4].view(np.float32).reshape(*lead, P)
+        o = ws[2 * ml:2 * ml + rows * D * 4].view(np.float32).reshape(*lead, P, D)
         return m, l, o
 
 

@@ -1,0 +1,141 @@
+"""GPU parity of multi-query (chunked-prefill) decode: a chunk of n_q queries per sequence at
+its last positions, each attending causally (its own window and ALiBi position), through the
+C ABI against the oracle (oracle/multiquery.py).  Same bar as single-query decode: max abs error
+<= 2e-3 and row-normwise relative error <= 1e-2; bit-identity where the arithmetic is fixed."""
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+from conftest import oracle_args
+from gpu_harness import GpuBatch, assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _mq(fmt, n_q, **kw):
+    base = dict(fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2, pool_total=None,
+                queries_per_seq=n_q)
+    base.update(kw)
+    return kvgen.make_inputs(kvgen.spec("c1", **base))
+
+
+def _oracle(inp, alibi=None):
+    return oracle.multi_query_attention(*oracle_args(inp), alibi=alibi)
+
+
+def _slopes(h, base=8.0):
+    return (2.0 ** (-base * (np.arange(h) + 1) / h)).astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("n_q,L", [(2, 2), (4, 17), (4, 300), (5, 1030), (16, 1500), (3, 4000)])
+def test_multi_query_lengths(fmt, n_q, L):
+    inp = _mq(fmt, n_q, context=L, num_seqs=2, seed=L + n_q)
+    gpu = GpuBatch(inp).run()
+    assert gpu.shape == inp.q.shape
+    assert_close(gpu, _oracle(inp), f"{fmt} n_q={n_q} L={L}")
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+@pytest.mark.parametrize("hq,hkv,n_q", [(4, 1, 4), (32, 8, 4), (8, 1, 8), (2, 2, 7), (64, 8, 3)])
+def test_multi_query_groups(fmt, hq, hkv, n_q):
+    """Rows per KV head n_q * g from 4 to 64 (one to four tiles of 16, ragged last tile)."""
+    inp = _mq(fmt, n_q, num_q_heads=hq, num_kv_heads=hkv, context=None, ctx_range=(n_q, 2600),
+              num_seqs=3)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} hq={hq} hkv={hkv} n_q={n_q}")
+
+
+@pytest.mark.parametrize("ps", [0, 128, -1, 32])
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_multi_query_window_alibi_cap(fmt, ps):
+    """Ragged lengths, windows on half the sequences (each query its own window), ALiBi from
+    each query's position, softcap (BF16), pages before the windows poisoned."""
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=6, num_q_heads=8, num_kv_heads=2,
+                                       ctx_range=(16, 3000), window=700, queries_per_seq=6,
+                                       softcap=50.0 if fmt == "bf16" else 0.0),
+                            poison_before_window=True)
+    sl = _slopes(8)
+    gpu = GpuBatch(inp, partition_size=ps, alibi=sl).run()
+    assert_close(gpu, _oracle(inp, sl), f"{fmt} mq window alibi ps={ps}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
+def test_multi_query_runs_bit_identical(fmt):
+    """Partitions per wave change the launch, not the bits (every query row restarts exactly)."""
+    lengths, windows = [5000, 1100, 2600, 40], [1100, 0, 333, 0]
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+                                       softcap=0.0, queries_per_seq=4),
+                            lengths=lengths, windows=windows, poison_before_window=True)
+    ref = _oracle(inp)
+    outs = {}
+    for run in (1, 2, 3):
+        outs[run] = GpuBatch(inp, partition_size=128, partitions_per_wave=run).run()
+        assert_close(outs[run], ref, f"{fmt} mq run={run}")
+    for run in (2, 3):
+        assert (outs[run].view(np.uint64) == outs[1].view(np.uint64)).all(), run
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "turbo4"])
+def test_multi_query_partials(fmt):
+    """Partition triples per (query, head) row, including rows that see no key of a partition
+    (a small window against 32-token partitions): m = -inf, l = 0, o = 0 there."""
+    # lengths 32k + 3 and 32k + 4: the last partition holds only the chunk's last 3 / 4 tokens,
+    # which its first queries do not see; window 40 also empties the first partition for some
+    inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2,
+                                       pool_total=None, queries_per_seq=8, num_seqs=2),
+                            lengths=[355, 612], windows=[40, 40])
+    gb = GpuBatch(inp, partition_size=32)
+    gb.run_phase1()
+    m, l, o = gb.partials()          # [B, n_q, Hq, P]
+    s = inp.spec
+    g = s.group
+    empty = 0
+    for b in range(s.num_seqs):
+        for hk in range(s.num_kv_heads):
+            for lo_, hi_, pm, pl, po in oracle.multi_query_partials(*oracle_args(inp), 32, b, hk,
+                                                                    rotated=True):
+                p = lo_ // 32
+                gm = m[b, :, hk * g:(hk + 1) * g, p].reshape(-1).astype(np.float64)
+                gl = l[b, :, hk * g:(hk + 1) * g, p].reshape(-1).astype(np.float64)
+                go = o[b, :, hk * g:(hk + 1) * g, p].reshape(-1, s.head_dim).astype(np.float64)
+                none = pl == 0
+                empty += int(none.sum())
+                assert (np.isneginf(gm[none])).all() and (gl[none] == 0).all() and (go[none] == 0).all()
+                lse = gm[~none] * np.log(2.0) + np.log(gl[~none])
+                assert np.abs(lse - (pm[~none] + np.log(pl[~none]))).max() < 5e-3
+                assert_close(go[~none], po[~none], f"{fmt} mq partial b{b} p{p}")
+    assert empty > 0
+
+
+def test_multi_query_zero_and_short_rows():
+    """L = 0: zero rows; 0 < L < n_q: NaN rows (no position exists for the first queries); the
+    sequence next to them matches the oracle."""
+    inp = _mq("fp8", 4, num_seqs=3, context=None, ctx_range=(4, 50))
+    inp.context_lens[:] = [0, 3, 50]
+    gpu = GpuBatch(inp).run()
+    assert (gpu[0] == 0).all()
+    assert np.isnan(gpu[1]).all()
+    ok = inp.context_lens.copy()
+    ok[1] = 4                      # the oracle's domain; sequences are independent
+    import dataclasses
+    ref = oracle.multi_query_attention(*oracle_args(dataclasses.replace(inp, context_lens=ok)),
+                                       seqs=[2])
+    assert_close(gpu[2:3], ref[2:3], "fp8 mq next to short rows")
+
+
+def test_one_query_chunk_equals_decode_bits():
+    """queries_per_seq = 1 runs the single-query kernels: bit-identical to leaving it 0."""
+    inp = _mq("turbo4", 1, context=None, ctx_range=(1, 3000), num_seqs=3)
+    a = GpuBatch(inp).run()
+    gb = GpuBatch(inp)
+    gb.dims.queries_per_seq = 0
+    b = gb.run()
+    assert (a.view(np.uint64) == b.view(np.uint64)).all()
