@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c4",
-                    help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 m-bf16 m-t4 m-t3 m-t8 (see kvgen.SPECS)")
+                    help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 m-bf16 m-t4 m-t3 m-t8 mq-fp8 mq-t4 mq-t3 "
+                         "(see kvgen.SPECS)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--partitions-per-wave", type=int, default=0,
                     help="launch tuning of the partition kernel (0 = the library's choice)")
@@ -73,11 +74,11 @@ def cpu_baseline(inp, seconds):
     pairs = 0
     t0 = time.perf_counter()
     order = [(b, hk) for b in range(s.num_seqs) for hk in range(s.num_kv_heads)]
+    fn = oracle.decode_attention if s.queries_per_seq == 1 else oracle.multi_query_attention
     for b, hk in order:
-        oracle.decode_attention(inp.q, inp.k_cache, inp.v_cache, inp.block_table,
-                                inp.context_lens, s.fmt, inp.scales, inp.codebook, inp.sign,
-                                inp.softmax_scale, inp.window, inp.softcap, s.num_kv_heads,
-                                s.head_dim, seqs=[b], kv_heads=[hk])
+        fn(inp.q, inp.k_cache, inp.v_cache, inp.block_table, inp.context_lens, s.fmt, inp.scales,
+           inp.codebook, inp.sign, inp.softmax_scale, inp.window, inp.softcap, s.num_kv_heads,
+           s.head_dim, seqs=[b], kv_heads=[hk])
         done_bytes += int(spans[b]) * per_pair
         pairs += 1
         if time.perf_counter() - t0 >= seconds:
@@ -225,8 +226,7 @@ def main():
     t = to_torch(inp, dev)
     ps = args.partition_size if args.partition_size is not None else spec.partition_size
     dims = kvd.Dims(**dims_kwargs(inp, ps, args.partitions_per_wave))
-    out = torch.empty((spec.num_seqs, spec.num_q_heads, spec.head_dim), dtype=torch.float32,
-                      device=dev)
+    out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=dev)   # [B, (n_q,) Hq, D]
     nws = kvd.workspace_bytes(dims)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) if nws else None
     flush = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)
@@ -293,11 +293,12 @@ def main():
             "window": spec.window, "softcap": spec.softcap,
             "kv_format": KV_NAMES[spec.fmt], "block_size": 16,
             "partition_size": ps if ps else 512, "kv_bytes_per_step": kv_bytes,
+            "queries_per_seq": spec.queries_per_seq,
             "mfma_operands": "bf16 for BF16/FP8 K and V, fp16 for codebook K and V (Turbo8: "
                              "bf16 QK, fp16 PV); fp32 accumulate",
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "decode_tokens_per_s": round(spec.num_seqs / mean_call, 1),
+        "decode_tokens_per_s": round(spec.num_seqs * spec.queries_per_seq / mean_call, 1),
         "ms_per_step_p10_p50_p90": [round(float(np.percentile(t_call, q)) * 1e3, 4) for q in (10, 50, 90)],
         "partition_kernel_ms": round(float(t_part.mean()) * 1e3, 4),
         "reduce_kernel_ms": round(float((t_call - t_part).mean()) * 1e3, 4),

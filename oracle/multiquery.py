@@ -39,9 +39,10 @@ def row_range(L: int, n_q: int, i: int, W: int) -> tuple[int, int]:
 
 def multi_query_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
                           sign, softmax_scale, window, softcap, num_kv_heads, head_dim,
-                          alibi=None, seqs=None):
+                          alibi=None, seqs=None, kv_heads=None):
     """out[b, i, h] for q bf16 bits [B, n_q, Hq, D]: query i is the decode query of the context
-    prefix that ends at its own position (fp64 [B, n_q, Hq, D])."""
+    prefix that ends at its own position (fp64 [B, n_q, Hq, D]; ``seqs`` / ``kv_heads`` restrict
+    the work to a sample, other rows are NaN)."""
     q = np.asarray(q)
     B, n_q, Hq, D = q.shape
     L = np.asarray(context_lens).astype(np.int64)
@@ -51,7 +52,8 @@ def multi_query_attention(q, k_cache, v_cache, block_table, context_lens, fmt, s
         ctx_i = np.where(L > 0, L - n_q + i + 1, 0)
         out[:, i] = decode_attention(q[:, i], k_cache, v_cache, block_table, ctx_i, fmt, scales,
                                      codebook, sign, softmax_scale, window, softcap,
-                                     num_kv_heads, head_dim, seqs=seqs, alibi=alibi)
+                                     num_kv_heads, head_dim, seqs=seqs, kv_heads=kv_heads,
+                                     alibi=alibi)
     return out
 
 
