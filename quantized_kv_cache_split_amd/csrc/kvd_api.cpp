@@ -307,7 +307,10 @@ int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v
         (scales && !aligned(scales, 4)) || (codebook && !aligned(codebook, 4)) ||
         (sign_pattern && !aligned(sign_pattern, 4)))
         return KVD_ERR_ALIGN;
-    if ((int64_t)d->num_seqs * n_new * d->num_kv_heads > ((int64_t)1 << 33)) return KVD_ERR_SHAPE;
+    // one workgroup per (sequence, page slot, KV head); T new tokens touch at most
+    // ceil(T / 16) + 1 pages of a sequence
+    const int64_t ps = ((int64_t)n_new + kvd::kPageTokens - 1) / kvd::kPageTokens + 1;
+    if ((int64_t)d->num_seqs * ps * d->num_kv_heads > 0x7FFFFFFFLL) return KVD_ERR_SHAPE;
     if (d->num_seqs == 0 || n_new == 0) return KVD_OK;
     kvd::AppendParams p{};
     p.k_new = k_new;
@@ -329,6 +332,7 @@ int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v
     p.max_blocks = d->max_blocks_per_seq;
     p.pool = d->num_pool_blocks;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    p.ps = (int32_t)ps;
     return kvd::launch_append(p, static_cast<hipStream_t>(stream)) == hipSuccess ? KVD_OK
                                                                                 : KVD_ERR_HIP;
 }

@@ -80,6 +80,7 @@ struct AppendParams {
     const float* sign;        // codebook formats: [D]
     int64_t k_chunk, v_chunk;
     int32_t fmt, B, T, Hkv, D, max_blocks, pool, kbits;
+    int32_t ps;               // page slots per sequence: pages one sequence's T new tokens touch, at most
 };
 
 // Launches `kernel` (which takes one parameter struct by value) and returns the status of this
