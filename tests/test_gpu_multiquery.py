@@ -139,3 +139,42 @@ def test_one_query_chunk_equals_decode_bits():
     gb.dims.queries_per_seq = 0
     b = gb.run()
     assert (a.view(np.uint64) == b.view(np.uint64)).all()
+
+
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_chunked_prefill_step(fmt):
+    """One chunked-prefill step end to end: append a chunk of 24 tokens per sequence to the cache
+    (kvd_append_kv), then attend with those 24 queries (queries_per_seq = 24) -- against the
+    oracle's cache writer followed by its multi-query attention."""
+    import dataclasses
+    import torch
+    import quantized_kv_cache_split_amd as kvd
+    from kvgen.torch_io import dims_kwargs, to_torch
+    from oracle import encode as enc
+
+    n_q, old = 24, [40, 1100, 7]
+    s = kvgen.spec("c1", fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2, pool_total=None,
+                   num_seqs=3, queries_per_seq=n_q, seed=21)
+    inp = kvgen.make_inputs(s, lengths=[L + n_q for L in old])
+    rng = np.random.default_rng(22)
+    kn = rng.standard_normal((3, n_q, 2, 128)).astype(np.float32)
+    vn = rng.standard_normal((3, n_q, 2, 128)).astype(np.float32)
+    pos = np.array(old, dtype=np.int32)
+    t = to_torch(inp, "cuda:0")
+    dims = kvd.Dims(**dims_kwargs(inp, 0))
+    kvd.append_kv(dims, fmt, torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                  t["block_table"], torch.from_numpy(pos).cuda(), n_q, t["k_cache"], t["v_cache"],
+                  t["scales"], t["codebook"], t["sign_pattern"])
+    out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda:0")
+    nws = kvd.workspace_bytes(dims)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda:0")
+    kvd.decode_attn_paged(dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"],
+                          t["context_lens"], fmt, t["scales"], t["codebook"], t["sign_pattern"],
+                          float(inp.softmax_scale), t["window"], float(inp.softcap), out,
+                          ws if nws else None)
+    torch.cuda.synchronize()
+    kc, vc, sc = enc.append_tokens(fmt, kn, vn, inp.block_table, pos, inp.k_cache, inp.v_cache,
+                                   inp.scales, inp.codebook, inp.sign)
+    ref = oracle.multi_query_attention(*oracle_args(dataclasses.replace(
+        inp, k_cache=kc, v_cache=vc, scales=sc)))
+    assert_close(out.double().cpu().numpy(), ref, f"{fmt} chunked prefill step")
