@@ -87,7 +87,9 @@ def cpu_baseline(inp, seconds):
     return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{pairs} of {len(order)} (sequence, KV head) pairs, {done_bytes / 1e6:.1f} MB "
-                      f"of KV in {dt:.1f} s (NumPy fp64 oracle, host cores {os.cpu_count()})"}
+                      f"of KV in {dt:.1f} s (NumPy fp64 oracle; host cores {os.cpu_count()}, "
+                      f"{len(os.sched_getaffinity(0))} in this process's affinity, BLAS threads "
+                      f"{threads})"}
 
 
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_kv_cache_split_amd", "csrc", f)
