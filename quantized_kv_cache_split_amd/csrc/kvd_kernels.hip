@@ -1,33 +1,39 @@
-// HIP kernels for single-query decode attention over a paged KV cache on gfx950 (MI355X).
+// HIP kernels for decode attention over a paged KV cache on gfx950 (MI355X): one query per
+// sequence, or a chunk of queries at a sequence's last positions (multi-token decode / chunked
+// prefill over the same cache).
 //
 // Two phases, as in turboquant-rs 0.4.1 src/cache/cuda/attention.rs ("partitioned attention +
 // reduce"; 512-token partitions; fp32 per-partition max, sum and output) and the attention.rs
 // README (Split-K decode for every cache format from 1024 tokens on, one shared float reduce):
 //
-//   partition_kernel<FMT, D, CAP>  one workgroup (4 waves) per (partition, KV head, sequence).
-//       Each wave walks pairs of 16-token pages, software-pipelined: while it computes pair k
-//       its loads for pair k+4 (the wave's next pair) are in flight, and the block-table
-//       entries of the pair after that are being fetched with scalar loads.  Per pair it
+//   partition_kernel<FMT, D, CAP, PF, MQ>  a 1-D grid of workgroups (4 waves for BF16 / FP8,
+//       8 for the codebook formats) over (partition slot, sequence, KV head x query tile).
+//       For a split sequence each wave walks a run of consecutive partitions of one (sequence,
+//       KV head, query tile) and writes every partition's (m, l, o) triple; an unsplit
+//       sequence's pages are shared by the workgroup's waves, which merge through LDS.  A wave
+//       walks pairs of 16-token pages, software-pipelined: PF pairs' loads are in flight while
+//       it computes, and the block-table entries ahead of them come in with scalar loads.  Per
+//       pair it
 //         - loads K and V of both pages straight into MFMA operand registers (16-byte loads
 //           for K; V rows are 32/16/8 bytes per 16-token row depending on the format);
-//         - computes S^T = K Q^T for 32 tokens x 16 query slots (the GQA group, zero padded)
-//           with v_mfma_f32_16x16x32_{bf16,f16}, dequantising in registers on the way: FP8 ->
-//           bf16 is exact; codebook levels come from a 16-entry LDS table;
-//         - runs an fp32 online softmax in the base-2 domain (the per-query max crosses the
-//           four 16-lane groups with two shuffles);
+//         - computes S^T = K Q^T for 32 tokens x 16 query rows (the GQA group -- or, with a
+//           chunk of queries, (query, head) pairs -- zero padded) with
+//           v_mfma_f32_16x16x32_{bf16,f16}, dequantising in registers on the way: FP8 -> bf16
+//           is exact; codebook levels come from conflict-free pair tables in LDS;
+//         - runs an fp32 online softmax in the base-2 domain (the per-row max crosses the four
+//           16-lane groups with two permlane swaps; the reference max moves lazily);
 //         - accumulates O^T += V^T P^T with the same MFMA shape.
-//       Operand precision: BF16 and FP8 caches use exact bf16 K/V/q operands and feed P as a
-//       bf16 hi + lo pair (2^-16 relative).  The codebook caches keep the levels and the
-//       rotated query as fp16 hi + lo pairs (about 2^-20 relative; the level error would
-//       otherwise be systematic) and round P once to fp16 (2^-12, random), with power-of-two
-//       scalings that keep every fp16 value in range.
-//       The MFMA output layout of S^T (lane = query, 4 lane groups x 4 rows = 16 tokens) is
+//       Operand precision: BF16 and FP8 K/V (and Turbo8 K) use exact bf16 operands and feed P
+//       as a bf16 hi + lo pair (2^-16 relative).  Codebook levels and the rotated query are
+//       fp16 hi + lo pairs (about 2^-20 relative; plain fp16 levels or query would add a
+//       logit error that large logits turn into a visible output error) and P is rounded once
+//       to fp16 (2^-12, random), with power-of-two scalings that keep every fp16 value in
+//       range.
+//       The MFMA output layout of S^T (lane = query row, 4 lane groups x 4 rows = 16 tokens) is
 //       exactly the B-operand layout of P^T for the PV product once the pair's two pages are
 //       interleaved as below, so no data moves between the two products.
-//       The four waves merge their (max, sum, output) through LDS; the workgroup writes its
-//       partition triple to the workspace, or the final row when the sequence is not split.
-//   reduce_kernel<FMT, D>    one workgroup per (query head, sequence): LSE merge of the
-//       partition triples, then (codebook formats) the inverse rotation diag(s) H / sqrt(D).
+//   reduce_kernel<FMT, D>    one wave per (query head, sequence x query of the chunk): LSE
+//       merge of the partition triples, then (codebook V) the inverse rotation diag(s) H / sqrt(D).
 //   gather_kernel            test export: dequantised values through the block table with the
 //       same page addressing, index unpacking and FP8 decode as the attention kernel.
 //
