@@ -1,0 +1,92 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py times (automatic
+partitions and partitions-per-wave, phase 1 then phase 2), on sampled outputs: every output row
+of a few seeded (sequence, KV head) pairs is compared with the oracle, which computes just those
+pairs.  Same bar as the small cases: max abs <= 2e-3, row-normwise relative <= 1e-2.
+
+The ragged configuration samples a windowed and an unwindowed sequence and its shortest and
+longest ones; the others sample sequences and KV heads by a seeded draw.
+"""
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+from conftest import oracle_args
+from gpu_harness import assert_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _bench_like_run(inp):
+    """The two calls bench.py times, with its dims (automatic partitioning and runs)."""
+    import torch
+    import quantized_kv_cache_split_amd as kvd
+    from kvgen.torch_io import dims_kwargs, to_torch
+
+    t = to_torch(inp, "cuda:0")
+    dims = kvd.Dims(**dims_kwargs(inp, inp.spec.partition_size, 0))
+    out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda:0")
+    nws = kvd.workspace_bytes(dims)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda:0") if nws else None
+    args = (dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
+            inp.spec.fmt, t["scales"], t["codebook"], t["sign_pattern"], float(inp.softmax_scale),
+            t["window"], float(inp.softcap), out, ws)
+    kvd.decode_partitions(*args)
+    kvd.reduce_partitions(*args)
+    torch.cuda.synchronize()
+    res = out.double().cpu().numpy()
+    del t, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def _pairs(inp, n_seq, n_head, seed):
+    s = inp.spec
+    r = np.random.default_rng(seed)
+    seqs = r.choice(s.num_seqs, size=min(n_seq, s.num_seqs), replace=False)
+    heads = r.choice(s.num_kv_heads, size=min(n_head, s.num_kv_heads), replace=False)
+    return [(int(b), int(h)) for b in seqs for h in heads]
+
+
+def _check(inp, gpu, pairs, what):
+    s = inp.spec
+    g = s.group
+    mq = s.queries_per_seq > 1
+    fn = oracle.multi_query_attention if mq else oracle.decode_attention
+    for b, hk in pairs:
+        ref = fn(*oracle_args(inp), seqs=[b], kv_heads=[hk])
+        rows = slice(hk * g, (hk + 1) * g)
+        if mq:
+            assert_close(gpu[b, :, rows], ref[b, :, rows], f"{what} seq {b} kv head {hk}")
+        else:
+            assert_close(gpu[b, rows], ref[b, rows], f"{what} seq {b} kv head {hk}")
+
+
+@pytest.mark.parametrize("name", ["c4", "m-bf16", "m-t4", "m-t3", "m-t8", "c2", "c5-t4", "c5-t3",
+                                  "c5-t8", "mq-fp8", "mq-t4"])
+def test_full_size_sampled(name):
+    inp = kvgen.make_inputs(kvgen.SPECS[name])
+    gpu = _bench_like_run(inp)
+    assert np.isfinite(gpu).all()
+    _check(inp, gpu, _pairs(inp, 2, 2, seed=len(name)), name)
+
+
+def test_full_size_ragged_window_cap():
+    """The ragged batch: lengths U{1..32768}, window 4096 on half the sequences, cap 50."""
+    inp = kvgen.make_inputs(kvgen.SPECS["c3"])
+    gpu = _bench_like_run(inp)
+    assert np.isfinite(gpu).all()
+    L, W = inp.context_lens, inp.window
+    win = np.flatnonzero(W > 0)
+    nowin = np.flatnonzero(W == 0)
+    picks = {int(win[np.argmax(L[win])]), int(nowin[np.argmax(L[nowin])]),
+             int(np.argmin(L)), int(np.argsort(L)[len(L) // 2])}
+    pairs = [(b, hk) for b in sorted(picks) for hk in (0, inp.spec.num_kv_heads - 1)]
+    _check(inp, gpu, pairs, "c3")
