@@ -90,3 +90,13 @@ def test_full_size_ragged_window_cap():
              int(np.argmin(L)), int(np.argsort(L)[len(L) // 2])}
     pairs = [(b, hk) for b in sorted(picks) for hk in (0, inp.spec.num_kv_heads - 1)]
     _check(inp, gpu, pairs, "c3")
+
+
+@pytest.mark.parametrize("fmt,L", [("fp8", 1 << 20), ("turbo4", 1 << 18), ("bf16", 3 * (1 << 17) + 5)])
+def test_very_long_context(fmt, L):
+    """One sequence far longer than the configs: 512 to 2048 partitions, i.e. up to 32 blocks of
+    64 partitions in the reduce, and a ragged last page -- against the oracle on every row."""
+    inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt, num_seqs=1, num_q_heads=8, num_kv_heads=1,
+                                       context=L))
+    gpu = _bench_like_run(inp)
+    assert_close(gpu, oracle.decode_attention(*oracle_args(inp)), f"{fmt} L={L}")
