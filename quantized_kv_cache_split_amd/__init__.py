@@ -30,9 +30,13 @@ KVD_ERR_HIP = -6
 
 def _hip_error() -> str:
     """Name and text of the HIP runtime's pending error on this thread (a failed launch leaves
-    its error there), or '' when there is none.  Reading it clears it."""
+    its error there), or '' when there is none.  Reading it clears it.  Asks the runtime already
+    mapped into the process (opening one by name could load a second runtime)."""
     try:
-        hip = ctypes.CDLL("libamdhip64.so")
+        mapped = hip_runtimes_mapped()
+        if len(mapped) != 1:
+            return ""
+        hip = ctypes.CDLL(mapped[0])
         hip.hipGetLastError.restype = ctypes.c_int
         hip.hipGetErrorName.argtypes = [ctypes.c_int]
         hip.hipGetErrorName.restype = ctypes.c_char_p

@@ -39,6 +39,16 @@ def test_one_hip_runtime_per_process():
     assert os.path.dirname(maps[0]) == os.path.realpath(os.path.join(os.path.dirname(torch.__file__), "lib"))
 
 
+def test_hip_error_detail_uses_the_mapped_runtime():
+    """The error detail of a failed launch is read from the HIP runtime already in the process;
+    asking for it never maps a second one (with nothing pending it is empty)."""
+    kvd.load()
+    before = kvd.hip_runtimes_mapped()
+    detail = kvd._hip_error()
+    assert kvd.hip_runtimes_mapped() == before
+    assert isinstance(detail, str)
+
+
 def dims(**kw):
     base = dict(num_seqs=16, num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
                 max_blocks_per_seq=2048, num_pool_blocks=33792, max_context_len=32768,
