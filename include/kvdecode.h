@@ -32,7 +32,10 @@
  * cache).  Query i sits at position p = L - n_q + i and attends causally exactly like the
  * decode query of the context prefix that ends there: keys [lo_i, p] with lo_i = max(0, p + 1 -
  * window[b]) under a window, else 0; the ALiBi term is alibi_slopes[h] * (j - p).  A sequence
- * with 0 < L < n_q gets NaN rows (its query positions would be negative).
+ * with 0 < L < n_q gets NaN rows (its query positions would be negative).  The queries of a
+ * chunk share the value operand of one matrix product, so a non-finite value stored in a key
+ * that one query attends reaches the rows of the others that do not (weight 0 times NaN);
+ * keys outside every query's range are never multiplied.
  *
  * Conventions for every entry point.
  *   - All array pointers are DEVICE pointers owned by the caller.  The library never

@@ -378,7 +378,8 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
 
     poison: spare pages and tail slots past each context length hold NaN (bf16 0x7FC0,
         fp8 0x7F, codebook norm NaN), so any read that reaches the arithmetic shows up.
-    poison_before_window: also poison pages that lie wholly before a window's start.
+    poison_before_window: also poison pages that lie wholly before the first key any query of
+        the sequence attends (L - W, or L - n_q + 1 - W for a chunk of n_q queries).
     unused_fill: block-table entries past a sequence's last page -> 'spare' (a poisoned spare
         page) or -1.
     kv_override: callable(seq, L) -> (K [Hkv, L, D], V [Hkv, L, D]) float32 logical values,
@@ -523,8 +524,9 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         ve = ve.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
         k_cache[phys] = pack_k_pages(fmt, ke)
         v_cache[phys] = pack_v_pages(fmt, ve)
-        if poison_before_window and W[b] > 0 and Lb > W[b]:
-            first_live = (Lb - int(W[b])) // BLOCK_SIZE
+        first_key = Lb - s.queries_per_seq + 1 - int(W[b])   # of the chunk's first query
+        if poison_before_window and W[b] > 0 and first_key > 0:
+            first_live = first_key // BLOCK_SIZE
             dead = phys[:first_live]
             if fmt == "bf16" or k_fp8:
                 kview[dead] = k_poison
