@@ -598,18 +598,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         hb = (size_t)pb * p.Hkv + hk;
     };
 
-    // ---- one pair: logits, online softmax, PV ------------------------------------------
-    // A pair index at or past npairs is a no-op: its token window is empty, so every logit
-    // is -inf, no reference moves, p = 0 and the V values are zero.
-    auto compute = [&](Raw& r, int k) {
-        const int pgA = pg0 + 2 * min(k, npairs - 1);
-        const bool hasB = pgA + 1 < pg1;
-        const int hi_k = k < npairs ? hi : lo;
-        const bool full = MQ ? (pgA * kPageTokens >= max(lo, tile_lo)) && hasB &&
-                                   ((pgA + 2) * kPageTokens <= min(hi_k, tile_hi))
-                             : (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
-
-        f32x4 sx = {0.f, 0.f, 0.f, 0.f}, sy = {0.f, 0.f, 0.f, 0.f};
+    // ---- one pair's logits: S^T = K Q^T for its two 16-token tiles ------------------------
+    auto qk = [&](Raw& r, f32x4& sx, f32x4& sy) {
+        sx = f32x4{0.f, 0.f, 0.f, 0.f};
+        sy = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == KVD_BF16) {
 #pragma unroll
@@ -650,6 +642,21 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             sx += sx2;
             sy += sy2;
         }
+    };
+
+    // ---- one pair: online softmax and PV, given its logits ----------------------------------
+    // A pair index at or past npairs is a no-op: its token window is empty, so every logit
+    // is -inf, no reference moves, p = 0 and the V values are zero.  `mid` runs after the
+    // softmax bookkeeping, in the basic block of the PV product: the pipelined walk computes
+    // the next pair's logits there, so that their table reads and MFMAs interleave with this
+    // pair's (the lazy-rescale branch would otherwise separate the two).
+    auto finish = [&](Raw& r, int k, f32x4 sx, f32x4 sy, auto&& mid) {
+        const int pgA = pg0 + 2 * min(k, npairs - 1);
+        const bool hasB = pgA + 1 < pg1;
+        const int hi_k = k < npairs ? hi : lo;
+        const bool full = MQ ? (pgA * kPageTokens >= max(lo, tile_lo)) && hasB &&
+                                   ((pgA + 2) * kPageTokens <= min(hi_k, tile_hi))
+                             : (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
 
         float z[8];
 #pragma unroll
@@ -754,6 +761,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             for (int t = 0; t < VT; ++t) oacc[t] *= f;
             m_run = m_new;
         }
+        mid();
         float pe[8], psum = 0.0f;
         const float m_ref = MQ ? fmaxf(m_run, -FLT_MAX) : m_run;
 #pragma unroll
@@ -802,6 +810,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
                 oacc[t] = mfma_bf16(vop, plo, oacc[t]);
             }
         }
+    };
+
+    auto compute = [&](Raw& r, int k) {
+        f32x4 sx, sy;
+        qk(r, sx, sy);
+        finish(r, k, sx, sy, [] {});
     };
 
     // ---- split sequences: close a partition after its last pair ------------------------
@@ -879,18 +893,48 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         // The scheduling barriers keep each refill after the compute that frees its buffer:
         // vmcnt retires in issue order, so a refill hoisted above an older pair's compute
         // would make that compute wait for every younger load too.
+        if constexpr (kVcb && !kKcb) {
+            // Turbo8 (FP8 K, codebook V; latency-bound): software-pipelined by one pair.  The
+            // logits of pair k + 1 are computed inside pair k's PV block, so the two products'
+            // MFMAs and the V table reads overlap.  Buffer i is still refilled once pair
+            // k + i's PV is done; the logits of the pair after the last are computed on the
+            // clamped loads and dropped.  (Measured: Turbo8 32K 88.0 -> 84.8 us.  With codebook
+            // K the next pair's K-table reads then wait on loads issued half a pair earlier
+            // instead of one and a half: Turbo4 / Turbo3 ran 2% slower, so they keep the
+            // plain walk.)
+            f32x4 sx, sy;
+            qk(buf[0], sx, sy);
 #pragma unroll 1
-        for (int k = 0; k < npairs; k += PF) {
+            for (int k = 0; k < npairs; k += PF) {
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                compute(buf[i], k + i);
-                if (si.split) close_partition(k + i);
-                __builtin_amdgcn_sched_barrier(0);
-                size_t ha, hb;
-                heads(ida[i], idb[i], ha, hb);
-                load_pair<FMT, D>(buf[i], p, ln, ha, hb);
-                fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int i = 0; i < PF; ++i) {
+                    f32x4 nx, ny;
+                    finish(buf[i], k + i, sx, sy, [&] { qk(buf[(i + 1) % PF], nx, ny); });
+                    if (si.split) close_partition(k + i);
+                    __builtin_amdgcn_sched_barrier(0);
+                    size_t ha, hb;
+                    heads(ida[i], idb[i], ha, hb);
+                    load_pair<FMT, D>(buf[i], p, ln, ha, hb);
+                    fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                    sx = nx;
+                    sy = ny;
+                }
+            }
+        } else {
+#pragma unroll 1
+            for (int k = 0; k < npairs; k += PF) {
+#pragma unroll
+                for (int i = 0; i < PF; ++i) {
+                    compute(buf[i], k + i);
+                    if (si.split) close_partition(k + i);
+                    __builtin_amdgcn_sched_barrier(0);
+                    size_t ha, hb;
+                    heads(ida[i], idb[i], ha, hb);
+                    load_pair<FMT, D>(buf[i], p, ln, ha, hb);
+                    fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
