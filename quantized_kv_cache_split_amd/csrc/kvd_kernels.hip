@@ -646,11 +646,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
 
     // ---- one pair: online softmax and PV, given its logits ----------------------------------
     // A pair index at or past npairs is a no-op: its token window is empty, so every logit
-    // is -inf, no reference moves, p = 0 and the V values are zero.  `mid` runs after the
-    // softmax bookkeeping, in the basic block of the PV product: the pipelined walk computes
-    // the next pair's logits there, so that their table reads and MFMAs interleave with this
-    // pair's (the lazy-rescale branch would otherwise separate the two).
-    auto finish = [&](Raw& r, int k, f32x4 sx, f32x4 sy, auto&& mid) {
+    // is -inf, no reference moves, p = 0 and the V values are zero.
+    auto finish = [&](Raw& r, int k, f32x4 sx, f32x4 sy) {
         const int pgA = pg0 + 2 * min(k, npairs - 1);
         const bool hasB = pgA + 1 < pg1;
         const int hi_k = k < npairs ? hi : lo;
@@ -761,7 +758,6 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
             for (int t = 0; t < VT; ++t) oacc[t] *= f;
             m_run = m_new;
         }
-        mid();
         float pe[8], psum = 0.0f;
         const float m_ref = MQ ? fmaxf(m_run, -FLT_MAX) : m_run;
 #pragma unroll
@@ -815,7 +811,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     auto compute = [&](Raw& r, int k) {
         f32x4 sx, sy;
         qk(r, sx, sy);
-        finish(r, k, sx, sy, [] {});
+        finish(r, k, sx, sy);
     };
 
     // ---- split sequences: close a partition after its last pair ------------------------
@@ -893,48 +889,18 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
         // The scheduling barriers keep each refill after the compute that frees its buffer:
         // vmcnt retires in issue order, so a refill hoisted above an older pair's compute
         // would make that compute wait for every younger load too.
-        if constexpr (kVcb && !kKcb) {
-            // Turbo8 (FP8 K, codebook V; latency-bound): software-pipelined by one pair.  The
-            // logits of pair k + 1 are computed inside pair k's PV block, so the two products'
-            // MFMAs and the V table reads overlap.  Buffer i is still refilled once pair
-            // k + i's PV is done; the logits of the pair after the last are computed on the
-            // clamped loads and dropped.  (Measured: Turbo8 32K 88.0 -> 84.8 us.  With codebook
-            // K the next pair's K-table reads then wait on loads issued half a pair earlier
-            // instead of one and a half: Turbo4 / Turbo3 ran 2% slower, so they keep the
-            // plain walk.)
-            f32x4 sx, sy;
-            qk(buf[0], sx, sy);
 #pragma unroll 1
-            for (int k = 0; k < npairs; k += PF) {
+        for (int k = 0; k < npairs; k += PF) {
 #pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    f32x4 nx, ny;
-                    finish(buf[i], k + i, sx, sy, [&] { qk(buf[(i + 1) % PF], nx, ny); });
-                    if (si.split) close_partition(k + i);
-                    __builtin_amdgcn_sched_barrier(0);
-                    size_t ha, hb;
-                    heads(ida[i], idb[i], ha, hb);
-                    load_pair<FMT, D>(buf[i], p, ln, ha, hb);
-                    fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
-                    __builtin_amdgcn_sched_barrier(0);
-                    sx = nx;
-                    sy = ny;
-                }
-            }
-        } else {
-#pragma unroll 1
-            for (int k = 0; k < npairs; k += PF) {
-#pragma unroll
-                for (int i = 0; i < PF; ++i) {
-                    compute(buf[i], k + i);
-                    if (si.split) close_partition(k + i);
-                    __builtin_amdgcn_sched_barrier(0);
-                    size_t ha, hb;
-                    heads(ida[i], idb[i], ha, hb);
-                    load_pair<FMT, D>(buf[i], p, ln, ha, hb);
-                    fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
+            for (int i = 0; i < PF; ++i) {
+                compute(buf[i], k + i);
+                if (si.split) close_partition(k + i);
+                __builtin_amdgcn_sched_barrier(0);
+                size_t ha, hb;
+                heads(ida[i], idb[i], ha, hb);
+                load_pair<FMT, D>(buf[i], p, ln, ha, hb);
+                fetch_ids(min(k + i + 2 * PF, klast), ida[i], idb[i]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -1150,12 +1116,14 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     p.out[i] = val;
 }
 
-// Pairs in flight per wave: two for every format (BF16 32 KB, FP8 16 KB per wave).  Deeper
-// prefetch does not pay: with every wave of the chip streaming, FP8 at four pairs in flight
-// reads about 1.5% slower than at two (more outstanding requests, more HBM contention), and
-// the codebook formats are bound by compute latency, not by the loads.
+// Pairs in flight per wave.  With every wave of the chip streaming random pages, fewer
+// outstanding requests read HBM more efficiently.  FP8 32K partition kernel, A/B on one GPU:
+// 195.6 us at one pair in flight (8 KB per wave) against 204.0 us at two; three pairs ran
+// 1.4% slower than two, four slower still.  Turbo8 (FP8 K) 32K: 80.9 against 85.1 us.  BF16
+// (16 KB per pair) runs the same at one or two.  Turbo4 / Turbo3 are bound by compute latency
+// and need the second pair to cover it (one pair: 1.5-3% slower).
 template <int FMT>
-constexpr int prefetch_depth() { return 2; }
+constexpr int prefetch_depth() { return FMT == KVD_FP8_E4M3 || FMT == KVD_TURBO8 ? 1 : 2; }
 
 template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
