@@ -177,3 +177,24 @@ def test_append_arg_errors():
     assert append_call(fmt=0, scales=None, cb=None, sign=None, n=0) == 0    # BF16 needs neither
     assert append_call(k=FAKE + 4) == -4 and append_call(kc=FAKE + 8) == -4
     assert append_call(n=0) == 0 and append_call(dims(num_seqs=0)) == 0    # nothing launched
+
+
+def test_build_script_runs_without_the_package():
+    """build() must work in a fresh checkout, where the library does not exist yet: the build
+    script is loaded by path (importing it through the package would run the package's
+    __init__, which refuses to load before the library is built), and its hipcc line targets
+    gfx950 with packed fp32 VALU ops switched off."""
+    import importlib.util
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    src = open(os.path.join(root, "__graft_entry__.py")).read()
+    assert "spec_from_file_location" in src and "from quantized_kv_cache_split_amd.build" not in src
+    spec = importlib.util.spec_from_file_location(
+        "_kvd_build_test", os.path.join(root, "quantized_kv_cache_split_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    cmd = mod.command("/tmp/unused.so")
+    assert "--offload-arch=gfx950" in cmd
+    i = cmd.index("-packed-fp32-ops")
+    assert cmd[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
+    assert all(s in cmd for s in mod.SOURCES)
