@@ -131,10 +131,13 @@ typedef struct kvd_dims {
                                     consecutive partitions of a split sequence one wavefront
                                     walks (it writes every partition's triple).  0: auto
                                     (about one wavefront per resident slot of the device when
-                                    every sequence had max_context_len tokens, at most 4);
-                                    > 0: that many.  Capped at 4096 / (head_dim * rows),
-                                    rows = min(16, n_q * Hq / Hkv), and treated as 1 when the
-                                    partition size is not a multiple of 32.  Must be >= 0. */
+                                    every sequence had max_context_len tokens, at most 4;
+                                    single-query BF16 at head_dim 128 uses a layout with one
+                                    workgroup per CU and runs of up to 8 when that covers
+                                    the device in one round); > 0: that many.  Capped at
+                                    4096 / (head_dim * rows), rows = min(16, n_q * Hq / Hkv),
+                                    and treated as 1 when the partition size is not a
+                                    multiple of 32.  Must be >= 0. */
     int32_t queries_per_seq;     /* n_q: queries per sequence, a chunk at the last n_q positions
                                     (above); 0 or 1: single-query decode.  The n_q * Hq / Hkv
                                     query rows of a KV head share one pass over its pages per

@@ -5,6 +5,7 @@
 // the partition kernel and then the reduce, and report a launch failure.  Unlike that wrapper
 // it allocates nothing: the partial buffers live in a caller-provided workspace.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 #include "kvd_internal.h"
 #include "kvdecode.h"
@@ -58,31 +59,49 @@ int device_cus() {
     return cus;
 }
 
-// Partitions each wave of the partition kernel walks.  A wave pays a fixed start-up (query
-// staging, the block-table -> page-load latency chain, filling its load pipeline) and leaves a
-// tail when it ends; walking several partitions amortises both.  The automatic choice keeps
-// about one wave per resident slot of the chip (P * Hkv * B waves / (CUs * 8)) as if every
-// sequence were max_context_len long, capped at kMaxRun (ragged batches, whose real work is
-// smaller, do better with short runs) and at the rows a wave can stage in LDS
-// (stage_rows(D) / group).  Runs need
-// partition boundaries on even pages (partition size a multiple of 32).
-int choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
-    if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return 1;
+// Partitions each wave of the partition kernel walks, and the kernel's layout.  A wave pays a
+// fixed start-up (query staging, the block-table -> page-load latency chain, filling its load
+// pipeline) and leaves a tail when it ends; walking several partitions amortises both.  The
+// automatic choice keeps about one wave per resident slot of the chip (P * Hkv * B waves /
+// resident waves) as if every sequence were max_context_len long.  Where the wide layout is
+// built (one workgroup per CU) it is taken if runs of at most kMaxRunWide cover the chip in
+// one round; otherwise runs are capped at kMaxRun (ragged batches, whose real work is smaller,
+// do better with short runs).  Runs are also capped at the rows a wave can stage in LDS
+// (stage_rows / group) and need partition boundaries on even pages (partition size a multiple
+// of 32).  An explicit partitions_per_wave always uses the two-workgroup layout.
+struct RunChoice {
+    int run;
+    bool wide;
+};
+RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
+    if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return {1, false};
+    const int64_t rows = query_rows(d);
+    const int64_t group_rows = rows < kvd::kMaxGroup ? rows : kvd::kMaxGroup;
+    auto staging_cap = [&](bool wide) -> int64_t {
+        return fmt < KVD_TURBO4 ? kvd::stage_rows(d->head_dim, wide) / group_rows : INT64_MAX;
+    };
     int64_t r = d->partitions_per_wave;
+    bool wide = false;
     if (r == 0) {
         const int64_t tiles = query_tiles(d);
         const int64_t waves = (int64_t)pl.P * d->num_kv_heads * tiles * d->num_seqs;
-        const int64_t slots = (int64_t)device_cus() * kvd::kWavesPerCU;
-        r = (waves + slots - 1) / slots;
-        if (r > kvd::kMaxRun) r = kvd::kMaxRun;
+        if (kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
+            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(true);
+            const int64_t rw = (waves + slots - 1) / slots;
+            if (rw <= kvd::kMaxRunWide && rw <= staging_cap(true)) {
+                wide = true;
+                r = rw;
+            }
+        }
+        if (!wide) {
+            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(false);
+            r = (waves + slots - 1) / slots;
+            if (r > kvd::kMaxRun) r = kvd::kMaxRun;
+        }
     }
-    if (fmt < KVD_TURBO4) {   // BF16 / FP8 stage the run's triples in LDS
-        const int64_t rows = query_rows(d);
-        const int64_t cap = kvd::stage_rows(d->head_dim) / (rows < kvd::kMaxGroup ? rows : kvd::kMaxGroup);
-        if (r > cap) r = cap;
-    }
+    if (r > staging_cap(wide)) r = staging_cap(wide);
     if (r > pl.P) r = pl.P;
-    return r < 1 ? 1 : (int)r;
+    return {r < 1 ? 1 : (int)r, wide};
 }
 
 // Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
@@ -190,7 +209,8 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.part_size = pl.part_size;
     p.P = pl.P;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
-    p.run = choose_run(d, pl, fmt);
+    const RunChoice rc = choose_run(d, pl, fmt);
+    p.run = rc.run;
     const int waves = kvd::waves_per_group(fmt);
     // token indices of every partition a workgroup can name must fit in int32
     if (pl.P && ((int64_t)pl.P + (int64_t)waves * p.run) * pl.part_size > 0x7FFFFFFFLL)
@@ -206,7 +226,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
         const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qt * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);
-        e = kvd::launch_partitions(fmt, p, grid, s);
+        e = kvd::launch_partitions(fmt, rc.wide, p, grid, s);
         if (e != hipSuccess) return KVD_ERR_HIP;
     }
     if ((phases & kPhase2) && pl.P) {

@@ -13,14 +13,23 @@ constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
 constexpr int kMaxGroup = 16;       // query heads one MFMA tile (one wave) handles
 constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
-constexpr int kWavesPerCU = 8;      // resident waves of the partition kernel per CU
+// Wide layout of the partition kernel: one 4-wave workgroup per CU (one wave per SIMD) with 64
+// staged rows per wave (137 KB of LDS), so runs of up to kMaxRunWide partitions.  Built for
+// single-query BF16 at head_dim 128, where the random-page stream reads faster with half the
+// waves (BF16 16 x 32K: 380 against 390 us per call); the host takes it only when such runs
+// cover the chip in one round (a large ragged batch balances better with short runs).
+constexpr int kMaxRunWide = 8;
+constexpr bool wide_layout_built(int fmt, int d, bool mq) { return fmt == 0 && d == 128 && !mq; }
+// Resident waves of the partition kernel per CU, and the waves per SIMD it is compiled for.
+constexpr int waves_per_cu(bool wide) { return wide ? 4 : 8; }
+constexpr int waves_per_simd(bool wide) { return wide ? 1 : 2; }
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
 // the codebook formats (sharing conflict-free codebook tables: 128 KB for Turbo4 / Turbo3, one
 // workgroup per CU; 64 KB for Turbo8, two per CU).
 constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
 // (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
-// a wave's run of partitions is capped at stage_rows(D) / group (BF16 / FP8).
-constexpr int stage_rows(int d) { return 4096 / d; }
+// a wave's run of partitions is capped at stage_rows / group (BF16 / FP8).
+constexpr int stage_rows(int d, bool wide) { return (wide ? 8192 : 4096) / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };
 
@@ -95,7 +104,7 @@ inline hipError_t launch_kernel(void (*kernel)(Params), dim3 grid, dim3 block, h
 }
 
 // Launchers (kvd_kernels.hip, kvd_append.hip).  Return hipSuccess or the launch error.
-hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_partitions(int fmt, bool wide, const LaunchParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);

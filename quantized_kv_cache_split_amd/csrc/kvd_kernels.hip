@@ -340,8 +340,8 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
 // partitions.
-template <int FMT, int D, bool CAP, int PF, bool MQ>
-__global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel(const LaunchParams p) {
+template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE>
+__global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) void partition_kernel(const LaunchParams p) {
     constexpr bool kKcb = k_codebook<FMT>();   // rotated query, K table, K norms
     constexpr bool kVcb = v_codebook<FMT>();   // V table, V norms, output in the rotated domain
     constexpr int kTables = kKcb ? 2 : 1;      // codebook pair tables in LDS (V table last)
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), 2) void partition_kernel
     // address 0 (K and V, 128 KB, one workgroup per CU for Turbo4 / Turbo3; V only, 64 KB, two
     // per CU for Turbo8), reused for the unsplit merge once every wave has finished its walk;
     // these waves write partials directly.
-    constexpr int SR = kVcb ? kMaxGroup : stage_rows(D);
+    constexpr int SR = kVcb ? kMaxGroup : stage_rows(D, WIDE);
     constexpr int SD = D + 4;
     struct Merge {
         float m[kW][SR];
@@ -1122,18 +1122,26 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
 // 1.4% slower than two, four slower still.  Turbo8 (FP8 K) 32K: 80.9 against 85.1 us.  BF16
 // (16 KB per pair) runs the same at one or two.  Turbo4 / Turbo3 are bound by compute latency
 // and need the second pair to cover it (one pair: 1.5-3% slower).
-template <int FMT>
-constexpr int prefetch_depth() { return FMT == KVD_FP8_E4M3 || FMT == KVD_TURBO8 ? 1 : 2; }
+template <int FMT, bool WIDE>
+constexpr int prefetch_depth() {
+    return FMT == KVD_FP8_E4M3 || FMT == KVD_TURBO8 || WIDE ? 1 : 2;
+}
 
 template <int FMT, int D>
-hipError_t launch_partitions_t(const LaunchParams& p, dim3 grid, hipStream_t s) {
-    constexpr int PF = prefetch_depth<FMT>();
+hipError_t launch_partitions_t(const LaunchParams& p, bool wide, dim3 grid, hipStream_t s) {
+    constexpr int PF = prefetch_depth<FMT, false>();
     const dim3 block(64 * waves_per_group(FMT));
     if (p.nq > 1)
-        return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true>, grid, block, s, p)
-                                : launch_kernel(partition_kernel<FMT, D, false, PF, true>, grid, block, s, p);
-    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, false>, grid, block, s, p)
-                            : launch_kernel(partition_kernel<FMT, D, false, PF, false>, grid, block, s, p);
+        return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true, false>, grid, block, s, p)
+                                : launch_kernel(partition_kernel<FMT, D, false, PF, true, false>, grid, block, s, p);
+    if constexpr (wide_layout_built(FMT, D, false)) {
+        constexpr int PFW = prefetch_depth<FMT, true>();
+        if (wide)
+            return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PFW, false, true>, grid, block, s, p)
+                                    : launch_kernel(partition_kernel<FMT, D, false, PFW, false, true>, grid, block, s, p);
+    }
+    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, false, false>, grid, block, s, p)
+                            : launch_kernel(partition_kernel<FMT, D, false, PF, false, false>, grid, block, s, p);
 }
 template <int FMT, int D>
 hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
@@ -1142,15 +1150,15 @@ hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_partitions(int fmt, const LaunchParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_partitions(int fmt, bool wide, const LaunchParams& p, dim3 grid, hipStream_t s) {
     switch (fmt) {
-        case KVD_BF16: return p.D == 64 ? launch_partitions_t<KVD_BF16, 64>(p, grid, s)
-                                        : launch_partitions_t<KVD_BF16, 128>(p, grid, s);
-        case KVD_FP8_E4M3: return p.D == 64 ? launch_partitions_t<KVD_FP8_E4M3, 64>(p, grid, s)
-                                            : launch_partitions_t<KVD_FP8_E4M3, 128>(p, grid, s);
-        case KVD_TURBO4: return launch_partitions_t<KVD_TURBO4, 128>(p, grid, s);
-        case KVD_TURBO8: return launch_partitions_t<KVD_TURBO8, 128>(p, grid, s);
-        default: return launch_partitions_t<KVD_TURBO3, 128>(p, grid, s);
+        case KVD_BF16: return p.D == 64 ? launch_partitions_t<KVD_BF16, 64>(p, wide, grid, s)
+                                        : launch_partitions_t<KVD_BF16, 128>(p, wide, grid, s);
+        case KVD_FP8_E4M3: return p.D == 64 ? launch_partitions_t<KVD_FP8_E4M3, 64>(p, wide, grid, s)
+                                            : launch_partitions_t<KVD_FP8_E4M3, 128>(p, wide, grid, s);
+        case KVD_TURBO4: return launch_partitions_t<KVD_TURBO4, 128>(p, wide, grid, s);
+        case KVD_TURBO8: return launch_partitions_t<KVD_TURBO8, 128>(p, wide, grid, s);
+        default: return launch_partitions_t<KVD_TURBO3, 128>(p, wide, grid, s);
     }
 }
 
