@@ -6,8 +6,9 @@
 // reduce"; 512-token partitions; fp32 per-partition max, sum and output) and the attention.rs
 // README (Split-K decode for every cache format from 1024 tokens on, one shared float reduce):
 //
-//   partition_kernel<FMT, D, CAP, PF, MQ>  a 1-D grid of workgroups (4 waves for BF16 / FP8,
-//       8 for the codebook formats) over (partition slot, sequence, KV head x query tile).
+//   partition_kernel<FMT, D, CAP, PF, MQ, WIDE>  a 1-D grid of workgroups (4 waves for BF16 /
+//       FP8, two per CU, or one per CU in the WIDE layout of single-query BF16; 8 for the
+//       codebook formats) over (partition slot, sequence, KV head x query tile).
 //       For a split sequence each wave walks a run of consecutive partitions of one (sequence,
 //       KV head, query tile) and writes every partition's (m, l, o) triple; an unsplit
 //       sequence's pages are shared by the workgroup's waves, which merge through LDS.  A wave
