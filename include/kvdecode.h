@@ -183,8 +183,9 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
                           size_t workspace_bytes, void* stream);
 
 /* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
- * partitions_per_wave partitions, four wavefronts per workgroup.  For a split sequence,
- * partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)) and its triple goes to the
+ * partitions_per_wave partitions, four wavefronts per workgroup (eight for the Turbo
+ * formats).  For a split sequence, partition p covers tokens
+ * [max(lo, p*P), min(L, (p+1)*P)) and its triple goes to the
  * workspace at (b, i, h, p):  m = max_j z_j * log2(e)  (base-2 units),
  * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
  * rotated domain for the Turbo formats; the keys j are those of the partition that query i

@@ -55,3 +55,38 @@ def test_random_configuration(case):
             f"hkv={s.num_kv_heads} nq={s.queries_per_seq} L={list(inp.context_lens)} "
             f"W={list(inp.window)} cap={s.softcap} ps={ps} ppw={ppw} alibi={alibi is not None}")
     assert_close(gpu, ref, what)
+
+
+def _draw_single_query(case):
+    """Single-query decode at head_dim 128 in the formats whose launch shapes differ most
+    (BF16 picks between its one- and two-workgroup-per-CU layouts; FP8 and Turbo8 walk with one
+    page pair in flight): automatic or explicit partitioning, contexts up to 12K."""
+    r = np.random.default_rng(np.random.SeedSequence([case, 0xD128]))
+    fmt = ["bf16", "fp8", "turbo8"][r.integers(3)]
+    hkv = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 4, 8, 16]))
+    B = int(r.integers(1, 9))
+    hi = int(r.choice([1500, 4100, 12000]))
+    lengths = r.integers(1, hi + 1, size=B)
+    lengths[r.integers(B)] = hi
+    windows = np.where(r.random(B) < 0.3, r.integers(1, hi + 1, size=B), 0)
+    spec = kvgen.spec("c1", fmt=fmt, head_dim=128, num_q_heads=g * hkv, num_kv_heads=hkv,
+                      num_seqs=B, pool_total=None, seed=1000 + case,
+                      softcap=float(r.choice([0.0, 0.0, 30.0])))
+    inp = kvgen.make_inputs(spec, lengths=lengths, windows=windows,
+                            poison_before_window=bool(r.integers(2)))
+    ps = int(r.choice([0, 0, 0, 256, 512]))
+    ppw = int(r.choice([0, 0, 0, 2, 4]))
+    return inp, ps, ppw
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_single_query_d128(case):
+    inp, ps, ppw = _draw_single_query(case)
+    s = inp.spec
+    ref = oracle.decode_attention(*oracle_args(inp))
+    gpu = GpuBatch(inp, partition_size=ps, partitions_per_wave=ppw).run()
+    what = (f"single-query case {case}: {s.fmt} B={s.num_seqs} hq={s.num_q_heads} "
+            f"hkv={s.num_kv_heads} L={list(inp.context_lens)} W={list(inp.window)} "
+            f"cap={s.softcap} ps={ps} ppw={ppw}")
+    assert_close(gpu, ref, what)
