@@ -824,6 +824,14 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         finish(r, k, sx, sy);
     };
 
+    // Codebook formats (8 waves, two per SIMD): the hardware issues from the older of a SIMD's
+    // two waves first, so waves 4-7 fall behind waves 0-3.  The pair start with opposite
+    // priorities and swap them at every partition they close.
+    bool prio_hi = (wave >> 2) & 1;
+    if constexpr (kVcb) {
+        if (prio_hi) __builtin_amdgcn_s_setprio(1);
+    }
+
     // ---- split sequences: close a partition after its last pair ------------------------
     // Writes the partition's triple (m = the exact max logit in base-2 units, l = the sum
     // taken relative to it, o = O / l in output units, which no reference choice affects) and
@@ -861,6 +869,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                         sm_l[wave][row] = lx;
                     }
                 }
+            }
+            if constexpr (kVcb) {   // hand the SIMD's issue priority to its other wave
+                prio_hi = !prio_hi;
+                if (prio_hi) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
             }
             m_run = m_true = -INFINITY;
             l_run = 0.0f;
