@@ -415,6 +415,46 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         return row0 + t + (size_t)i * (p.Hq - p.g);
     };
 
+    // Start-up loads of the codebook formats: the levels for the tables and (codebook K) the
+    // query rows to rotate depend only on the launch and on this workgroup's head and
+    // sequence.  They go out together here, ahead of the first wait on the sequence's length,
+    // so the round trips overlap (issued one after another they took ~5 of the ~8 us
+    // start-up).
+    [[maybe_unused]] float cb_k0 = 0.0f, cb_k1 = 0.0f, cb_v0 = 0.0f, cb_v1 = 0.0f;
+    [[maybe_unused]] float kmax = 0.0f, vmax = 0.0f;
+    constexpr int kQPer = kKcb ? (kMaxGroup * D + kThr - 1) / kThr : 1;   // query elements per thread
+    [[maybe_unused]] uint16_t q_raw[kQPer];
+    [[maybe_unused]] float q_sgn[kQPer];
+    if constexpr (kVcb) {
+        // levels: 2^kbits K levels then 16 V levels, or (Turbo8) 16 V levels
+        const int kl = kKcb ? 1 << p.kbits : 0;
+        if constexpr (kKcb) {
+            // a fixed trip count (one scalar load); the array holds kl + 16 >= 24 floats
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float c = fabsf(p.codebook[i]);
+                kmax = i < kl ? fmaxf(kmax, c) : kmax;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
+        const int e = (tid >> 1) & 255;   // this thread's table entry (index byte)
+        if constexpr (kKcb) {
+            cb_k0 = p.codebook[e % kl];
+            cb_k1 = p.codebook[(e / kl) % kl];
+        }
+        cb_v0 = p.codebook[kl + (e & 15)];
+        cb_v1 = p.codebook[kl + (e >> 4)];
+    }
+    if constexpr (kKcb) {
+#pragma unroll
+        for (int u = 0; u < kQPer; ++u) {
+            const int i = min(tid + u * kThr, g * D - 1);   // clamped; stored only if in range
+            q_raw[u] = p.q[row_index(i / D) * D + i % D];
+            q_sgn[u] = p.sign[i % D];
+        }
+    }
+
     if (si.bad || si.L == 0) {
         if (xb == 0) {
             const float v = si.bad ? __builtin_nanf("") : 0.0f;
@@ -477,20 +517,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 
     if constexpr (kVcb) {
         // codebook pair tables (levels scaled by a power of two so the largest magnitude is in
-        // [0.5, 1)); the levels are 2^kbits K levels then 16 V levels, or (Turbo8) 16 V levels
-        const int kl = kKcb ? 1 << p.kbits : 0;
-        float kmax = 0.0f, vmax = 0.0f;
-        // A fixed trip count, so the 16 loads go out as one scalar load.  A loop to kl emitted a
-        // dependent load-and-wait per level, 4-7 us per workgroup at the start of a launch.
-        // (The array holds kl + 16 >= 24 floats, so reading 16 stays inside it.)
-        if constexpr (kKcb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float c = fabsf(p.codebook[i]);
-                kmax = i < kl ? fmaxf(kmax, c) : kmax;
-            }
-        }
-        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
+        // [0.5, 1)), from the levels loaded at the start
         ksc = pow2_normaliser(kmax);
         const float vsc = pow2_normaliser(vmax);
         {
@@ -500,11 +527,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             uint32_t h, l;
             u32x4 kv = {0u, 0u, 0u, 0u};
             if constexpr (kKcb) {
-                const int ki0 = e % kl, ki1 = (e / kl) % kl;
-                f16_hilo(p.codebook[ki0] * ksc, p.codebook[ki1] * ksc, h, l);
+                f16_hilo(cb_k0 * ksc, cb_k1 * ksc, h, l);
                 kv = u32x4{h, l, h, l};
             }
-            f16_hilo(p.codebook[kl + (e & 15)] * vsc, p.codebook[kl + (e >> 4)] * vsc, h, l);
+            f16_hilo(cb_v0 * vsc, cb_v1 * vsc, h, l);
             const u32x4 vv = {h, l, h, l};
 #pragma unroll
             for (int c = 0; c < kLutCopies / 2; c += 2) {
@@ -518,11 +544,11 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         if constexpr (!kKcb) __syncthreads();
     }
     if constexpr (kKcb) {
-        // q_rot = H (s * q): rows of the group in LDS, then the butterfly
-        for (int i = tid; i < g * D; i += kThr) {
-            const int r = i / D, d = i % D;
-            const uint16_t qb = p.q[row_index(r) * D + d];
-            lds.row[i] = bf16_bits_to_f32(qb) * p.sign[d];
+        // q_rot = H (s * q): rows of the group in LDS (loaded at the start), then the butterfly
+#pragma unroll
+        for (int u = 0; u < kQPer; ++u) {
+            const int i = tid + u * kThr;
+            if (i < g * D) lds.row[i] = bf16_bits_to_f32(q_raw[u]) * q_sgn[u];
         }
         __syncthreads();
         fwht_rows<D>(lds.row, g, tid, kThr);
