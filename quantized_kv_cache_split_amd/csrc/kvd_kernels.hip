@@ -422,9 +422,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // start-up).
     [[maybe_unused]] float cb_k0 = 0.0f, cb_k1 = 0.0f, cb_v0 = 0.0f, cb_v1 = 0.0f;
     [[maybe_unused]] float kmax = 0.0f, vmax = 0.0f;
-    constexpr int kQPer = kKcb ? (kMaxGroup * D + kThr - 1) / kThr : 1;   // query elements per thread
-    [[maybe_unused]] uint16_t q_raw[kQPer];
-    [[maybe_unused]] float q_sgn[kQPer];
+    // codebook K: wave w rotates query rows w, w + kW, ... (lane l holds elements 2l, 2l + 1)
+    constexpr int kQRows = kKcb ? (kMaxGroup + kW - 1) / kW : 1;
+    [[maybe_unused]] uint32_t q_raw[kQRows];
+    [[maybe_unused]] float q_s0 = 0.0f, q_s1 = 0.0f;
     if constexpr (kVcb) {
         // levels: 2^kbits K levels then 16 V levels, or (Turbo8) 16 V levels
         const int kl = kKcb ? 1 << p.kbits : 0;
@@ -447,11 +448,13 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         cb_v1 = p.codebook[kl + (e >> 4)];
     }
     if constexpr (kKcb) {
+        static_assert(D == 128, "two query elements per lane");
+        q_s0 = p.sign[2 * lane];
+        q_s1 = p.sign[2 * lane + 1];
 #pragma unroll
-        for (int u = 0; u < kQPer; ++u) {
-            const int i = min(tid + u * kThr, g * D - 1);   // clamped; stored only if in range
-            q_raw[u] = p.q[row_index(i / D) * D + i % D];
-            q_sgn[u] = p.sign[i % D];
+        for (int u = 0; u < kQRows; ++u) {   // rows past g are clamped (loaded, never used)
+            const int r = min(wave + kW * u, g - 1);
+            q_raw[u] = *reinterpret_cast<const uint32_t*>(p.q + row_index(r) * D + 2 * lane);
         }
     }
 
@@ -544,21 +547,34 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         if constexpr (!kKcb) __syncthreads();
     }
     if constexpr (kKcb) {
-        // q_rot = H (s * q): rows of the group in LDS (loaded at the start), then the butterfly
-#pragma unroll
-        for (int u = 0; u < kQPer; ++u) {
-            const int i = tid + u * kThr;
-            if (i < g * D) lds.row[i] = bf16_bits_to_f32(q_raw[u]) * q_sgn[u];
-        }
-        __syncthreads();
-        fwht_rows<D>(lds.row, g, tid, kThr);
+        // q_rot = H (s * q), one row per wave in registers: the butterfly stages of the
+        // Sylvester-order transform in the usual order (element stride 1 inside the lane, then
+        // strides 2 .. 64 across lanes 1 .. 32 apart), and the row's power-of-two normaliser;
+        // rows and normalisers then go to LDS for every wave's operands (one barrier, which
+        // also completes the tables)
         float* const sm_row = lds.row;
         auto& sm_rowscale = lds.rowscale;
-        for (int r = wave; r < g; r += kW) {       // per-row power-of-two normaliser
-            float mx = fmaxf(fabsf(sm_row[r * D + lane]), fabsf(sm_row[r * D + 64 + lane]));
 #pragma unroll
-            for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-            if (lane == 0) sm_rowscale[r] = pow2_normaliser(mx);
+        for (int u = 0; u < kQRows; ++u) {
+            const int r = wave + kW * u;
+            if (r < g) {
+                const float a0 = bf16_bits_to_f32(q_raw[u] & 0xFFFFu) * q_s0;
+                const float a1 = bf16_bits_to_f32(q_raw[u] >> 16) * q_s1;
+                float b0 = a0 + a1, b1 = a0 - a1;
+#pragma unroll
+                for (int h = 1; h < 64; h <<= 1) {
+                    const bool upper = (lane & h) != 0;
+                    const float o0 = __shfl_xor(b0, h), o1 = __shfl_xor(b1, h);
+                    b0 = upper ? o0 - b0 : b0 + o0;
+                    b1 = upper ? o1 - b1 : b1 + o1;
+                }
+                float mx = fmaxf(fabsf(b0), fabsf(b1));
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+                sm_row[r * D + 2 * lane] = b0;
+                sm_row[r * D + 2 * lane + 1] = b1;
+                if (lane == 0) sm_rowscale[r] = pow2_normaliser(mx);
+            }
         }
         __syncthreads();
         const float qs = sm_rowscale[qn];
