@@ -535,10 +535,15 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             }
             f16_hilo(cb_v0 * vsc, cb_v1 * vsc, h, l);
             const u32x4 vv = {h, l, h, l};
+            // Copy order staggered by entry: in each store the 16 lanes of a pass write 16
+            // different 16-byte bank groups (entries are 256 bytes apart, so the same copy of
+            // every entry would sit in the same banks: 8-way conflicts, ~2M conflict cycles
+            // per Turbo4 launch).
 #pragma unroll
             for (int c = 0; c < kLutCopies / 2; c += 2) {
-                if constexpr (kKcb) lds.u.lut[0][(e * kLutCopies + c0 + c) / 2] = kv;
-                lds.u.lut[kTables - 1][(e * kLutCopies + c0 + c) / 2] = vv;
+                const int cc = (c + 2 * e) & (kLutCopies / 2 - 1);
+                if constexpr (kKcb) lds.u.lut[0][(e * kLutCopies + c0 + cc) / 2] = kv;
+                lds.u.lut[kTables - 1][(e * kLutCopies + c0 + cc) / 2] = vv;
             }
         }
         oscale = 1.0f / vsc;
