@@ -396,7 +396,17 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // p.nq * p.g rows (p.g for single-query decode).  More rows than kMaxGroup are split into
     // p.qt tiles ("virtual heads") of up to kMaxGroup rows, each processed like a KV head of its
     // own (its pages are read once per tile).
-    const int wg = blockIdx.x;
+    // Codebook formats: the per-token norms of KV heads 2j and 2j + 1 of a page share one
+    // 128-byte line, so within every full block of 16 workgroups, units 2i and 2i + 1 go to
+    // linear ids that are 8 apart (the same XCD, dispatched together) and one L2 fetches the
+    // line for both.  A bijection on full blocks, the identity on the tail.
+    int wg = blockIdx.x;
+    if constexpr (kVcb) {
+        if (wg < (int)(gridDim.x & ~15u)) {
+            const int r = wg & 15;
+            wg = (wg & ~15) + ((r & 7) << 1) + (r >> 3);
+        }
+    }
     const int nvh = p.Hkv * p.qt;
     const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = wg / (nvh * p.B);
     const int hk = vh / p.qt, qtile = vh - hk * p.qt;
