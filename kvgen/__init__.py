@@ -109,6 +109,10 @@ SPECS: dict[str, Spec] = {
                    queries_per_seq=2),
     "mq-t4": Spec("turbo4-L32768-q4", 8, 32, 8, 128, "turbo4", context=32768, queries_per_seq=4),
     "mq-t3": Spec("turbo3-L32768-q4", 8, 32, 8, 128, "turbo3", context=32768, queries_per_seq=4),
+    # Multi-query attention (one KV head for all 64 query heads) at 32K: four 16-row query
+    # tiles read each KV head's pages.
+    "mqa-fp8": Spec("fp8-e4m3-L32768-mqa64", 16, 64, 1, 128, "fp8", context=32768),
+    "mqa-t4": Spec("turbo4-L32768-mqa64", 8, 64, 1, 128, "turbo4", context=32768),
 }
 
 

@@ -396,15 +396,18 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // p.nq * p.g rows (p.g for single-query decode).  More rows than kMaxGroup are split into
     // p.qt tiles ("virtual heads") of up to kMaxGroup rows, each processed like a KV head of its
     // own (its pages are read once per tile).
-    // Codebook formats: the per-token norms of KV heads 2j and 2j + 1 of a page share one
-    // 128-byte line, so within every full block of 16 workgroups, units 2i and 2i + 1 go to
-    // linear ids that are 8 apart (the same XCD, dispatched together) and one L2 fetches the
-    // line for both.  A bijection on full blocks, the identity on the tail.
+    // Units that read the same lines run on one XCD at the same time, so its L2 fetches each
+    // line once for all of them: the p.qt query tiles of a KV head read the same pages, and in
+    // the codebook formats KV heads 2j and 2j + 1 share every 128-byte line of per-token norms.
+    // With m such consecutive units, within every full block of 8m workgroups, unit
+    // m * x + j goes to linear id 8 * j + x (XCD x, dispatched in consecutive rounds).  A
+    // bijection on full blocks, the identity on the tail.
     int wg = blockIdx.x;
-    if constexpr (kVcb) {
-        if (wg < (int)(gridDim.x & ~15u)) {
-            const int r = wg & 15;
-            wg = (wg & ~15) + ((r & 7) << 1) + (r >> 3);
+    if (const int m = (kVcb ? 2 : 1) * p.qt; m > 1) {
+        const int blk = 8 * m;
+        if (wg < (int)gridDim.x / blk * blk) {
+            const int r = wg % blk;
+            wg += (r & 7) * m + (r >> 3) - r;
         }
     }
     const int nvh = p.Hkv * p.qt;
