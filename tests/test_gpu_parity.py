@@ -368,3 +368,22 @@ def test_large_group_alibi_runs(fmt):
     for run in (1, 3):
         assert_close(GpuBatch(inp, partitions_per_wave=run, alibi=sl).run(), ref,
                      f"{fmt} g=40 alibi run={run}")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
+@pytest.mark.parametrize("run", [1, 2])
+def test_grouped_tiles_full_blocks_and_tail(fmt, run):
+    """Several query tiles per KV head (g = 24: two tiles) with a grid that holds full blocks of
+    the XCD grouping (8 * m workgroups, m = tiles per KV head, twice that for the codebook
+    formats) and a ragged tail that keeps the identity order.  Every unit must be computed once."""
+    inp = _small(fmt, num_q_heads=48, num_kv_heads=2, context=None, ctx_range=(1, 6000),
+                 num_seqs=5, seed=11)
+    ps = 256
+    # workgroup count of the partition launch: partition slots x KV heads x tiles x sequences
+    waves = 8 if fmt.startswith("turbo") else 4
+    n_part = -(-6000 // ps)
+    grid = -(-n_part // (waves * run)) * 2 * 2 * 5
+    m = 2 * (2 if fmt.startswith("turbo") else 1)
+    assert grid >= 8 * m and grid % (8 * m) != 0, grid
+    got = GpuBatch(inp, partition_size=ps, partitions_per_wave=run).run()
+    assert_close(got, _oracle(inp), f"{fmt} g=24 run={run} grid={grid}")
