@@ -255,17 +255,31 @@ def _q_rows(q_bits, b, h0, g):
     return bf16_to_f64(np.asarray(q_bits)[b, h0: h0 + g])
 
 
+# Memory bound of the oracle: the keys of one (sequence, KV head) are gathered at most this many
+# at a time.  One block's K and V in fp64 take 2 * 65536 * D * 8 bytes (128 MiB at D = 128), so
+# every context up to 64K keys is computed in one piece, as the plain definition reads; only
+# longer ones are cut into blocks, whose (max, sum, output) triples the LSE rule merges -- the
+# same sum in another order, which the split decode itself relies on (turboquant-rs fused
+# attention: per-partition max / sum / output, then the reduce).
+KEY_BLOCK = 1 << 16
+
+
+def key_blocks(lo: int, hi: int, block: int) -> list[tuple[int, int]]:
+    """Consecutive ranges [t0, t1) of at most ``block`` keys that tile [lo, hi) exactly."""
+    return [(t0, min(hi, t0 + block)) for t0 in range(lo, hi, block)]
+
+
 def decode_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales, codebook,
                      sign, softmax_scale, window, softcap, num_kv_heads, head_dim,
-                     seqs=None, kv_heads=None, chunk=8192, alibi=None):
+                     seqs=None, kv_heads=None, chunk=KEY_BLOCK, alibi=None):
     """out[b, h] = softmax(scale * q_h K^T) V over the attended keys of sequence b, fp64.
 
     q: bf16 bits [B, Hq, D]; caches in the paged layout; context_lens / window int [B]
     (window None -> no window); alibi: per-query-head slopes [Hq] or None.  Rows of sequences
     with context length 0 are zero.
     ``seqs`` / ``kv_heads`` restrict the work to a sample (other rows are left NaN).
-    The keys are processed ``chunk`` tokens at a time and merged with the LSE rule, which is
-    the same sum in another order (bounded memory for long contexts).
+    Keys are gathered ``chunk`` at a time (``key_blocks``); a range of at most ``chunk`` keys is
+    one block and needs no merge, longer ranges are merged with the LSE rule.
     """
     q = np.asarray(q)
     B, Hq, D = q.shape
@@ -282,16 +296,18 @@ def decode_attention(q, k_cache, v_cache, block_table, context_lens, fmt, scales
                 continue
             qr = _q_rows(q, b, hk * g, g)
             parts = []
-            for t0 in range(lo, hi, chunk):
-                t1 = min(hi, t0 + chunk)
+            for t0, t1 in key_blocks(lo, hi, chunk):
                 kk = gather_kv(fmt, "k", k_cache, block_table[b], hk, t0, t1, D, scales=scales,
                                codebook=codebook, sign=sign)
                 vv = gather_kv(fmt, "v", v_cache, block_table[b], hk, t0, t1, D, scales=scales,
                                codebook=codebook, sign=sign)
                 bias = None if alibi is None else alibi_bias(np.asarray(alibi)[rows], L, t0, t1)
                 parts.append(attend(qr, kk, vv, softmax_scale, softcap, bias))
-            ms, ls, os_ = zip(*parts)
-            out[b, rows] = lse_merge(ms, ls, os_)
+            if len(parts) == 1:
+                out[b, rows] = parts[0][2]
+            else:
+                ms, ls, os_ = zip(*parts)
+                out[b, rows] = lse_merge(ms, ls, os_)
     return out
 
 
