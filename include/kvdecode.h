@@ -215,14 +215,45 @@ int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cac
  * sequence `seq`, KV head `kv_head`, gathered through the block table, written as fp32
  * [n_tokens][D] in the storage domain: BF16 widened; FP8 E4M3FN(code) * scale rounded to fp32;
  * Turbo norm * codebook[index] rounded to fp32 (still rotated).  is_v selects V (1) or K (0).
- * `scales`, `codebook` as for kvd_decode_attn_paged.  Uses the attention kernel's page
- * addressing, index unpacking and FP8 decode (the attention kernel itself feeds the codebook
- * levels to its matrix cores as fp16 hi + lo pairs).  Tokens must lie in
- * [0, 16 * max_blocks_per_seq). */
+ * `scales`, `codebook` as for kvd_decode_attn_paged.  A separate gather kernel forms these
+ * values (one thread per element, its own page addressing and index extraction; it shares the
+ * FP8 -> bf16 decode and the 3-bit field selection with the attention kernel).  The attention
+ * kernel never forms norm * codebook[index]: it factors the norm out and feeds the levels to
+ * its matrix cores as fp16 hi + lo pairs; kvd_dequant_operands exports those operands.  Tokens
+ * must lie in [0, 16 * max_blocks_per_seq). */
 int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cache,
                        const float* scales, const float* codebook, const int32_t* block_table,
                        int32_t seq, int32_t kv_head, int32_t token_begin, int32_t n_tokens,
                        float* out, void* stream);
+
+/* Test export: the matrix-core operands the partition kernel forms from the cache, produced by
+ * the partition kernel's own load (lane map, 16-byte loads), FP8 decode and codebook pair-table
+ * code, for page pairs pair_begin .. pair_begin + n_pairs - 1 of sequence `seq`, KV head
+ * `kv_head` (pair k = the sequence's pages 2k and 2k + 1; requires
+ * 2 * (pair_begin + n_pairs) <= max_blocks_per_seq).  Arguments as for kvd_decode_attn_paged.
+ * out: uint32 [n_pairs][64][head_dim + 16], one record per lane l of a 64-lane wavefront, with
+ * n = l % 16, j = l / 16.  The lane's tokens (page 0/1 of the pair, slot):
+ *   QK tile X: (n / 8, 8 ((n / 4) % 2) + n % 4); tile Y: four slots later;
+ *   softmax / PV: (j / 2, 8 (j % 2) + e), e = 0..7.
+ * Words [16 s, 16 s + 16), s = 0 .. D/32 - 1: QK step s operands x0, x1 (tile X), y0, y1 (Y), 4
+ *   words each, covering head elements
+ *     BF16: d = 32 s + 8 j + e;  FP8 / Turbo8 K: d = 64 (s / 2) + 16 j + 8 (s % 2) + e;
+ *     Turbo4/3 K: d = 32 j + 8 s + e   (e = 0..7).
+ *   BF16 / FP8 / Turbo8 K: x0 = the eight values as bf16 (FP8 exact: E4M3FN(code), unscaled),
+ *   x1 = 0.  Turbo4/3 K: x0 = fp16 [h0 h1 l0 l1 h2 h3 l2 l3], x1 = the same for e = 4..7,
+ *   with (h, l) = (fp16(c), fp16(c - h)) of c = codebook level * 2^-E, 2^-E the power of two
+ *   that puts the largest K level magnitude in [0.5, 1).
+ * Words [D/2 + 8 t, D/2 + 8 t + 8), t = 0 .. D/16 - 1: PV tile t operands v0, v1 for head
+ *   element d = 16 t + n and the lane's eight softmax tokens e: BF16 / FP8 v0 = bf16 values,
+ *   v1 = 0; codebook V: v0 = fp16 [h0 h1 l0 l1 h2 h3 l2 l3] of tokens 0..3, v1 of 4..7 (V
+ *   levels, normaliser of the V levels).
+ * Words [D, D + 16): fp32 K norms of the eight softmax tokens (Turbo4/3; else 0), then their
+ *   V norms (codebook V; else 0).
+ * A pair with a block-table entry outside the pool gets all-ones records. */
+int kvd_dequant_operands(const kvd_dims* dims, int fmt, const void* k_cache,
+                         const void* v_cache, const float* scales, const float* codebook,
+                         const int32_t* block_table, int32_t seq, int32_t kv_head,
+                         int32_t pair_begin, int32_t n_pairs, uint32_t* out, void* stream);
 
 /* KV append (quantize-on-write): stores n_new new tokens of every sequence in the paged cache,
  * in the layout above, so the decode entry points read them back.  Sources: the attention.rs

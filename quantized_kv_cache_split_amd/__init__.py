@@ -14,7 +14,7 @@ import os
 
 __all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "TURBO8", "FORMATS",
            "workspace_bytes", "decode_attn_paged", "decode_partitions", "reduce_partitions",
-           "dequant_gather", "append_kv", "status_str", "library_path", "load",
+           "dequant_gather", "dequant_operands", "append_kv", "status_str", "library_path", "load",
            "hip_runtimes_mapped"]
 
 BF16, FP8_E4M3, TURBO4, TURBO3, TURBO8 = 0, 1, 2, 3, 4
@@ -119,6 +119,12 @@ def load() -> ctypes.CDLL:
                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_void_p]
         lib.kvd_dequant_gather.restype = ctypes.c_int
+        lib.kvd_dequant_operands.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p]
+        lib.kvd_dequant_operands.restype = ctypes.c_int
         lib.kvd_append_kv.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
@@ -207,6 +213,20 @@ def dequant_gather(dims, fmt, is_v, cache, scales, codebook, block_table, seq, k
                                    _stream(stream))
     if st != 0:
         raise KvdError(st, "kvd_dequant_gather")
+    return out
+
+
+def dequant_operands(dims, fmt, k_cache, v_cache, scales, codebook, block_table, seq, kv_head,
+                     pair_begin, n_pairs, out, stream=None):
+    """The partition kernel's matrix-core operands of page pairs [pair_begin, pair_begin +
+    n_pairs) of one (sequence, KV head) -> out uint32 [n_pairs][64][head_dim + 16]
+    (kvd_dequant_operands)."""
+    st = load().kvd_dequant_operands(ctypes.byref(dims), _fmt(fmt), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(scales), _ptr(codebook), _ptr(block_table), int(seq),
+                                     int(kv_head), int(pair_begin), int(n_pairs), _ptr(out),
+                                     _stream(stream))
+    if st != 0:
+        raise KvdError(st, "kvd_dequant_operands")
     return out
 
 

@@ -312,6 +312,51 @@ int kvd_dequant_gather(const kvd_dims* d, int fmt, int is_v, const void* cache,
                                                                                  : KVD_ERR_HIP;
 }
 
+int kvd_dequant_operands(const kvd_dims* d, int fmt, const void* k_cache, const void* v_cache,
+                         const float* scales, const float* codebook, const int32_t* block_table,
+                         int32_t seq, int32_t kv_head, int32_t pair_begin, int32_t n_pairs,
+                         uint32_t* out, void* stream) {
+    int st = check_dims(d, fmt);
+    if (st != KVD_OK) return st;
+    if (!k_cache || !v_cache || !block_table || !out) return KVD_ERR_NULL;
+    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (fmt >= KVD_TURBO4 && !codebook) return KVD_ERR_NULL;
+    if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+        !aligned(block_table, 4) || (scales && !aligned(scales, 16)) ||
+        (codebook && !aligned(codebook, 4)))
+        return KVD_ERR_ALIGN;
+    if (seq < 0 || seq >= d->num_seqs || kv_head < 0 || kv_head >= d->num_kv_heads ||
+        pair_begin < 0 || n_pairs < 0 ||
+        2 * ((int64_t)pair_begin + n_pairs) > (int64_t)d->max_blocks_per_seq)
+        return KVD_ERR_SHAPE;
+    if (n_pairs == 0) return KVD_OK;
+    kvd::OperandParams op{};
+    LaunchParams& p = op.lp;
+    p.k = static_cast<const uint8_t*>(k_cache);
+    p.v = static_cast<const uint8_t*>(v_cache);
+    p.bt = block_table;
+    p.scales = scales;
+    p.codebook = codebook;
+    p.k_chunk = k_chunk_bytes(fmt, d->head_dim);
+    p.v_chunk = v_chunk_bytes(fmt, d->head_dim);
+    p.B = d->num_seqs;
+    p.Hq = d->num_q_heads;
+    p.Hkv = d->num_kv_heads;
+    p.g = d->num_q_heads / d->num_kv_heads;
+    p.D = d->head_dim;
+    p.max_blocks = d->max_blocks_per_seq;
+    p.pool = d->num_pool_blocks;
+    p.max_ctx = d->max_context_len;
+    p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
+    op.out = out;
+    op.seq = seq;
+    op.kv_head = kv_head;
+    op.pair0 = pair_begin;
+    op.npairs = n_pairs;
+    return kvd::launch_operands(fmt, op, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? KVD_OK : KVD_ERR_HIP;
+}
+
 int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v_new,
                   const int32_t* block_table, const int32_t* positions, int32_t n_new,
                   void* k_cache, void* v_cache, float* scales, const float* codebook,

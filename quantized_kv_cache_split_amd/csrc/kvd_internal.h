@@ -75,6 +75,18 @@ struct GatherParams {
     int32_t fmt, is_v, Hkv, D, max_blocks, pool, seq, kv_head, t0, n, kbits;
 };
 
+// Arguments of the operand export: the partition kernel's load and dequantisation code run on
+// page pairs pair0 .. pair0 + npairs - 1 of one (sequence, KV head); lp carries the cache,
+// scales, codebook, block table and sizes exactly as a decode launch does.
+struct OperandParams {
+    LaunchParams lp;
+    uint32_t* out;            // [npairs][64 lanes][D + 16] words
+    int32_t seq, kv_head, pair0, npairs;
+};
+// 32-bit words the operand export writes per (pair, lane): QK operands (x0 x1 y0 y1 per step,
+// D / 2 words), PV operands (v0 v1 per tile, D / 2 words), then 16 norm words.
+constexpr int operand_words(int d) { return d + 16; }
+
 // Arguments of the KV append (quantize-on-write) kernel.
 struct AppendParams {
     const float* k_new;       // [B][T][Hkv][D] fp32
@@ -107,6 +119,7 @@ inline hipError_t launch_kernel(void (*kernel)(Params), dim3 grid, dim3 block, h
 hipError_t launch_partitions(int fmt, bool wide, const LaunchParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
+hipError_t launch_operands(int fmt, const OperandParams& p, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace kvd

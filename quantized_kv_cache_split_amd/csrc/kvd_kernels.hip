@@ -330,6 +330,126 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 }
 
 // ------------------------------------------------------------------------------------------
+// in-register dequantisation: MFMA operands of one page pair
+// ------------------------------------------------------------------------------------------
+// The A operands of QK step s (head elements 32s .. 32s + 31 in the order of the query operand)
+// for the pair's two 16-token tiles X and Y.  BF16 / FP8 K (also Turbo8 K): one bf16x8 operand
+// per tile in x0 / y0 (FP8 -> bf16 is exact); x1 / y1 are zero.  Codebook K: two interleaved
+// fp16 hi / lo operands per tile from the K pair table (x0 = elements 0..3, x1 = 4..7 of the
+// lane's eight).
+template <int FMT, int D>
+__device__ __forceinline__ void k_operands(const PairRaw<FMT, D>& r, int s, const char* lds,
+                                           uint32_t kbase, u32x4& x0, u32x4& x1, u32x4& y0,
+                                           u32x4& y1) {
+    x1 = y1 = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (FMT == KVD_BF16) {
+        x0 = r.kx[s];
+        y0 = r.ky[s];
+    } else if constexpr (k_fp8<FMT>()) {
+        const int i = s / 2, h = s % 2;   // codes 8h .. 8h + 7 of x-vector 4i + j
+        const u32x2 ax0 = fp8x4_to_bf16(r.kx[i][2 * h]), ax1 = fp8x4_to_bf16(r.kx[i][2 * h + 1]);
+        const u32x2 ay0 = fp8x4_to_bf16(r.ky[i][2 * h]), ay1 = fp8x4_to_bf16(r.ky[i][2 * h + 1]);
+        x0 = u32x4{ax0[0], ax0[1], ax1[0], ax1[1]};
+        y0 = u32x4{ay0[0], ay0[1], ay1[0], ay1[1]};
+    } else if constexpr (FMT == KVD_TURBO4) {
+        lut_nib8(lds, kbase, r.kx[s], x0, x1);
+        lut_nib8(lds, kbase, r.ky[s], y0, y1);
+    } else {
+        lut_tri8(lds, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
+        lut_tri8(lds, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
+    }
+}
+
+// The A operand(s) of PV tile t (head elements 16t + n, the lane's eight tokens as k-slots).
+// BF16 / FP8 V: one bf16x8 operand in v0 (v1 zero).  Codebook V: two interleaved fp16 hi / lo
+// operands from the V pair table (v0 = tokens 0..3, v1 = 4..7).
+template <int FMT, int D>
+__device__ __forceinline__ void v_operands(const PairRaw<FMT, D>& r, int t, const char* lds,
+                                           uint32_t vbase, u32x4& v0, u32x4& v1) {
+    if constexpr (FMT == KVD_BF16) {
+        v0 = r.v[t];
+        v1 = u32x4{0u, 0u, 0u, 0u};
+    } else if constexpr (FMT == KVD_FP8_E4M3) {
+        const u32x2 a0 = fp8x4_to_bf16(r.v[t][0]), a1 = fp8x4_to_bf16(r.v[t][1]);
+        v0 = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        v1 = u32x4{0u, 0u, 0u, 0u};
+    } else {
+        lut_nib8(lds, vbase, r.v[t], v0, v1);
+    }
+}
+
+// Codebook levels a workgroup's tables are built from: the two levels of this thread's table
+// entry e = (tid / 2) % 256 (entry i0 + n i1 holds levels i0 and i1; n = 2^kbits for K, 16 for
+// V) and the largest level magnitudes.  The array holds 2^kbits K levels then 16 V levels
+// (Turbo8: the 16 V levels).
+struct Levels {
+    float k0, k1, v0, v1, kmax, vmax;
+};
+template <int FMT>
+__device__ __forceinline__ Levels load_levels(const float* codebook, int kbits, int tid) {
+    constexpr bool kKcb = k_codebook<FMT>();
+    Levels lv{0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    const int kl = kKcb ? 1 << kbits : 0;
+    if constexpr (kKcb) {
+        // a fixed trip count (one scalar load); the array holds kl + 16 >= 24 floats
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float c = fabsf(codebook[i]);
+            lv.kmax = i < kl ? fmaxf(lv.kmax, c) : lv.kmax;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lv.vmax = fmaxf(lv.vmax, fabsf(codebook[kl + i]));
+    const int e = (tid >> 1) & 255;
+    if constexpr (kKcb) {
+        lv.k0 = codebook[e % kl];
+        lv.k1 = codebook[(e / kl) % kl];
+    }
+    lv.v0 = codebook[kl + (e & 15)];
+    lv.v1 = codebook[kl + (e >> 4)];
+    return lv;
+}
+
+// Fills the conflict-free pair tables (K table at LDS byte 0 for codebook K, then the V table)
+// with the levels scaled by the power-of-two normalisers ksc / vsc.  512 threads: thread t
+// fills half of the kLutCopies copies of entry t / 2 of every table.  The copy order is
+// staggered by entry: in each store the 16 lanes of a pass write 16 different 16-byte bank
+// groups (entries are 256 bytes apart, so the same copy of every entry would sit in the same
+// banks: 8-way conflicts).
+template <int FMT>
+__device__ __forceinline__ void fill_tables(u32x4* lut, int tid, const Levels& lv, float ksc,
+                                            float vsc) {
+    constexpr bool kKcb = k_codebook<FMT>();
+    constexpr int kTableVecs = 256 * kLutCopies / 2;   // u32x4 per table
+    const int e = tid >> 1, c0 = (tid & 1) * (kLutCopies / 2);
+    uint32_t h, l;
+    u32x4 kv = {0u, 0u, 0u, 0u};
+    if constexpr (kKcb) {
+        f16_hilo(lv.k0 * ksc, lv.k1 * ksc, h, l);
+        kv = u32x4{h, l, h, l};
+    }
+    f16_hilo(lv.v0 * vsc, lv.v1 * vsc, h, l);
+    const u32x4 vv = {h, l, h, l};
+#pragma unroll
+    for (int c = 0; c < kLutCopies / 2; c += 2) {
+        const int cc = (c + 2 * e) & (kLutCopies / 2 - 1);
+        if constexpr (kKcb) lut[(e * kLutCopies + c0 + cc) / 2] = kv;
+        lut[(kKcb ? kTableVecs : 0) + (e * kLutCopies + c0 + cc) / 2] = vv;
+    }
+}
+
+__device__ __forceinline__ LaneMap lane_map(int lane) {
+    LaneMap ln;
+    ln.n = lane & 15;
+    ln.j = lane >> 4;
+    ln.a_sel = ln.n >> 3;
+    ln.a_pos = 8 * ((ln.n >> 2) & 1) + (ln.n & 3);
+    ln.v_sel = ln.j >> 1;
+    ln.v_pos0 = 8 * (ln.j & 1);
+    return ln;
+}
+
+// ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
 // Grid ceil(P / (4 R)) * Hkv * B (1-D), 4 waves, R = p.run partitions per wave.  For a split
@@ -433,33 +553,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // sequence.  They go out together here, ahead of the first wait on the sequence's length,
     // so the round trips overlap (issued one after another they took ~5 of the ~8 us
     // start-up).
-    [[maybe_unused]] float cb_k0 = 0.0f, cb_k1 = 0.0f, cb_v0 = 0.0f, cb_v1 = 0.0f;
-    [[maybe_unused]] float kmax = 0.0f, vmax = 0.0f;
+    [[maybe_unused]] Levels lv{0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // codebook K: wave w rotates query rows w, w + kW, ... (lane l holds elements 2l, 2l + 1)
     constexpr int kQRows = kKcb ? (kMaxGroup + kW - 1) / kW : 1;
     [[maybe_unused]] uint32_t q_raw[kQRows];
     [[maybe_unused]] float q_s0 = 0.0f, q_s1 = 0.0f;
-    if constexpr (kVcb) {
-        // levels: 2^kbits K levels then 16 V levels, or (Turbo8) 16 V levels
-        const int kl = kKcb ? 1 << p.kbits : 0;
-        if constexpr (kKcb) {
-            // a fixed trip count (one scalar load); the array holds kl + 16 >= 24 floats
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float c = fabsf(p.codebook[i]);
-                kmax = i < kl ? fmaxf(kmax, c) : kmax;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vmax = fmaxf(vmax, fabsf(p.codebook[kl + i]));
-        const int e = (tid >> 1) & 255;   // this thread's table entry (index byte)
-        if constexpr (kKcb) {
-            cb_k0 = p.codebook[e % kl];
-            cb_k1 = p.codebook[(e / kl) % kl];
-        }
-        cb_v0 = p.codebook[kl + (e & 15)];
-        cb_v1 = p.codebook[kl + (e >> 4)];
-    }
+    if constexpr (kVcb) lv = load_levels<FMT>(p.codebook, p.kbits, tid);
     if constexpr (kKcb) {
         static_assert(D == 128, "two query elements per lane");
         q_s0 = p.sign[2 * lane];
@@ -499,13 +598,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     }
     const bool live = lo < hi;
 
-    LaneMap ln;
-    ln.n = lane & 15;
-    ln.j = lane >> 4;
-    ln.a_sel = ln.n >> 3;
-    ln.a_pos = 8 * ((ln.n >> 2) & 1) + (ln.n & 3);
-    ln.v_sel = ln.j >> 1;
-    ln.v_pos0 = 8 * (ln.j & 1);
+    const LaneMap ln = lane_map(lane);
     const int n = ln.n, j = ln.j;
     const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;   // copy of this lane
     const uint32_t kbase = lut_lane;                                      // K table (byte 0)
@@ -534,31 +627,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     if constexpr (kVcb) {
         // codebook pair tables (levels scaled by a power of two so the largest magnitude is in
         // [0.5, 1)), from the levels loaded at the start
-        ksc = pow2_normaliser(kmax);
-        const float vsc = pow2_normaliser(vmax);
-        {
-            // 512 threads: thread t fills half the copies of entry t / 2 of every table
-            static_assert(kThr == 2 * 256, "one thread pair per table entry");
-            const int e = tid >> 1, c0 = (tid & 1) * (kLutCopies / 2);
-            uint32_t h, l;
-            u32x4 kv = {0u, 0u, 0u, 0u};
-            if constexpr (kKcb) {
-                f16_hilo(cb_k0 * ksc, cb_k1 * ksc, h, l);
-                kv = u32x4{h, l, h, l};
-            }
-            f16_hilo(cb_v0 * vsc, cb_v1 * vsc, h, l);
-            const u32x4 vv = {h, l, h, l};
-            // Copy order staggered by entry: in each store the 16 lanes of a pass write 16
-            // different 16-byte bank groups (entries are 256 bytes apart, so the same copy of
-            // every entry would sit in the same banks: 8-way conflicts, ~2M conflict cycles
-            // per Turbo4 launch).
-#pragma unroll
-            for (int c = 0; c < kLutCopies / 2; c += 2) {
-                const int cc = (c + 2 * e) & (kLutCopies / 2 - 1);
-                if constexpr (kKcb) lds.u.lut[0][(e * kLutCopies + c0 + cc) / 2] = kv;
-                lds.u.lut[kTables - 1][(e * kLutCopies + c0 + cc) / 2] = vv;
-            }
-        }
+        ksc = pow2_normaliser(lv.kmax);
+        const float vsc = pow2_normaliser(lv.vmax);
+        static_assert(kThr == 2 * 256, "one thread pair per table entry");
+        fill_tables<FMT>(&lds.u.lut[0][0], tid, lv, ksc, vsc);
         oscale = 1.0f / vsc;
         // the tables are complete before any wave's walk reads them (codebook K: the query
         // rotation's barriers below do the same)
@@ -673,32 +745,19 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         sx = f32x4{0.f, 0.f, 0.f, 0.f};
         sy = f32x4{0.f, 0.f, 0.f, 0.f};
         f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FMT == KVD_BF16) {
+        if constexpr (!kKcb) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                sx = mfma_bf16(r.kx[s], qop[s], sx);
-                sy = mfma_bf16(r.ky[s], qop[s], sy);
-            }
-        } else if constexpr (k_fp8<FMT>()) {
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const int i = s / 2, h = s % 2;
-                const u32x2 ax0 = fp8x4_to_bf16(r.kx[i][2 * h]), ax1 = fp8x4_to_bf16(r.kx[i][2 * h + 1]);
-                const u32x2 ay0 = fp8x4_to_bf16(r.ky[i][2 * h]), ay1 = fp8x4_to_bf16(r.ky[i][2 * h + 1]);
-                sx = mfma_bf16(u32x4{ax0[0], ax0[1], ax1[0], ax1[1]}, qop[s], sx);
-                sy = mfma_bf16(u32x4{ay0[0], ay0[1], ay1[0], ay1[1]}, qop[s], sy);
+                u32x4 x0, x1, y0, y1;
+                k_operands<FMT, D>(r, s, lds_bytes, kbase, x0, x1, y0, y1);
+                sx = mfma_bf16(x0, qop[s], sx);
+                sy = mfma_bf16(y0, qop[s], sy);
             }
         } else {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 u32x4 x0, x1, y0, y1;
-                if constexpr (FMT == KVD_TURBO4) {
-                    lut_nib8(lds_bytes, kbase, r.kx[s], x0, x1);
-                    lut_nib8(lds_bytes, kbase, r.ky[s], y0, y1);
-                } else {
-                    lut_tri8(lds_bytes, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
-                    lut_tri8(lds_bytes, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
-                }
+                k_operands<FMT, D>(r, s, lds_bytes, kbase, x0, x1, y0, y1);
                 // two accumulator chains per tile halve the dependent-MFMA latency
                 sx = mfma_f16(x0, qdup[s][0], sx);     // (k hi + k lo) * q hi
                 sx2 = mfma_f16(x1, qdup[s][1], sx2);
@@ -848,7 +907,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
                 u32x4 v0, v1;
-                lut_nib8(lds_bytes, vbase, r.v[t], v0, v1);
+                v_operands<FMT, D>(r, t, lds_bytes, vbase, v0, v1);
                 oacc[t] = mfma_f16(v0, pb0, oacc[t]);
                 oacc[t] = mfma_f16(v1, pb1, oacc[t]);
             }
@@ -865,13 +924,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             }
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
-                u32x4 vop;
-                if constexpr (FMT == KVD_BF16) {
-                    vop = r.v[t];
-                } else {
-                    const u32x2 a0 = fp8x4_to_bf16(r.v[t][0]), a1 = fp8x4_to_bf16(r.v[t][1]);
-                    vop = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                }
+                u32x4 vop, vunused;
+                v_operands<FMT, D>(r, t, lds_bytes, vbase, vop, vunused);
                 oacc[t] = mfma_bf16(vop, phi, oacc[t]);
                 oacc[t] = mfma_bf16(vop, plo, oacc[t]);
             }
@@ -1199,6 +1253,73 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     p.out[i] = val;
 }
 
+// ------------------------------------------------------------------------------------------
+// test export: the partition kernel's own MFMA operands of page pairs
+// ------------------------------------------------------------------------------------------
+// 512 threads (eight waves), the same table build as the partition kernel's codebook formats;
+// wave w of workgroup x takes page pair pair0 + 8x + w of one (sequence, KV head) (pages 2k and
+// 2k + 1 of the sequence), loads it with load_pair and the lane map of the partition kernel and
+// forms the QK and PV operands with k_operands / v_operands.  Record of lane l (D + 16 words):
+// for each QK step s: x0, x1, y0, y1; for each PV tile t: v0, v1; then K norms (8 floats of the
+// lane's eight softmax tokens), V norms (8), zero where the format has none.  A pair whose block
+// table entry lies outside the pool writes all-ones records.
+template <int FMT, int D>
+__global__ __launch_bounds__(512) void operand_kernel(const OperandParams op) {
+    constexpr bool kKcb = k_codebook<FMT>();
+    constexpr bool kVcb = v_codebook<FMT>();
+    constexpr int kTables = kKcb ? 2 : 1;
+    constexpr int KS = D / 32, VT = D / 16, W = operand_words(D);
+    __shared__ u32x4 lut[kVcb ? kTables * 256 * kLutCopies / 2 : 1];
+    const LaunchParams& p = op.lp;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const char* const lds_bytes = reinterpret_cast<const char*>(lut);
+    if constexpr (kVcb) {
+        const Levels lv = load_levels<FMT>(p.codebook, p.kbits, tid);
+        fill_tables<FMT>(lut, tid, lv, pow2_normaliser(lv.kmax), pow2_normaliser(lv.vmax));
+        __syncthreads();
+    }
+    const int k = blockIdx.x * 8 + wave;
+    if (k >= op.npairs) return;
+    const int pair = op.pair0 + k;
+    const LaneMap ln = lane_map(lane);
+    const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;
+    const uint32_t kbase = lut_lane, vbase = lut_lane | (kKcb ? 0x10000u : 0u);
+    uint32_t* rec = op.out + ((size_t)k * 64 + lane) * W;
+    const int32_t* btrow = p.bt + (size_t)op.seq * p.max_blocks;
+    const int pa = btrow[2 * pair], pb = btrow[2 * pair + 1];
+    if (pa < 0 || pa >= p.pool || pb < 0 || pb >= p.pool) {
+        for (int i = 0; i < W; ++i) rec[i] = 0xFFFFFFFFu;
+        return;
+    }
+    PairRaw<FMT, D> r;
+    load_pair<FMT, D>(r, p, ln, (size_t)pa * p.Hkv + op.kv_head, (size_t)pb * p.Hkv + op.kv_head);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        u32x4 x[4];
+        k_operands<FMT, D>(r, s, lds_bytes, kbase, x[0], x[1], x[2], x[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(rec + 16 * s + 4 * i) = x[i];
+    }
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+        u32x4 v0, v1;
+        v_operands<FMT, D>(r, t, lds_bytes, vbase, v0, v1);
+        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t) = v0;
+        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t + 4) = v1;
+    }
+    f32x4 nrm[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if constexpr (kKcb) { nrm[0] = r.kn0; nrm[1] = r.kn1; }
+    if constexpr (kVcb) { nrm[2] = r.vn0; nrm[3] = r.vn1; }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4*>(rec + D + 4 * i) = nrm[i];
+}
+
+template <int FMT, int D>
+hipError_t launch_operands_t(const OperandParams& p, hipStream_t s) {
+    return launch_kernel(operand_kernel<FMT, D>, dim3((p.npairs + 7) / 8), dim3(512), s, p);
+}
+
 // Pairs in flight per wave.  With every wave of the chip streaming random pages, fewer
 // outstanding requests read HBM more efficiently.  FP8 32K partition kernel, A/B on one GPU:
 // 195.6 us at one pair in flight (8 KB per wave) against 204.0 us at two; three pairs ran
@@ -1254,6 +1375,18 @@ hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s) {
         case KVD_TURBO4: return launch_reduce_t<KVD_TURBO4, 128>(p, s);
         case KVD_TURBO8: return launch_reduce_t<KVD_TURBO8, 128>(p, s);
         default: return launch_reduce_t<KVD_TURBO3, 128>(p, s);
+    }
+}
+
+hipError_t launch_operands(int fmt, const OperandParams& p, hipStream_t s) {
+    switch (fmt) {
+        case KVD_BF16: return p.lp.D == 64 ? launch_operands_t<KVD_BF16, 64>(p, s)
+                                           : launch_operands_t<KVD_BF16, 128>(p, s);
+        case KVD_FP8_E4M3: return p.lp.D == 64 ? launch_operands_t<KVD_FP8_E4M3, 64>(p, s)
+                                               : launch_operands_t<KVD_FP8_E4M3, 128>(p, s);
+        case KVD_TURBO4: return launch_operands_t<KVD_TURBO4, 128>(p, s);
+        case KVD_TURBO8: return launch_operands_t<KVD_TURBO8, 128>(p, s);
+        default: return launch_operands_t<KVD_TURBO3, 128>(p, s);
     }
 }
 
