@@ -182,6 +182,30 @@ int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cac
                           float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* Largest partition workspace (bytes) kvd_decode_attn_paged_noalloc can use. */
+#define KVD_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  kvd_decode_attn_paged without the workspace
+ * arguments: the partition triples go to a device array inside the library,
+ * KVD_NOALLOC_WORKSPACE_BYTES on each GPU the library runs on, held from the library's load
+ * until the process ends.  The first call on a GPU looks up that GPU's copy of the array
+ * (hipGetSymbolAddress, with the GPU current); no call allocates or frees memory.
+ * Errors: as kvd_decode_attn_paged; KVD_ERR_WORKSPACE when kvd_workspace_bytes(dims) exceeds
+ * KVD_NOALLOC_WORKSPACE_BYTES (each (query row, partition) triple takes (head_dim + 2) * 4
+ * bytes: the array holds about 258,000 of them at head_dim 128, e.g. 16 sequences x 64 query
+ * heads at 32K context use 65,536); KVD_ERR_HIP when the array's address cannot be obtained.
+ * All calls on one GPU share its array, which keeps the last call's contents.  Nothing in it
+ * needs to start at zero (each call writes every triple it reads back), but calls that overlap
+ * in time on one GPU -- on different streams, or from host threads without ordering -- race on
+ * it and give wrong results; calls enqueued on one stream are ordered and safe. */
+int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  const int32_t* context_lens, int fmt, const float* scales,
+                                  const float* codebook, const float* sign_pattern,
+                                  float softmax_scale, const int32_t* window, float softcap,
+                                  const float* alibi_slopes, float* out, void* stream);
+
 /* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
  * partitions_per_wave partitions, four wavefronts per workgroup (eight for the Turbo
  * formats).  For a split sequence, partition p covers tokens

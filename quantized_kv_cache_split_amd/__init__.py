@@ -13,7 +13,7 @@ import ctypes
 import os
 
 __all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "TURBO8", "FORMATS",
-           "workspace_bytes", "decode_attn_paged", "decode_partitions", "reduce_partitions",
+           "workspace_bytes", "decode_attn_paged", "decode_attn_paged_noalloc", "decode_partitions", "reduce_partitions",
            "dequant_gather", "dequant_operands", "append_kv", "status_str", "library_path", "load",
            "hip_runtimes_mapped"]
 
@@ -113,6 +113,8 @@ def load() -> ctypes.CDLL:
             f = getattr(lib, name)
             f.argtypes = _ATTN_ARGS
             f.restype = ctypes.c_int
+        lib.kvd_decode_attn_paged_noalloc.argtypes = _ATTN_ARGS[:15] + [ctypes.c_void_p]
+        lib.kvd_decode_attn_paged_noalloc.restype = ctypes.c_int
         lib.kvd_dequant_gather.argtypes = [ctypes.POINTER(Dims), ctypes.c_int, ctypes.c_int,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
@@ -184,6 +186,25 @@ def decode_attn_paged(dims, q, k_cache, v_cache, block_table, context_lens, fmt,
     return _attn("kvd_decode_attn_paged", dims, q, k_cache, v_cache, block_table, context_lens,
                  fmt, scales, codebook, sign_pattern, softmax_scale, window, softcap, out,
                  workspace, stream, alibi_slopes)
+
+
+NOALLOC_WORKSPACE_BYTES = 128 << 20   # KVD_NOALLOC_WORKSPACE_BYTES
+
+
+def decode_attn_paged_noalloc(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,
+                              codebook, sign_pattern, softmax_scale, window, softcap, out,
+                              stream=None, alibi_slopes=None):
+    """Both phases with the library's own static workspace (no allocation); see
+    kvd_decode_attn_paged_noalloc in include/kvdecode.h."""
+    name = "kvd_decode_attn_paged_noalloc"
+    st = load().kvd_decode_attn_paged_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(context_lens), _fmt(fmt), _ptr(scales), _ptr(codebook), _ptr(sign_pattern),
+        float(softmax_scale), _ptr(window), float(softcap), _ptr(alibi_slopes), _ptr(out),
+        _stream(stream))
+    if st != 0:
+        raise KvdError(st, name)
+    return out
 
 
 def decode_partitions(dims, q, k_cache, v_cache, block_table, context_lens, fmt, scales,

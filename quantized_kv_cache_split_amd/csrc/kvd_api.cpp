@@ -254,6 +254,21 @@ int kvd_decode_attn_paged(const kvd_dims* d, const void* q, const void* k, const
                softmax_scale, window, softcap, alibi, out, ws, ws_bytes, stream);
 }
 
+int kvd_decode_attn_paged_noalloc(const kvd_dims* d, const void* q, const void* k, const void* v,
+                                  const int32_t* bt, const int32_t* ctx, int fmt,
+                                  const float* scales, const float* codebook, const float* sign,
+                                  float softmax_scale, const int32_t* window, float softcap,
+                                  const float* alibi, float* out, void* stream) {
+    int st = check_dims(d, fmt);
+    if (st != KVD_OK) return st;
+    if (make_plan(d).bytes > kvd::kNoAllocWorkspaceBytes) return KVD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (kvd::noalloc_workspace(&ws) != hipSuccess) return KVD_ERR_HIP;
+    return run(kPhase1 | kPhase2, d, q, k, v, bt, ctx, fmt, scales, codebook, sign,
+               softmax_scale, window, softcap, alibi, out, ws, kvd::kNoAllocWorkspaceBytes,
+               stream);
+}
+
 int kvd_decode_partitions(const kvd_dims* d, const void* q, const void* k, const void* v,
                           const int32_t* bt, const int32_t* ctx, int fmt, const float* scales,
                           const float* codebook, const float* sign, float softmax_scale,

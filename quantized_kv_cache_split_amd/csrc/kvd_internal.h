@@ -33,6 +33,10 @@ constexpr int stage_rows(int d, bool wide) { return (wide ? 8192 : 4096) / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };
 
+// Partition workspace of the allocation-free entry point: a device array inside the library,
+// one per GPU (KVD_NOALLOC_WORKSPACE_BYTES in include/kvdecode.h).
+constexpr size_t kNoAllocWorkspaceBytes = (size_t)128 << 20;
+
 // Everything a kernel needs, passed by value as the kernel argument.
 struct LaunchParams {
     const uint16_t* q;        // bf16 [B][Hq][D]
@@ -120,6 +124,10 @@ hipError_t launch_partitions(int fmt, bool wide, const LaunchParams& p, dim3 gri
 hipError_t launch_reduce(int fmt, const LaunchParams& p, hipStream_t s);
 hipError_t launch_gather(const GatherParams& p, hipStream_t s);
 hipError_t launch_operands(int fmt, const OperandParams& p, hipStream_t s);
+
+// Device address of the library's static workspace array on the current device (looked up
+// with hipGetSymbolAddress on the first call per device, then cached).
+hipError_t noalloc_workspace(void** ptr);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 
 }  // namespace kvd

@@ -48,6 +48,7 @@
 #include <float.h>
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "kvd_internal.h"
@@ -1352,7 +1353,32 @@ hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {
     return launch_kernel(reduce_kernel<FMT, D>, dim3(p.Hq, p.B * p.nq), dim3(64), s, p);
 }
 
+// Workspace of the allocation-free entry point.  The host-side name `scratch` is a stand-in,
+// not a device address: host code uses only the pointer hipGetSymbolAddress returns for the
+// current device (each GPU holds its own copy of the array, at its own address).
+static __device__ __align__(256) unsigned char scratch[kNoAllocWorkspaceBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
 }  // namespace
+
+hipError_t noalloc_workspace(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // with the device current; two threads racing here store the same address
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
+}
 
 hipError_t launch_partitions(int fmt, bool wide, const LaunchParams& p, dim3 grid, hipStream_t s) {
     switch (fmt) {

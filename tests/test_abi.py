@@ -198,3 +198,21 @@ def test_build_script_runs_without_the_package():
     i = cmd.index("-packed-fp32-ops")
     assert cmd[i - 3:i] == ["-Xclang", "-target-feature", "-Xclang"]
     assert all(s in cmd for s in mod.SOURCES)
+
+
+def test_noalloc_rejects_oversized_workspace_before_any_hip_call():
+    """The allocation-free entry point refuses dims whose partition workspace exceeds its
+    static array, and bad shapes, on the host (no GPU needed: nothing is looked up or
+    launched)."""
+    lib = kvd.load()
+    na = lambda d, fmt=0: lib.kvd_decode_attn_paged_noalloc(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, fmt, FAKE, FAKE, FAKE, 0.1, None, 0.0,
+        None, FAKE, None)
+    big = dims(num_seqs=64, max_context_len=65536, max_blocks_per_seq=4096)   # 68M floats of o
+    assert kvd.workspace_bytes(big) > kvd.NOALLOC_WORKSPACE_BYTES
+    assert na(big) == -5
+    assert na(dims(head_dim=96)) == -2
+    assert na(dims(), fmt=9) == -3
+    assert kvd.NOALLOC_WORKSPACE_BYTES == 128 << 20
+    header = open(HEADER).read()
+    assert "#define KVD_NOALLOC_WORKSPACE_BYTES ((size_t)128 << 20)" in header
