@@ -127,17 +127,17 @@ typedef struct kvd_dims {
                                     >= 1024 tokens, else a single partition;
                                     > 0: always split at that many tokens (a multiple of 16);
                                     -1: never split */
-    int32_t partitions_per_wave; /* launch tuning, results do not depend on it: how many
-                                    consecutive partitions of a split sequence one wavefront
-                                    walks (it writes every partition's triple).  0: auto
+    int32_t partitions_per_wave; /* launch tuning: how many consecutive partitions of a split
+                                    sequence one wavefront walks; it writes one triple for the
+                                    run (results agree to rounding: the online softmax groups
+                                    its sums by run).  0: auto
                                     (about one wavefront per resident slot of the device when
                                     every sequence had max_context_len tokens, at most 4;
                                     single-query BF16 at head_dim 128 uses a layout with one
                                     workgroup per CU and runs of up to 8 when that covers
-                                    the device in one round); > 0: that many.  Capped at
-                                    4096 / (head_dim * rows), rows = min(16, n_q * Hq / Hkv),
-                                    and treated as 1 when the partition size is not a
-                                    multiple of 32.  Must be >= 0. */
+                                    the device in one round); > 0: that many.  Capped at the
+                                    partitions of max_context_len and treated as 1 when the
+                                    partition size is not a multiple of 32.  Must be >= 0. */
     int32_t queries_per_seq;     /* n_q: queries per sequence, a chunk at the last n_q positions
                                     (above); 0 or 1: single-query decode.  The n_q * Hq / Hkv
                                     query rows of a KV head share one pass over its pages per
@@ -145,7 +145,8 @@ typedef struct kvd_dims {
                                     num_seqs * n_q <= 65535. */
 } kvd_dims;
 
-/* Bytes of device workspace kvd_decode_attn_paged needs: the per-partition fp32 triples
+/* Bytes of device workspace kvd_decode_attn_paged needs: slots for per-partition fp32 triples
+ * (a run of partitions writes one, at the slot of its first partition)
  * m [B][n_q][Hq][P], l [B][n_q][Hq][P] and o [B][n_q][Hq][P][D], P = ceil(max_context_len /
  * partition size), each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
 size_t kvd_workspace_bytes(const kvd_dims* dims);
@@ -206,16 +207,17 @@ int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const voi
                                   float softmax_scale, const int32_t* window, float softcap,
                                   const float* alibi_slopes, float* out, void* stream);
 
-/* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of
- * partitions_per_wave partitions, four wavefronts per workgroup (eight for the Turbo
- * formats).  For a split sequence, partition p covers tokens
- * [max(lo, p*P), min(L, (p+1)*P)) and its triple goes to the
- * workspace at (b, i, h, p):  m = max_j z_j * log2(e)  (base-2 units),
- * l = sum_j exp(z_j - max z),  o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the
- * rotated domain for the Turbo formats; the keys j are those of the partition that query i
- * sees, and a query that sees none of them gets m = -inf, l = 0, o = 0.  Partitions outside
- * the sequence's range are not written.  Sequences that are not split get their final output
- * row written here. */
+/* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of R
+ * consecutive partitions (R = partitions_per_wave when > 0, capped as described there; else the
+ * automatic choice), four wavefronts per workgroup (eight for the Turbo formats).  For a split
+ * sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)); with p0 the first
+ * partition of the sequence's range, run k covers partitions p0 + kR .. p0 + kR + R - 1 (those
+ * inside the range) and its one triple goes to the workspace at (b, i, h, p0 + kR):
+ * m = max_j z_j * log2(e)  (base-2 units),  l = sum_j exp(z_j - max z),
+ * o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the rotated domain for the Turbo
+ * formats; the keys j are those of the run that query i sees, and a query that sees none of
+ * them gets m = -inf, l = 0, o = 0.  Other slots are not written.  Sequences that are not split
+ * get their final output row written here. */
 int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,
@@ -224,8 +226,9 @@ int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cac
                           float* out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* Phase 2 alone (same arguments; reads the workspace phase 1 filled).  For each split
- * (b, h): M = max_p m_p, w_p = l_p 2^(m_p - M), out = sum_p w_p o_p / sum_p w_p, then (Turbo)
+/* Phase 2 alone (same arguments, so the same run length R; reads the workspace phase 1
+ * filled).  For each split (b, h), over its runs k: M = max_k m_k, w_k = l_k 2^(m_k - M),
+ * out = sum_k w_k o_k / sum_k w_k, then (Turbo)
  * out <- diag(s) H out / sqrt(D).  Rows of sequences that are not split are left untouched. */
 int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table,

@@ -61,25 +61,20 @@ int device_cus() {
 
 // Partitions each wave of the partition kernel walks, and the kernel's layout.  A wave pays a
 // fixed start-up (query staging, the block-table -> page-load latency chain, filling its load
-// pipeline) and leaves a tail when it ends; walking several partitions amortises both.  The
-// automatic choice keeps about one wave per resident slot of the chip (P * Hkv * B waves /
-// resident waves) as if every sequence were max_context_len long.  Where the wide layout is
-// built (one workgroup per CU) it is taken if runs of at most kMaxRunWide cover the chip in
-// one round; otherwise runs are capped at kMaxRun (ragged batches, whose real work is smaller,
-// do better with short runs).  Runs are also capped at the rows a wave can stage in LDS
-// (stage_rows / group) and need partition boundaries on even pages (partition size a multiple
-// of 32).  An explicit partitions_per_wave always uses the two-workgroup layout.
+// pipeline) and leaves a tail when it ends, and it writes one (m, l, o) triple per run;
+// walking several partitions amortises all three.  The automatic choice keeps about one wave
+// per resident slot of the chip (P * Hkv * B waves / resident waves) as if every sequence were
+// max_context_len long.  Where the wide layout is built (one workgroup per CU) it is taken if
+// runs of at most kMaxRunWide cover the chip in one round; otherwise runs are capped at kMaxRun
+// (ragged batches, whose real work is smaller, do better with short runs).  Runs need
+// partition boundaries on even pages (partition size a multiple of 32).  An explicit
+// partitions_per_wave always uses the two-workgroup layout.
 struct RunChoice {
     int run;
     bool wide;
 };
 RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return {1, false};
-    const int64_t rows = query_rows(d);
-    const int64_t group_rows = rows < kvd::kMaxGroup ? rows : kvd::kMaxGroup;
-    auto staging_cap = [&](bool wide) -> int64_t {
-        return fmt < KVD_TURBO4 ? kvd::stage_rows(d->head_dim, wide) / group_rows : INT64_MAX;
-    };
     int64_t r = d->partitions_per_wave;
     bool wide = false;
     if (r == 0) {
@@ -88,7 +83,7 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         if (kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
             const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(true);
             const int64_t rw = (waves + slots - 1) / slots;
-            if (rw <= kvd::kMaxRunWide && rw <= staging_cap(true)) {
+            if (rw <= kvd::kMaxRunWide) {
                 wide = true;
                 r = rw;
             }
@@ -99,7 +94,6 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
             if (r > kvd::kMaxRun) r = kvd::kMaxRun;
         }
     }
-    if (r > staging_cap(wide)) r = staging_cap(wide);
     if (r > pl.P) r = pl.P;
     return {r < 1 ? 1 : (int)r, wide};
 }

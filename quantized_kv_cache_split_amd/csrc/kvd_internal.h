@@ -13,8 +13,9 @@ constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
 constexpr int kMaxGroup = 16;       // query heads one MFMA tile (one wave) handles
 constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
-// Wide layout of the partition kernel: one 4-wave workgroup per CU (one wave per SIMD) with 64
-// staged rows per wave (137 KB of LDS), so runs of up to kMaxRunWide partitions.  Built for
+// Wide layout of the partition kernel: one 4-wave workgroup per CU (one wave per SIMD; its LDS
+// area of 137 KB keeps a second workgroup off the CU), with runs of up to kMaxRunWide
+// partitions.  Built for
 // single-query BF16 at head_dim 128, where the random-page stream reads faster with half the
 // waves (BF16 16 x 32K: 380 against 390 us per call); the host takes it only when such runs
 // cover the chip in one round (a large ragged batch balances better with short runs).
@@ -27,8 +28,9 @@ constexpr int waves_per_simd(bool wide) { return wide ? 1 : 2; }
 // the codebook formats (sharing conflict-free codebook tables: 128 KB for Turbo4 / Turbo3, one
 // workgroup per CU; 64 KB for Turbo8, two per CU).
 constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
-// (m, l, o) rows of finished partitions one wave of the partition kernel stages in LDS;
-// a wave's run of partitions is capped at stage_rows / group (BF16 / FP8).
+// Rows of the per-wave LDS merge area of the BF16 / FP8 partition kernel (the unsplit merge
+// uses the first kMaxGroup).  Its size is what holds the kernel at two workgroups per CU
+// (67.6 KB each at D = 128) or one in the wide layout (137 KB).
 constexpr int stage_rows(int d, bool wide) { return (wide ? 8192 : 4096) / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };

@@ -10,7 +10,7 @@
 //       FP8, two per CU, or one per CU in the WIDE layout of single-query BF16; 8 for the
 //       codebook formats) over (partition slot, sequence, KV head x query tile).
 //       For a split sequence each wave walks a run of consecutive partitions of one (sequence,
-//       KV head, query tile) and writes every partition's (m, l, o) triple; an unsplit
+//       KV head, query tile) and writes one (m, l, o) triple for the run; an unsplit
 //       sequence's pages are shared by the workgroup's waves, which merge through LDS.  A wave
 //       walks pairs of 16-token pages, software-pipelined: PF pairs' loads are in flight while
 //       it computes, and the block-table entries ahead of them come in with scalar loads.  Per
@@ -456,8 +456,9 @@ __device__ __forceinline__ LaneMap lane_map(int lane) {
 // Grid ceil(P / (4 R)) * Hkv * B (1-D), 4 waves, R = p.run partitions per wave.  For a split
 // sequence wave w of workgroup x owns the run of R consecutive partitions that starts at
 // partition plo + (4x + w) R (plo = the first partition the attended range touches), streams
-// through all of them without draining its load pipeline, and writes each partition's triple
-// straight from registers once the partition's last page pair is done.  For an unsplit
+// through all of them without draining its load pipeline, and writes one triple for the whole
+// run (the online softmax merges its partitions as it goes) to the slot of the run's first
+// partition; the reduce merges the runs.  For an unsplit
 // sequence (workgroup 0 only) the four waves share the attended range (consecutive quarters of
 // its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
@@ -474,15 +475,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     static_assert(!kVcb || D == 128, "codebook formats are built for head_dim 128");
     using Raw = PairRaw<FMT, D>;
 
-    // LDS.  BF16 / FP8 (4 waves, two workgroups per CU): per-wave staging of finished (m, l, o)
-    // rows -- a split wave stages the triples of the partitions it closes (row r * g + n for
-    // the r-th partition of its run, query n) and copies them to the workspace after its walk,
-    // so no global store joins the in-order stream of its loads; the unsplit merge uses rows
-    // 0..g-1.  Rows are D + 4 floats apart so the 16 query rows a ds_write_b128 touches start
-    // in different banks.  Codebook-V formats (8 waves): the conflict-free pair tables at LDS
+    // LDS.  BF16 / FP8 (4 waves): per-wave rows of the unsplit merge (rows 0..g-1), D + 4
+    // floats apart so the 16 query rows a ds_write_b128 touches start in different banks.  The
+    // area is sized (stage_rows) so that two workgroups fit per CU, or one in the WIDE layout:
+    // it sets the occupancy.  Codebook-V formats (8 waves): the conflict-free pair tables at LDS
     // address 0 (K and V, 128 KB, one workgroup per CU for Turbo4 / Turbo3; V only, 64 KB, two
-    // per CU for Turbo8), reused for the unsplit merge once every wave has finished its walk;
-    // these waves write partials directly.
+    // per CU for Turbo8), reused for the unsplit merge once every wave has finished its walk.
     constexpr int SR = kVcb ? kMaxGroup : stage_rows(D, WIDE);
     constexpr int SD = D + 4;
     struct Merge {
@@ -580,15 +578,15 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     }
     // token range [lo, hi) of this wave (uniform per workgroup: whether any wave has work);
     // split waves also track the partition being accumulated and where its tokens end
-    int lo, hi, part = 0, part_end = 0, part_first = 0;
+    int lo, hi, part_end = 0, part_first = 0;
     if (si.split) {
         const int plo = si.lo / p.part_size, phi = (si.L - 1) / p.part_size;
         if (plo + xb * kW * p.run > phi) return;
-        part = part_first = plo + (xb * kW + wave) * p.run;
-        const int pend = min(part + p.run, phi + 1);
-        lo = max(si.lo, part * p.part_size);
+        part_first = plo + (xb * kW + wave) * p.run;
+        const int pend = min(part_first + p.run, phi + 1);
+        lo = max(si.lo, part_first * p.part_size);
         hi = min(si.L, pend * p.part_size);
-        part_end = min(hi, (part + 1) * p.part_size);
+        part_end = min(hi, (part_first + 1) * p.part_size);
     } else {
         if (xb != 0) return;
         const int pg0 = (si.lo / kPageTokens) & ~1, pg1 = (si.L - 1) / kPageTokens + 1;
@@ -941,63 +939,21 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 
     // Codebook formats (8 waves, two per SIMD): the hardware issues from the older of a SIMD's
     // two waves first, so waves 4-7 fall behind waves 0-3.  The pair start with opposite
-    // priorities and swap them at every partition they close.
+    // priorities and swap them at every partition boundary they cross.  The condition is
+    // wave-uniform; pairs past the end cross nothing.
     bool prio_hi = (wave >> 2) & 1;
     if constexpr (kVcb) {
         if (prio_hi) __builtin_amdgcn_s_setprio(1);
     }
-
-    // ---- split sequences: close a partition after its last pair ------------------------
-    // Writes the partition's triple (m = the exact max logit in base-2 units, l = the sum
-    // taken relative to it, o = O / l in output units, which no reference choice affects) and
-    // restarts the softmax state for the next partition of the run exactly as a fresh wave
-    // starts it, so the triples do not depend on how many partitions a wave walks.  The
-    // condition is wave-uniform; pairs past the end never close anything.
-    auto close_partition = [&](int k) {
-        const int tend = (pg0 + 2 * k + 2) * kPageTokens;   // first token after pair k
-        if (k < npairs && tend >= part_end) {
-            float lt = l_run + __shfl_xor(l_run, 16);
-            lt += __shfl_xor(lt, 32);
-            const float osc = kVcb ? oscale * sig_run : oscale;
-            // a query row that saw no key of this partition: m = -inf, l = 0, o = 0
-            const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
-            const float lx = lt > 0.0f ? lt * fast_exp2(m_run - m_true) : 0.0f;   // relative to the exact max
-            if constexpr (kVcb) {
-                if (qlive) {
-                    const size_t slot = row_index(n) * p.P + part;
-#pragma unroll
-                    for (int t = 0; t < VT; ++t)
-                        *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
-                    if (j == 0) {
-                        p.ws_m[slot] = m_true;
-                        p.ws_l[slot] = lx;
-                    }
-                }
-            } else {
-                const int row = (part - part_first) * g + n;
-                if (qlive && row < SR) {   // the host keeps run * g <= SR
-#pragma unroll
-                    for (int t = 0; t < VT; ++t)
-                        *reinterpret_cast<f32x4*>(&sm_o[wave][row * SD + 16 * t + 4 * j]) = oacc[t] * sc;
-                    if (j == 0) {
-                        sm_m[wave][row] = m_true;
-                        sm_l[wave][row] = lx;
-                    }
-                }
-            }
-            if constexpr (kVcb) {   // hand the SIMD's issue priority to its other wave
+    auto partition_boundary = [&](int k) {
+        if constexpr (kVcb) {
+            const int tend = (pg0 + 2 * k + 2) * kPageTokens;   // first token after pair k
+            if (k < npairs && tend >= part_end) {
                 prio_hi = !prio_hi;
                 if (prio_hi) __builtin_amdgcn_s_setprio(1);
                 else __builtin_amdgcn_s_setprio(0);
+                part_end = min(hi, part_end + p.part_size);
             }
-            m_run = m_true = -INFINITY;
-            l_run = 0.0f;
-            sig_run = kSigInit;
-            inv_sig = 1.0f / kSigInit;
-#pragma unroll
-            for (int t = 0; t < VT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            ++part;
-            part_end = min(hi, part_end + p.part_size);
         }
     };
 
@@ -1032,7 +988,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 #pragma unroll
             for (int i = 0; i < PF; ++i) {
                 compute(buf[i], k + i);
-                if (si.split) close_partition(k + i);
+                if (si.split) partition_boundary(k + i);
                 __builtin_amdgcn_sched_barrier(0);
                 size_t ha, hb;
                 heads(ida[i], idb[i], ha, hb);
@@ -1044,27 +1000,26 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     }
 
     // ---- results ---------------------------------------------------------------------------
+    // Split sequences: the run's triple, merged over its partitions, goes to the slot of its
+    // first partition: m = the exact max logit in base-2 units, l = the sum taken relative to
+    // it, o = O / l in output units (no reference choice affects them).  A query row that saw
+    // no key of the run: m = -inf, l = 0, o = 0.
     if (si.split) {
-        if (kVcb || !live) return;   // codebook-V formats wrote their triples directly
-        // copy the run's staged triples to the workspace (this wave's own LDS rows: a
-        // wavefront-scope fence orders the other lanes' writes before the reads)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int nrows = min((part - part_first) * g, SR);
-        constexpr int C = D / 4;   // f32x4 per row
-        for (int i = lane; i < nrows * C; i += 64) {
-            const int row = i / C, c = i % C;
-            const int r = row / g, qn_ = row - r * g;
-            const size_t slot = row_index(qn_) * p.P + part_first + r;
-            *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 4 * c) =
-                *reinterpret_cast<const f32x4*>(&sm_o[wave][row * SD + 4 * c]);
-        }
-        for (int row = lane; row < nrows; row += 64) {
-            const int r = row / g, qn_ = row - r * g;
-            const size_t slot = row_index(qn_) * p.P + part_first + r;
-            p.ws_m[slot] = sm_m[wave][row];
-            p.ws_l[slot] = sm_l[wave][row];
+        if (!live) return;
+        float lt = l_run + __shfl_xor(l_run, 16);
+        lt += __shfl_xor(lt, 32);
+        const float osc = kVcb ? oscale * sig_run : oscale;
+        const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
+        const float lx = lt > 0.0f ? lt * fast_exp2(m_run - m_true) : 0.0f;
+        if (qlive) {
+            const size_t slot = row_index(n) * p.P + part_first;
+#pragma unroll
+            for (int t = 0; t < VT; ++t)
+                *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
+            if (j == 0) {
+                p.ws_m[slot] = m_true;
+                p.ws_l[slot] = lx;
+            }
         }
         return;
     }
@@ -1116,11 +1071,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence x query of the chunk); lane l owns output elements
-// E*l .. E*l + E - 1
-// (E = D / 64).  Partitions are taken 64 at a time: each lane loads the (m, l) of one of them
-// and then every lane loads its slice of all 64 partition outputs, so a block costs one memory
-// round trip.  The block's weights are computed lane-parallel and broadcast with v_readlane;
-// blocks after the first rescale the running sums to the new maximum (online LSE).
+// E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per run of p.run
+// partitions, at the slot of the run's first partition (runs start at the sequence's first
+// partition).  Triples are taken 64 at a time: each lane loads the (m, l) of one of them and
+// then every lane loads its slice of all 64 outputs, so a block costs one memory round trip.
+// The block's weights are computed lane-parallel and broadcast with v_readlane; blocks after
+// the first rescale the running sums to the new maximum (online LSE).
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     constexpr bool kVcb = v_codebook<FMT>();   // partial outputs are in the rotated domain
@@ -1130,7 +1086,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     const SeqInfo si = seq_info<true>(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
     const int p0 = si.lo / p.part_size, p1 = (si.L - 1) / p.part_size;
-    const int n = p1 - p0 + 1;
+    const int R = p.run;
+    const int n = (p1 - p0 + R) / R;             // runs (triples) of the sequence
     const size_t row = (size_t)bi * p.Hq + hq;   // out / workspace row (b, query, head)
     const float* ms = p.ws_m + row * p.P + p0;
     const float* ls = p.ws_l + row * p.P + p0;
@@ -1143,13 +1100,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     for (int base = 0; base < n; base += kBlock) {
         // indices past the end are clamped (their loads stay in bounds) and weighted 0
         const int q = min(base + lane, n - 1);
-        const float mq = ms[q], lq = ls[q];
+        const float mq = ms[(size_t)q * R], lq = ls[(size_t)q * R];
         float v[kBlock][E];
 #pragma unroll
         for (int u = 0; u < kBlock; ++u) {
             const int qq = min(base + u, n - 1);
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
+            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * R * D + e];
         }
         __builtin_amdgcn_sched_barrier(0);   // keep all of the block's loads ahead of any use
         const bool in = base + lane < n;

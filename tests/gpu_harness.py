@@ -125,3 +125,32 @@ def assert_close(gpu, ref, what=""):
     assert ea <= ABS_TOL and er <= REL_TOL, (what, ea, er)
     assert e2 <= ROW_RMS_TOL[format_of(what)], (what, e2)
     return ea, er
+
+
+def merge_runs(parts, part_size, run):
+    """Group an oracle's per-partition triples [(lo, hi, m, l, o), ...] (in order, natural-log
+    m) into the runs of ``run`` consecutive partitions the partition kernel merges (runs start
+    at the first partition of the range), merging each run with the LSE rule:
+    M = max m_i, l = sum l_i e^(m_i - M), o = sum l_i e^(m_i - M) o_i / l.  Rows with no key in a
+    run keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)], slot = the run's first
+    partition."""
+    if not parts:
+        return []
+    p0 = parts[0][0] // part_size
+    groups = {}
+    for lo, hi, m, l, o in parts:
+        groups.setdefault((lo // part_size - p0) // run, []).append((lo, hi, m, l, o))
+    out = []
+    for k in sorted(groups):
+        g = groups[k]
+        ms = np.array([x[2] for x in g], dtype=np.float64)
+        ls = np.array([x[3] for x in g], dtype=np.float64)
+        os_ = np.array([x[4] for x in g], dtype=np.float64)
+        M = ms.max(axis=0)
+        safe = np.where(np.isfinite(M), M, 0.0)
+        w = np.where(ls > 0, ls * np.exp(np.where(ls > 0, ms, 0.0) - safe), 0.0)
+        L = w.sum(axis=0)
+        O = np.einsum("pr,prd->rd", w, os_) / np.where(L > 0, L, 1.0)[:, None]
+        out.append((p0 + k * run, g[0][0], g[-1][1], M, L, O))
+    return out
+

@@ -68,8 +68,9 @@ def test_multi_query_window_alibi_cap(fmt, ps):
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
-def test_multi_query_runs_bit_identical(fmt):
-    """Partitions per wave change the launch, not the bits (every query row restarts exactly)."""
+def test_multi_query_runs_agree(fmt):
+    """Partitions per wave change the launch and the grouping of the sums (one triple per run
+    and query row), not the result."""
     lengths, windows = [5000, 1100, 2600, 40], [1100, 0, 333, 0]
     inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=4, num_q_heads=8, num_kv_heads=2,
                                        softcap=0.0, queries_per_seq=4),
@@ -79,8 +80,9 @@ def test_multi_query_runs_bit_identical(fmt):
     for run in (1, 2, 3):
         outs[run] = GpuBatch(inp, partition_size=128, partitions_per_wave=run).run()
         assert_close(outs[run], ref, f"{fmt} mq run={run}")
+    tol = 1e-5 if fmt in ("bf16", "fp8") else 5e-4
     for run in (2, 3):
-        assert (outs[run].view(np.uint64) == outs[1].view(np.uint64)).all(), run
+        assert np.abs(outs[run] - outs[1]).max() <= tol, run
 
 
 @pytest.mark.parametrize("fmt", ["bf16", "turbo4"])
@@ -92,7 +94,7 @@ def test_multi_query_partials(fmt):
     inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2,
                                        pool_total=None, queries_per_seq=8, num_seqs=2),
                             lengths=[355, 612], windows=[40, 40])
-    gb = GpuBatch(inp, partition_size=32)
+    gb = GpuBatch(inp, partition_size=32, partitions_per_wave=1)
     gb.run_phase1()
     m, l, o = gb.partials()          # [B, n_q, Hq, P]
     s = inp.spec

@@ -14,7 +14,7 @@ import pytest
 import kvgen
 import oracle
 from conftest import oracle_args
-from gpu_harness import GpuBatch, assert_close
+from gpu_harness import GpuBatch, assert_close, merge_runs
 
 pytestmark = pytest.mark.gpu
 
@@ -191,10 +191,10 @@ def test_partition_modes_agree(fmt):
 
 
 @pytest.mark.parametrize("fmt", kvgen.FORMATS)
-def test_partitions_per_wave_bit_identical(fmt):
-    """Walking several partitions per wave changes the launch, not the results: every run length
-    gives the same bits (each partition restarts the state exactly as a fresh wave), and those
-    bits match the oracle.  Windows put the first attended token on odd and even pages."""
+def test_partitions_per_wave_agree(fmt):
+    """Walking several partitions per wave changes the launch and how the online softmax groups
+    the sums (one triple per run), not the result: every run length matches the oracle and the
+    others to MODE_AGREE.  Windows put the first attended token on odd and even pages."""
     lengths = [5000, 4100, 3000, 1100, 2600, 700]
     windows = [1100, 0, 1333, 0, 2049, 100]
     inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=len(lengths), num_q_heads=8,
@@ -210,7 +210,7 @@ def test_partitions_per_wave_bit_identical(fmt):
             outs[ps, run] = GpuBatch(inp, partition_size=ps, partitions_per_wave=run).run()
             assert_close(outs[ps, run], ref, f"{fmt} ps={ps} run={run}")
         for run in (2, 3, 5, 8):
-            assert (outs[ps, run].view(np.uint64) == outs[ps, 1].view(np.uint64)).all(), (ps, run)
+            assert np.abs(outs[ps, run] - outs[ps, 1]).max() <= MODE_AGREE[fmt], (ps, run)
 
 
 # --------------------------------------------------------------------------------------------
@@ -276,9 +276,10 @@ def test_partials_match_oracle(fmt, run):
     s = inp.spec
     for b in range(s.num_seqs):
         for hk in range(s.num_kv_heads):
-            parts = oracle.partition_partials(*oracle_args(inp), 128, b, hk, rotated=True)
-            for lo_, hi_, pm, pl, po in parts:
-                p = lo_ // 128
+            # one triple per run of `run` partitions, at the slot of its first partition
+            parts = merge_runs(oracle.partition_partials(*oracle_args(inp), 128, b, hk,
+                                                         rotated=True), 128, run)
+            for p, lo_, hi_, pm, pl, po in parts:
                 rows = slice(hk * s.group, hk * s.group + s.group)
                 m_nat = m[b, rows, p].astype(np.float64) * np.log(2.0)
                 # BF16/FP8 logits are exact bf16 products summed in fp32.  The codebook formats
@@ -365,7 +366,7 @@ def test_alibi_position_coded_v(fmt):
 def test_alibi_partials_match_oracle(fmt):
     inp = _small(fmt, context=None, ctx_range=(200, 700), num_seqs=2)
     sl = _slopes(inp.spec.num_q_heads)
-    gb = GpuBatch(inp, partition_size=128, alibi=sl)
+    gb = GpuBatch(inp, partition_size=128, partitions_per_wave=1, alibi=sl)
     gb.run_phase1()
     m, l, o = gb.partials()
     s = inp.spec
