@@ -127,17 +127,18 @@ typedef struct kvd_dims {
                                     >= 1024 tokens, else a single partition;
                                     > 0: always split at that many tokens (a multiple of 16);
                                     -1: never split */
-    int32_t partitions_per_wave; /* launch tuning: how many consecutive partitions of a split
-                                    sequence one wavefront walks; it writes one triple for the
-                                    run (results agree to rounding: the online softmax groups
-                                    its sums by run).  0: auto
-                                    (about one wavefront per resident slot of the device when
-                                    every sequence had max_context_len tokens, at most 4;
-                                    single-query BF16 at head_dim 128 uses a layout with one
-                                    workgroup per CU and runs of up to 8 when that covers
-                                    the device in one round); > 0: that many.  Capped at the
-                                    partitions of max_context_len and treated as 1 when the
-                                    partition size is not a multiple of 32.  Must be >= 0. */
+    int32_t partitions_per_wave; /* launch tuning: the run one wavefront walks through a split
+                                    sequence; it writes one triple for the run (results agree
+                                    to rounding: the online softmax groups its sums by run).
+                                    0: auto -- the page pairs of a batch of max_context_len
+                                    sequences split evenly over the device's resident
+                                    wavefronts (whole 32-token pairs, at least one partition,
+                                    at most 4 partitions; single-query BF16 at head_dim 128
+                                    uses a layout with one workgroup per CU and runs of up to 8
+                                    partitions when that covers the device in one round);
+                                    > 0: runs of that many partitions.  Capped at the
+                                    partitions of max_context_len; runs are one partition when
+                                    the partition size is not a multiple of 32.  >= 0. */
     int32_t queries_per_seq;     /* n_q: queries per sequence, a chunk at the last n_q positions
                                     (above); 0 or 1: single-query decode.  The n_q * Hq / Hkv
                                     query rows of a KV head share one pass over its pages per
@@ -146,7 +147,7 @@ typedef struct kvd_dims {
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: slots for per-partition fp32 triples
- * (a run of partitions writes one, at the slot of its first partition)
+ * (the runs of a sequence write consecutive slots from its first partition's)
  * m [B][n_q][Hq][P], l [B][n_q][Hq][P] and o [B][n_q][Hq][P][D], P = ceil(max_context_len /
  * partition size), each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
 size_t kvd_workspace_bytes(const kvd_dims* dims);
@@ -207,12 +208,13 @@ int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const voi
                                   float softmax_scale, const int32_t* window, float softcap,
                                   const float* alibi_slopes, float* out, void* stream);
 
-/* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of R
- * consecutive partitions (R = partitions_per_wave when > 0, capped as described there; else the
- * automatic choice), four wavefronts per workgroup (eight for the Turbo formats).  For a split
- * sequence, partition p covers tokens [max(lo, p*P), min(L, (p+1)*P)); with p0 the first
- * partition of the sequence's range, run k covers partitions p0 + kR .. p0 + kR + R - 1 (those
- * inside the range) and its one triple goes to the workspace at (b, i, h, p0 + kR):
+/* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of T tokens
+ * (partitions_per_wave > 0: T = that many partitions; 0: the automatic choice, a whole number
+ * of 32-token page pairs of at least one partition), four wavefronts per workgroup (twelve for
+ * Turbo4 / Turbo3, eight for Turbo8).  For a split sequence with attended range [lo, L), let p0
+ * be the first partition the range touches (P tokens per partition); run k covers tokens
+ * [p0*P + k*T, p0*P + (k+1)*T) intersected with [lo, L), and its one triple goes to the
+ * workspace at (b, i, h, p0 + k):
  * m = max_j z_j * log2(e)  (base-2 units),  l = sum_j exp(z_j - max z),
  * o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the rotated domain for the Turbo
  * formats; the keys j are those of the run that query i sees, and a query that sees none of
@@ -267,7 +269,7 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
  *     BF16: d = 32 s + 8 j + e;  FP8 / Turbo8 K: d = 64 (s / 2) + 16 j + 8 (s % 2) + e;
  *     Turbo4/3 K: d = 32 j + 8 s + e   (e = 0..7).
  *   BF16 / FP8 / Turbo8 K: x0 = the eight values as bf16 (FP8 exact: E4M3FN(code), unscaled),
- *   x1 = 0.  Turbo4/3 K: x0 = fp16 [h0 h1 l0 l1 h2 h3 l2 l3], x1 = the same for e = 4..7,
+ *   x1 = 0.  Turbo4/3 K: x0 = fp16 [h0 .. h7], x1 = fp16 [l0 .. l7] of the eight elements,
  *   with (h, l) = (fp16(c), fp16(c - h)) of c = codebook level * 2^-E, 2^-E the power of two
  *   that puts the largest K level magnitude in [0.5, 1).
  * Words [D/2 + 8 t, D/2 + 8 t + 8), t = 0 .. D/16 - 1: PV tile t operands v0, v1 for head

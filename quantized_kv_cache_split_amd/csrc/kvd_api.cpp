@@ -59,43 +59,52 @@ int device_cus() {
     return cus;
 }
 
-// Partitions each wave of the partition kernel walks, and the kernel's layout.  A wave pays a
-// fixed start-up (query staging, the block-table -> page-load latency chain, filling its load
-// pipeline) and leaves a tail when it ends, and it writes one (m, l, o) triple per run;
-// walking several partitions amortises all three.  The automatic choice keeps about one wave
-// per resident slot of the chip (P * Hkv * B waves / resident waves) as if every sequence were
-// max_context_len long.  Where the wide layout is built (one workgroup per CU) it is taken if
-// runs of at most kMaxRunWide cover the chip in one round; otherwise runs are capped at kMaxRun
-// (ragged batches, whose real work is smaller, do better with short runs).  Runs need
-// partition boundaries on even pages (partition size a multiple of 32).  An explicit
-// partitions_per_wave always uses the two-workgroup layout.
+// Tokens each wave of the partition kernel walks (its run), and the kernel's layout.  A wave
+// pays a fixed start-up (query staging, the block-table -> page-load latency chain, filling its
+// load pipeline), leaves a tail when it ends and writes one (m, l, o) triple per run, so runs
+// should be long; the chip should also be covered in one round.  The automatic choice splits
+// the page pairs of a batch whose sequences were all max_context_len long evenly over the
+// device's resident wave slots (runs of whole page pairs, at least one partition long).  Where
+// the wide layout is built (one workgroup per CU) it is taken if runs of at most kMaxRunWide
+// partitions cover the chip in one round; otherwise runs are capped at kMaxRun partitions
+// (ragged batches, whose real work is smaller, do better with short runs).  Runs other than
+// one partition need partition boundaries on even pages (partition size a multiple of 32).  An
+// explicit partitions_per_wave R gives runs of R partitions in the two-workgroup layout.
 struct RunChoice {
-    int run;
+    int run_tokens;
     bool wide;
 };
 RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
-    if (!pl.P || pl.part_size % (2 * kvd::kPageTokens) != 0) return {1, false};
-    int64_t r = d->partitions_per_wave;
+    const int ps = pl.part_size;
+    if (!pl.P || ps % (2 * kvd::kPageTokens) != 0) return {ps, false};
+    const int64_t pair_tokens = 2 * kvd::kPageTokens;
+    int64_t tokens;
     bool wide = false;
-    if (r == 0) {
-        const int64_t tiles = query_tiles(d);
-        const int64_t waves = (int64_t)pl.P * d->num_kv_heads * tiles * d->num_seqs;
+    if (d->partitions_per_wave > 0) {
+        tokens = (int64_t)d->partitions_per_wave * ps;
+    } else {
+        const int64_t pairs = (d->max_context_len + pair_tokens - 1) / pair_tokens;
+        const int64_t units = (int64_t)d->num_kv_heads * query_tiles(d) * d->num_seqs;
+        auto run_for = [&](bool w) -> int64_t {
+            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w);
+            const int64_t rp = (pairs * units + slots - 1) / slots;   // pairs per wave
+            return rp * pair_tokens < ps ? ps : rp * pair_tokens;
+        };
         if (kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
-            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(true);
-            const int64_t rw = (waves + slots - 1) / slots;
-            if (rw <= kvd::kMaxRunWide) {
+            const int64_t t = run_for(true);
+            if (t <= (int64_t)kvd::kMaxRunWide * ps) {
                 wide = true;
-                r = rw;
+                tokens = t;
             }
         }
         if (!wide) {
-            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(false);
-            r = (waves + slots - 1) / slots;
-            if (r > kvd::kMaxRun) r = kvd::kMaxRun;
+            tokens = run_for(false);
+            if (tokens > (int64_t)kvd::kMaxRun * ps) tokens = (int64_t)kvd::kMaxRun * ps;
         }
     }
-    if (r > pl.P) r = pl.P;
-    return {r < 1 ? 1 : (int)r, wide};
+    const int64_t span = (int64_t)pl.P * ps;
+    if (tokens > span) tokens = span;
+    return {(int)tokens, wide};
 }
 
 // Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
@@ -204,10 +213,13 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.P = pl.P;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
     const RunChoice rc = choose_run(d, pl, fmt);
-    p.run = rc.run;
+    p.run_tokens = rc.run_tokens;
     const int waves = kvd::waves_per_group(fmt);
-    // token indices of every partition a workgroup can name must fit in int32
-    if (pl.P && ((int64_t)pl.P + (int64_t)waves * p.run) * pl.part_size > 0x7FFFFFFFLL)
+    // runs of a sequence, at most (one per partition)
+    const int64_t runs = pl.P ? ((int64_t)pl.P * pl.part_size + rc.run_tokens - 1) / rc.run_tokens
+                              : 0;
+    // token indices of every run a workgroup can name must fit in int32
+    if (pl.P && (int64_t)pl.P * pl.part_size + (int64_t)waves * rc.run_tokens > 0x7FFFFFFFLL)
         return KVD_ERR_SHAPE;
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
@@ -215,8 +227,8 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     if (phases & kPhase1) {
-        // `waves` waves per workgroup, p.run partitions per wave
-        const int px = pl.P ? (pl.P + waves * p.run - 1) / (waves * p.run) : 1;
+        // `waves` waves per workgroup, one run per wave
+        const int px = pl.P ? (int)((runs + waves - 1) / waves) : 1;
         const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qt * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);

@@ -21,13 +21,16 @@ constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave 
 // cover the chip in one round (a large ragged batch balances better with short runs).
 constexpr int kMaxRunWide = 8;
 constexpr bool wide_layout_built(int fmt, int d, bool mq) { return fmt == 0 && d == 128 && !mq; }
-// Resident waves of the partition kernel per CU, and the waves per SIMD it is compiled for.
-constexpr int waves_per_cu(bool wide) { return wide ? 4 : 8; }
-constexpr int waves_per_simd(bool wide) { return wide ? 1 : 2; }
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
-// the codebook formats (sharing conflict-free codebook tables: 128 KB for Turbo4 / Turbo3, one
-// workgroup per CU; 64 KB for Turbo8, two per CU).
+// the codebook formats (sharing conflict-free codebook tables: 130 KB for Turbo4 / Turbo3, one
+// workgroup per CU; 64 KB for Turbo8).  Measured on Turbo4 / Turbo3: twelve waves per workgroup
+// (three per SIMD, one page pair in flight) ran 1-4% slower than eight with two pairs in flight.
 constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
+// Waves per SIMD the partition kernel is compiled for (its register budget: 512 / this).
+constexpr int waves_per_simd(bool wide) { return wide ? 1 : 2; }
+// Resident waves per CU the automatic run choice fills (Turbo8 could hold two workgroups per
+// CU, but sixteen waves read its random pages more slowly than eight).
+constexpr int waves_per_cu(bool wide) { return wide ? 4 : 8; }
 // Rows of the per-wave LDS merge area of the BF16 / FP8 partition kernel (the unsplit merge
 // uses the first kMaxGroup).  Its size is what holds the kernel at two workgroups per CU
 // (67.6 KB each at D = 128) or one in the wide layout (137 KB).
@@ -66,7 +69,7 @@ struct LaunchParams {
     int32_t part_size;        // tokens per partition (split sequences)
     int32_t P;                // partitions per sequence in the workspace / grid
     int32_t kbits;            // turbo K index width (4 or 3)
-    int32_t run;              // partitions one wave walks (split sequences), >= 1
+    int32_t run_tokens;       // tokens of one wave's run (split sequences), >= part_size
     float softmax_scale;
     float softcap;
 };

@@ -67,6 +67,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 constexpr int kLutCopies = 32;   // copies of each codebook pair table (one per LDS bank pair)
+// K pair table (codebook K): hi dwords of entry e at e * 256 + [0, 128), lo dwords 4 entries
+// further on, at (e + 4) * 256 + [128, 256): the two reads of one entry are kKLoOffset bytes
+// apart, more than a two-address LDS read can span, so each lands in its own register.
+constexpr int kKLoOffset = 4 * 256 + 128;
+constexpr int kKTableBytes = (256 + 4) * 256;
+constexpr int kVTableBytes = 256 * 256;
+
 constexpr float kLog2e = 1.4426950408889634f;
 
 // How K and V of each format are stored:
@@ -79,6 +86,10 @@ template <int FMT>
 constexpr bool k_fp8() { return FMT == KVD_FP8_E4M3 || FMT == KVD_TURBO8; }
 template <int FMT>
 constexpr bool v_codebook() { return k_codebook<FMT>() || FMT == KVD_TURBO8; }
+// LDS byte of the V pair table: after the K table (codebook K), else 0.  The lane's V address
+// comes from one v_perm with byte 2 = 1 (64 KB) plus this constant's remaining 1024 bytes.
+template <int FMT>
+constexpr int v_table_base() { return k_codebook<FMT>() ? kKTableBytes : 0; }
 template <int FMT, int D>
 constexpr int k_chunk() { return FMT == KVD_BF16 ? 32 * D : k_fp8<FMT>() ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
 template <int FMT, int D>
@@ -123,21 +134,24 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
 }
 
 // Codebook pair tables.  Entry (i0 + n * i1), n = 16 (4-bit) or 8 (3-bit), holds the packed
-// fp16 dwords of the two levels (c[i0], c[i1]): .x = hi(c[i0]) | hi(c[i1]) << 16 and
-// .y = lo(c[i0]) | lo(c[i1]) << 16, with c ~= hi + lo.  One 8-byte LDS read per two indices.
+// fp16 dwords of the two levels (c[i0], c[i1]): hi = hi(c[i0]) | hi(c[i1]) << 16 and
+// lo = lo(c[i0]) | lo(c[i1]) << 16, with c ~= hi + lo.  Entries are 256 bytes apart, and each
+// table is stored kLutCopies = 32 times so that lane l reads copy l % 32: the lanes of one LDS
+// pass then hit different banks whatever the indices (a single shared table costs about 3.3x
+// more LDS cycles for random indices).  The address of entry b (a byte of the index word w) is
+// lanebase.byte0 | b << 8 | lanebase.byte2 << 16, one v_perm_b32.
 //
-// Bank-conflict-free layout: each table is stored kLutCopies = 32 times, entry e of copy c at
-// byte e * 256 + c * 8 (64 KB per table; the V table starts at byte 65536).  Lane l reads copy
-// l % 32, so whatever the indices, the 32 lanes of one LDS pass read 32 different bank pairs
-// (a single shared table costs about 3.3x more LDS cycles for random indices).  With
-// lanebase = (l % 32) * 8 (+ 65536 for the V table), the address of entry b (a byte of w) is
-// lanebase.byte0 | b << 8 | lanebase.byte2 << 16: one v_perm_b32.
+// V table (after the K table, else at LDS byte 0): copy c of entry e is the 8-byte pair
+// {hi, lo} at e * 256 + c * 8 (lanebase = (l % 32) * 8).  Four reads give eight indices as the
+// "interleaved" MFMA operands a0 = {hi(e0,e1), lo(e0,e1), hi(e2,e3), lo(e2,e3)}, a1 the same
+// for e4..e7, i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3]; against the repeated P operand
+// [p0 p1 p0 p1 p2 p3 p2 p3] one MFMA accumulates (hi + lo) * p for four tokens.
 //
-// The reads land directly as "interleaved" MFMA operands: for eight indices e0..e7,
-//   a0 = {hi(e0,e1), lo(e0,e1), hi(e2,e3), lo(e2,e3)},  a1 = the same for e4..e7,
-// i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3].  Paired with a B operand whose slots repeat each
-// value, [x0 x1 x0 x1 x2 x3 x2 x3], one MFMA accumulates (hi + lo) * x for four elements; with
-// [y0 y1 0 0 y2 y3 0 0] it accumulates hi * y.
+// K table (codebook K, LDS byte 0): the two halves separately, copy c of entry e's hi dword at
+// e * 256 + c * 4 and of its lo dword kKLoOffset bytes further on (lanebase = (l % 32) * 4).
+// Eight reads give eight indices as two plain operands, k-slots [h0 .. h7] and [l0 .. l7], so
+// the query operand needs no repeated slots: hi * q_hi + lo * q_hi + hi * q_lo takes three MFMAs
+// per eight elements and 8 VGPRs of query per 32 elements.
 template <int K>
 __device__ __forceinline__ u32x2 lut_byte(const char* lds, uint32_t lanebase, uint32_t w) {
     static_assert(K >= 0 && K < 4, "byte index");
@@ -152,17 +166,25 @@ __device__ __forceinline__ void lut_nib8(const char* lds, uint32_t lanebase, uin
     a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
     a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
 }
-// 8 3-bit indices (index e at bits 3e of the low 24 bits of f): 6-bit pair indices.
-__device__ __forceinline__ void lut_tri8(const char* lds, uint32_t lanebase, uint32_t f,
-                                         u32x4& a0, u32x4& a1) {
-    u32x2 e[4];
+// K table: 8 4-bit indices (index e at bits 4e of w) -> hi and lo operands.
+__device__ __forceinline__ void klut_nib8(const char* lds, uint32_t lanebase, uint32_t w,
+                                          u32x4& ahi, u32x4& alo) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, lanebase, (12u << 24) | (2u << 16) | ((4u + k) << 8));
+        ahi[k] = *reinterpret_cast<const uint32_t*>(lds + addr);
+        alo[k] = *reinterpret_cast<const uint32_t*>(lds + addr + kKLoOffset);
+    }
+}
+// K table: 8 3-bit indices (index e at bits 3e of the low 24 bits of f), as 6-bit pair indices.
+__device__ __forceinline__ void klut_tri8(const char* lds, uint32_t lanebase, uint32_t f,
+                                          u32x4& ahi, u32x4& alo) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t addr = (__builtin_amdgcn_ubfe(f, 6 * i, 6) << 8) | lanebase;
-        e[i] = *reinterpret_cast<const u32x2*>(lds + addr);
+        ahi[i] = *reinterpret_cast<const uint32_t*>(lds + addr);
+        alo[i] = *reinterpret_cast<const uint32_t*>(lds + addr + kKLoOffset);
     }
-    a0 = u32x4{e[0][0], e[0][1], e[1][0], e[1][1]};
-    a1 = u32x4{e[2][0], e[2][1], e[3][0], e[3][1]};
 }
 // The 24-bit field holding indices 8h..8h+7 of a 32-index, 3-bit group (w0..w2 = its 12 bytes).
 __device__ __forceinline__ uint32_t tri_field(uint32_t w0, uint32_t w1, uint32_t w2, int h) {
@@ -232,6 +254,18 @@ __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
     s.split = p.part_mode == kPartFixed ? true
             : (p.part_mode == kPartNever ? false : span >= kAutoSplitMin);
     return s;
+}
+
+// Runs of a split sequence.  A run is p.run_tokens consecutive tokens (a whole number of
+// partitions, or of page pairs covering at least one partition) counted from the first token
+// of the first partition the attended range touches (plo * part_size); run i covers
+// [base + i * run_tokens, base + (i + 1) * run_tokens) intersected with [lo, L), one wave walks
+// it, and its merged triple goes to workspace slot plo + i.  Returns the number of runs.
+__device__ __forceinline__ int split_runs(const LaunchParams& p, const SeqInfo& si, int& plo,
+                                          int& base) {
+    plo = si.lo / p.part_size;
+    base = plo * p.part_size;
+    return (si.L - base + p.run_tokens - 1) / p.run_tokens;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -335,9 +369,8 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 // ------------------------------------------------------------------------------------------
 // The A operands of QK step s (head elements 32s .. 32s + 31 in the order of the query operand)
 // for the pair's two 16-token tiles X and Y.  BF16 / FP8 K (also Turbo8 K): one bf16x8 operand
-// per tile in x0 / y0 (FP8 -> bf16 is exact); x1 / y1 are zero.  Codebook K: two interleaved
-// fp16 hi / lo operands per tile from the K pair table (x0 = elements 0..3, x1 = 4..7 of the
-// lane's eight).
+// per tile in x0 / y0 (FP8 -> bf16 is exact); x1 / y1 are zero.  Codebook K: the fp16 hi parts
+// of the lane's eight elements in x0 (y0) and their lo parts in x1 (y1), from the K table.
 template <int FMT, int D>
 __device__ __forceinline__ void k_operands(const PairRaw<FMT, D>& r, int s, const char* lds,
                                            uint32_t kbase, u32x4& x0, u32x4& x1, u32x4& y0,
@@ -353,11 +386,11 @@ __device__ __forceinline__ void k_operands(const PairRaw<FMT, D>& r, int s, cons
         x0 = u32x4{ax0[0], ax0[1], ax1[0], ax1[1]};
         y0 = u32x4{ay0[0], ay0[1], ay1[0], ay1[1]};
     } else if constexpr (FMT == KVD_TURBO4) {
-        lut_nib8(lds, kbase, r.kx[s], x0, x1);
-        lut_nib8(lds, kbase, r.ky[s], y0, y1);
+        klut_nib8(lds, kbase, r.kx[s], x0, x1);
+        klut_nib8(lds, kbase, r.ky[s], y0, y1);
     } else {
-        lut_tri8(lds, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
-        lut_tri8(lds, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
+        klut_tri8(lds, kbase, tri_field(r.kx[0], r.kx[1], r.kx[2], s), x0, x1);
+        klut_tri8(lds, kbase, tri_field(r.ky[0], r.ky[1], r.ky[2], s), y0, y1);
     }
 }
 
@@ -375,13 +408,13 @@ __device__ __forceinline__ void v_operands(const PairRaw<FMT, D>& r, int t, cons
         v0 = u32x4{a0[0], a0[1], a1[0], a1[1]};
         v1 = u32x4{0u, 0u, 0u, 0u};
     } else {
-        lut_nib8(lds, vbase, r.v[t], v0, v1);
+        lut_nib8(lds + (v_table_base<FMT>() & 0xFFFF), vbase, r.v[t], v0, v1);
     }
 }
 
 // Codebook levels a workgroup's tables are built from: the two levels of this thread's table
-// entry e = (tid / 2) % 256 (entry i0 + n i1 holds levels i0 and i1; n = 2^kbits for K, 16 for
-// V) and the largest level magnitudes.  The array holds 2^kbits K levels then 16 V levels
+// entry e = tid % 256 (entry i0 + n i1 holds levels i0 and i1; n = 2^kbits for K, 16 for V; the
+// entry fill_tables gives the thread) and the largest level magnitudes.  The array holds 2^kbits K levels then 16 V levels
 // (Turbo8: the 16 V levels).
 struct Levels {
     float k0, k1, v0, v1, kmax, vmax;
@@ -401,7 +434,7 @@ __device__ __forceinline__ Levels load_levels(const float* codebook, int kbits, 
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) lv.vmax = fmaxf(lv.vmax, fabsf(codebook[kl + i]));
-    const int e = (tid >> 1) & 255;
+    const int e = tid & 255;
     if constexpr (kKcb) {
         lv.k0 = codebook[e % kl];
         lv.k1 = codebook[(e / kl) % kl];
@@ -412,30 +445,35 @@ __device__ __forceinline__ Levels load_levels(const float* codebook, int kbits, 
 }
 
 // Fills the conflict-free pair tables (K table at LDS byte 0 for codebook K, then the V table)
-// with the levels scaled by the power-of-two normalisers ksc / vsc.  512 threads: thread t
-// fills half of the kLutCopies copies of entry t / 2 of every table.  The copy order is
-// staggered by entry: in each store the 16 lanes of a pass write 16 different 16-byte bank
-// groups (entries are 256 bytes apart, so the same copy of every entry would sit in the same
-// banks: 8-way conflicts).
-template <int FMT>
-__device__ __forceinline__ void fill_tables(u32x4* lut, int tid, const Levels& lv, float ksc,
+// with the levels scaled by the power-of-two normalisers ksc / vsc.  NT threads (a multiple of
+// 256): thread t takes entry t % 256 and every (NT / 256)-th of its sixteen 16-byte slots
+// (K: slots 0..7 hold four hi copies each, 8..15 four lo copies, kKLoOffset - 128 bytes
+// further on; V: two {hi, lo} copies each).
+// The slot order is staggered by entry, so the 16 lanes of a store pass write 16 different
+// 16-byte bank groups (entries are 256 bytes apart: the same slot of every entry would sit in
+// the same banks).
+template <int FMT, int NT>
+__device__ __forceinline__ void fill_tables(char* lds, int tid, const Levels& lv, float ksc,
                                             float vsc) {
+    static_assert(NT % 256 == 0, "whole entries per thread group");
     constexpr bool kKcb = k_codebook<FMT>();
-    constexpr int kTableVecs = 256 * kLutCopies / 2;   // u32x4 per table
-    const int e = tid >> 1, c0 = (tid & 1) * (kLutCopies / 2);
-    uint32_t h, l;
-    u32x4 kv = {0u, 0u, 0u, 0u};
-    if constexpr (kKcb) {
-        f16_hilo(lv.k0 * ksc, lv.k1 * ksc, h, l);
-        kv = u32x4{h, l, h, l};
-    }
-    f16_hilo(lv.v0 * vsc, lv.v1 * vsc, h, l);
-    const u32x4 vv = {h, l, h, l};
+    constexpr int kParts = NT / 256;
+    const int e = tid & 255, part = tid >> 8;
+    uint32_t kh = 0u, kl = 0u, vh, vl;
+    if constexpr (kKcb) f16_hilo(lv.k0 * ksc, lv.k1 * ksc, kh, kl);
+    f16_hilo(lv.v0 * vsc, lv.v1 * vsc, vh, vl);
+    const u32x4 khi = {kh, kh, kh, kh}, klo = {kl, kl, kl, kl}, vv = {vh, vl, vh, vl};
+    char* const vt = lds + v_table_base<FMT>();
 #pragma unroll
-    for (int c = 0; c < kLutCopies / 2; c += 2) {
-        const int cc = (c + 2 * e) & (kLutCopies / 2 - 1);
-        if constexpr (kKcb) lut[(e * kLutCopies + c0 + cc) / 2] = kv;
-        lut[(kKcb ? kTableVecs : 0) + (e * kLutCopies + c0 + cc) / 2] = vv;
+    for (int i = 0; i < (16 + kParts - 1) / kParts; ++i) {
+        const int v = part + i * kParts;
+        if (kParts * i + kParts <= 16 || v < 16) {
+            const int slot = (v + e) & 15;
+            if constexpr (kKcb)
+                *reinterpret_cast<u32x4*>(lds + e * 256 + slot * 16 + (slot < 8 ? 0 : kKLoOffset - 128)) =
+                slot < 8 ? khi : klo;
+            *reinterpret_cast<u32x4*>(vt + e * 256 + slot * 16) = vv;
+        }
     }
 }
 
@@ -453,12 +491,11 @@ __device__ __forceinline__ LaneMap lane_map(int lane) {
 // ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-// Grid ceil(P / (4 R)) * Hkv * B (1-D), 4 waves, R = p.run partitions per wave.  For a split
-// sequence wave w of workgroup x owns the run of R consecutive partitions that starts at
-// partition plo + (4x + w) R (plo = the first partition the attended range touches), streams
-// through all of them without draining its load pipeline, and writes one triple for the whole
-// run (the online softmax merges its partitions as it goes) to the slot of the run's first
-// partition; the reduce merges the runs.  For an unsplit
+// Grid ceil(runs / W) * Hkv * B (1-D), W waves per workgroup.  For a split sequence wave w of
+// workgroup x owns run W x + w (split_runs: p.run_tokens consecutive tokens from the first
+// attended partition's start, at least one partition), streams through it without draining
+// its load pipeline, and writes one triple for the whole run (the online softmax merges as it
+// goes) to slot plo + W x + w; the reduce merges the runs.  For an unsplit
 // sequence (workgroup 0 only) the four waves share the attended range (consecutive quarters of
 // its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
@@ -467,7 +504,6 @@ template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE>
 __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) void partition_kernel(const LaunchParams p) {
     constexpr bool kKcb = k_codebook<FMT>();   // rotated query, K table, K norms
     constexpr bool kVcb = v_codebook<FMT>();   // V table, V norms, output in the rotated domain
-    constexpr int kTables = kKcb ? 2 : 1;      // codebook pair tables in LDS (V table last)
     constexpr int kW = waves_per_group(FMT);   // waves per workgroup
     constexpr int kThr = 64 * kW;
     constexpr int KS = D / 32;   // QK MFMA steps (k = 32 head elements each)
@@ -493,7 +529,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     };
     struct LdsTurbo {
         union {
-            u32x4 lut[kTables][256 * kLutCopies / 2];   // [K table,] V table (64 KB each)
+            u32x4 lut[(v_table_base<FMT>() + kVTableBytes) / 16];   // [K table,] V table
             Merge st;
         } u;
         float row[kMaxGroup * D];                 // query rotation / output rotation
@@ -577,16 +613,17 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         return;
     }
     // token range [lo, hi) of this wave (uniform per workgroup: whether any wave has work);
-    // split waves also track the partition being accumulated and where its tokens end
-    int lo, hi, part_end = 0, part_first = 0;
+    // split waves also track their workspace slot and the next partition boundary
+    int lo, hi, part_end = 0, run_slot = 0;
     if (si.split) {
-        const int plo = si.lo / p.part_size, phi = (si.L - 1) / p.part_size;
-        if (plo + xb * kW * p.run > phi) return;
-        part_first = plo + (xb * kW + wave) * p.run;
-        const int pend = min(part_first + p.run, phi + 1);
-        lo = max(si.lo, part_first * p.part_size);
-        hi = min(si.L, pend * p.part_size);
-        part_end = min(hi, (part_first + 1) * p.part_size);
+        int plo, base;
+        const int nruns = split_runs(p, si, plo, base);
+        if (xb * kW >= nruns) return;
+        const int i = xb * kW + wave;
+        run_slot = plo + i;
+        lo = max(si.lo, base + i * p.run_tokens);
+        hi = min(si.L, base + (i + 1) * p.run_tokens);
+        part_end = min(hi, (lo / p.part_size + 1) * p.part_size);
     } else {
         if (xb != 0) return;
         const int pg0 = (si.lo / kPageTokens) & ~1, pg1 = (si.L - 1) / kPageTokens + 1;
@@ -599,9 +636,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 
     const LaneMap ln = lane_map(lane);
     const int n = ln.n, j = ln.j;
-    const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;   // copy of this lane
-    const uint32_t kbase = lut_lane;                                      // K table (byte 0)
-    const uint32_t vbase = lut_lane | (kKcb ? 0x10000u : 0u);             // V table
+    // table copy of this lane: 4-byte K halves at byte 0, 8-byte V pairs after the K table
+    const uint32_t kbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
+    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 8u | (uint32_t)(v_table_base<FMT>() & 0x10000);
 
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
@@ -617,8 +654,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     const int tile_lo = MQ ? (si.W > 0 ? max(0, si.L - p.nq + (rbase + g - 1) / p.g + 1 - si.W) : 0)
                            : si.lo;
     u32x4 qop[KS];                      // BF16 / FP8 K: q (bf16) for step s
-    u32x4 qdup[kKcb ? KS : 1][2];       // codebook K: q hi, each pair repeated
-    u32x4 qlo0[kKcb ? KS : 1][2];       // codebook K: q lo pairs interleaved with zeros
+    u32x4 qhi[kKcb ? KS : 1];           // codebook K: fp16 hi parts of q for step s
+    u32x4 qlo[kKcb ? KS : 1];           // codebook K: fp16 lo parts
     float zscale;           // logit -> base-2 softmax argument (without per-token factors)
     float oscale = 1.0f;    // accumulator -> output units (FP8 V scale / codebook scales)
     float ksc = 1.0f;       // K table normaliser (codebook K)
@@ -628,8 +665,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         // [0.5, 1)), from the levels loaded at the start
         ksc = pow2_normaliser(lv.kmax);
         const float vsc = pow2_normaliser(lv.vmax);
-        static_assert(kThr == 2 * 256, "one thread pair per table entry");
-        fill_tables<FMT>(&lds.u.lut[0][0], tid, lv, ksc, vsc);
+        fill_tables<FMT, kThr>(reinterpret_cast<char*>(&lds.u.lut[0]), tid, lv, ksc, vsc);
         oscale = 1.0f / vsc;
         // the tables are complete before any wave's walk reads them (codebook K: the query
         // rotation's barriers below do the same)
@@ -677,10 +713,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                          h[i], l[i]);
                 if (!qlive) h[i] = l[i] = 0u;
             }
-            qdup[s][0] = u32x4{h[0], h[0], h[1], h[1]};
-            qdup[s][1] = u32x4{h[2], h[2], h[3], h[3]};
-            qlo0[s][0] = u32x4{l[0], 0u, l[1], 0u};
-            qlo0[s][1] = u32x4{l[2], 0u, l[3], 0u};
+            qhi[s] = u32x4{h[0], h[1], h[2], h[3]};
+            qlo[s] = u32x4{l[0], l[1], l[2], l[3]};
         }
         zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
     } else {
@@ -757,15 +791,13 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             for (int s = 0; s < KS; ++s) {
                 u32x4 x0, x1, y0, y1;
                 k_operands<FMT, D>(r, s, lds_bytes, kbase, x0, x1, y0, y1);
-                // two accumulator chains per tile halve the dependent-MFMA latency
-                sx = mfma_f16(x0, qdup[s][0], sx);     // (k hi + k lo) * q hi
-                sx2 = mfma_f16(x1, qdup[s][1], sx2);
-                sx = mfma_f16(x0, qlo0[s][0], sx);     // k hi * q lo
-                sx2 = mfma_f16(x1, qlo0[s][1], sx2);
-                sy = mfma_f16(y0, qdup[s][0], sy);
-                sy2 = mfma_f16(y1, qdup[s][1], sy2);
-                sy = mfma_f16(y0, qlo0[s][0], sy);
-                sy2 = mfma_f16(y1, qlo0[s][1], sy2);
+                // k hi * q hi + k lo * q hi + k hi * q lo, two accumulator chains per tile
+                sx = mfma_f16(x0, qhi[s], sx);
+                sx2 = mfma_f16(x1, qhi[s], sx2);
+                sy = mfma_f16(y0, qhi[s], sy);
+                sy2 = mfma_f16(y1, qhi[s], sy2);
+                sx2 = mfma_f16(x0, qlo[s], sx2);
+                sy2 = mfma_f16(y0, qlo[s], sy2);
             }
             sx += sx2;
             sy += sy2;
@@ -1012,7 +1044,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
         const float lx = lt > 0.0f ? lt * fast_exp2(m_run - m_true) : 0.0f;
         if (qlive) {
-            const size_t slot = row_index(n) * p.P + part_first;
+            const size_t slot = row_index(n) * p.P + run_slot;
 #pragma unroll
             for (int t = 0; t < VT; ++t)
                 *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
@@ -1071,9 +1103,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence x query of the chunk); lane l owns output elements
-// E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per run of p.run
-// partitions, at the slot of the run's first partition (runs start at the sequence's first
-// partition).  Triples are taken 64 at a time: each lane loads the (m, l) of one of them and
+// E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per run, at slots
+// plo .. plo + runs - 1 (split_runs).  Triples are taken 64 at a time: each lane loads the (m, l) of one of them and
 // then every lane loads its slice of all 64 outputs, so a block costs one memory round trip.
 // The block's weights are computed lane-parallel and broadcast with v_readlane; blocks after
 // the first rescale the running sums to the new maximum (online LSE).
@@ -1085,9 +1116,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     const int hq = blockIdx.x, bi = blockIdx.y, b = bi / p.nq, lane = threadIdx.x;
     const SeqInfo si = seq_info<true>(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
-    const int p0 = si.lo / p.part_size, p1 = (si.L - 1) / p.part_size;
-    const int R = p.run;
-    const int n = (p1 - p0 + R) / R;             // runs (triples) of the sequence
+    int p0, base;
+    const int n = split_runs(p, si, p0, base);   // runs (triples) of the sequence
     const size_t row = (size_t)bi * p.Hq + hq;   // out / workspace row (b, query, head)
     const float* ms = p.ws_m + row * p.P + p0;
     const float* ls = p.ws_l + row * p.P + p0;
@@ -1100,13 +1130,13 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     for (int base = 0; base < n; base += kBlock) {
         // indices past the end are clamped (their loads stay in bounds) and weighted 0
         const int q = min(base + lane, n - 1);
-        const float mq = ms[(size_t)q * R], lq = ls[(size_t)q * R];
+        const float mq = ms[q], lq = ls[q];
         float v[kBlock][E];
 #pragma unroll
         for (int u = 0; u < kBlock; ++u) {
             const int qq = min(base + u, n - 1);
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * R * D + e];
+            for (int e = 0; e < E; ++e) v[u][e] = os[(size_t)qq * D + e];
         }
         __builtin_amdgcn_sched_barrier(0);   // keep all of the block's loads ahead of any use
         const bool in = base + lane < n;
@@ -1225,24 +1255,24 @@ template <int FMT, int D>
 __global__ __launch_bounds__(512) void operand_kernel(const OperandParams op) {
     constexpr bool kKcb = k_codebook<FMT>();
     constexpr bool kVcb = v_codebook<FMT>();
-    constexpr int kTables = kKcb ? 2 : 1;
     constexpr int KS = D / 32, VT = D / 16, W = operand_words(D);
-    __shared__ u32x4 lut[kVcb ? kTables * 256 * kLutCopies / 2 : 1];
+    __shared__ u32x4 lut[kVcb ? (v_table_base<FMT>() + kVTableBytes) / 16 : 1];
     const LaunchParams& p = op.lp;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const char* const lds_bytes = reinterpret_cast<const char*>(lut);
     if constexpr (kVcb) {
         const Levels lv = load_levels<FMT>(p.codebook, p.kbits, tid);
-        fill_tables<FMT>(lut, tid, lv, pow2_normaliser(lv.kmax), pow2_normaliser(lv.vmax));
+        fill_tables<FMT, 512>(reinterpret_cast<char*>(lut), tid, lv, pow2_normaliser(lv.kmax),
+                              pow2_normaliser(lv.vmax));
         __syncthreads();
     }
     const int k = blockIdx.x * 8 + wave;
     if (k >= op.npairs) return;
     const int pair = op.pair0 + k;
     const LaneMap ln = lane_map(lane);
-    const uint32_t lut_lane = (uint32_t)(lane & (kLutCopies - 1)) * 8u;
-    const uint32_t kbase = lut_lane, vbase = lut_lane | (kKcb ? 0x10000u : 0u);
+    const uint32_t kbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
+    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 8u | (uint32_t)(v_table_base<FMT>() & 0x10000);
     uint32_t* rec = op.out + ((size_t)k * 64 + lane) * W;
     const int32_t* btrow = p.bt + (size_t)op.seq * p.max_blocks;
     const int pa = btrow[2 * pair], pb = btrow[2 * pair + 1];

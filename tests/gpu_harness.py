@@ -132,8 +132,8 @@ def merge_runs(parts, part_size, run):
     m) into the runs of ``run`` consecutive partitions the partition kernel merges (runs start
     at the first partition of the range), merging each run with the LSE rule:
     M = max m_i, l = sum l_i e^(m_i - M), o = sum l_i e^(m_i - M) o_i / l.  Rows with no key in a
-    run keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)], slot = the run's first
-    partition."""
+    run keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)]: run k of a range whose
+    first partition is p0 sits in workspace slot p0 + k."""
     if not parts:
         return []
     p0 = parts[0][0] // part_size
@@ -151,6 +151,6 @@ def merge_runs(parts, part_size, run):
         w = np.where(ls > 0, ls * np.exp(np.where(ls > 0, ms, 0.0) - safe), 0.0)
         L = w.sum(axis=0)
         O = np.einsum("pr,prd->rd", w, os_) / np.where(L > 0, L, 1.0)[:, None]
-        out.append((p0 + k * run, g[0][0], g[-1][1], M, L, O))
+        out.append((p0 + k, g[0][0], g[-1][1], M, L, O))
     return out
 

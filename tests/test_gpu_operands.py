@@ -54,6 +54,16 @@ def _interleaved(idx8, hi, lo):
     return np.array(words, dtype=np.uint32)
 
 
+def _split(idx8, hi, lo):
+    """Words [h0|h1, h2|h3, h4|h5, h6|h7] then [l0|l1, ..., l6|l7] of eight indices (the K-table
+    operands: hi parts, then lo parts)."""
+    h = [hi[i] for i in idx8]
+    l = [lo[i] for i in idx8]
+    return np.array([h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16,
+                     l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16],
+                    dtype=np.uint32)
+
+
 def _pairs_of_bits(b8):
     return np.array([b8[0] | b8[1] << 16, b8[2] | b8[3] << 16, b8[4] | b8[5] << 16,
                      b8[6] | b8[7] << 16], dtype=np.uint32)
@@ -104,7 +114,7 @@ def expected_records(inp, b, hk, n_pairs):
                                 nan[k, lane, w0 + e // 2] = True
                     else:
                         d = 32 * j + 8 * s_ + np.arange(8)
-                        rec[w0: w0 + 8] = _interleaved(ks[tok, d], kh, kl)
+                        rec[w0: w0 + 8] = _split(ks[tok, d], kh, kl)
             toks = (2 * k + v_sel) * 16 + v_pos0 + np.arange(8)
             for t in range(D // 16):
                 w0 = D // 2 + 8 * t

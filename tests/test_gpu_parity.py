@@ -409,11 +409,12 @@ def test_grouped_tiles_full_blocks_and_tail(fmt, run):
     formats) and a ragged tail that keeps the identity order.  Every unit must be computed once."""
     inp = _small(fmt, num_q_heads=48, num_kv_heads=2, context=None, ctx_range=(1, 6000),
                  num_seqs=5, seed=11)
-    ps = 256
-    # workgroup count of the partition launch: partition slots x KV heads x tiles x sequences
+    # workgroup count of the partition launch: ceil(runs / waves) x KV heads x tiles x sequences,
+    # runs = ceil(partitions / run) (waves per workgroup: 4 BF16 / FP8, 8 codebook formats)
     waves = 8 if fmt.startswith("turbo") else 4
+    ps = 256
     n_part = -(-6000 // ps)
-    grid = -(-n_part // (waves * run)) * 2 * 2 * 5
+    grid = -(-(-(-n_part // run)) // waves) * 2 * 2 * 5
     m = 2 * (2 if fmt.startswith("turbo") else 1)
     assert grid >= 8 * m and grid % (8 * m) != 0, grid
     got = GpuBatch(inp, partition_size=ps, partitions_per_wave=run).run()
