@@ -70,14 +70,18 @@
  *                         bit k = bit k%8 of byte k/8; 4-bit: even e in the low nibble).
  *                         V (both Turbo formats, 4-bit): [D][16 nibbles = 8 B] -- index of
  *                         (t, d) is nibble t of row d (even t in the low nibble).
- *                         k_chunk = 8*D (TURBO4) or 6*D (TURBO3), v_chunk = 8*D bytes.
+ *                         After the indices of every K and V chunk: norm[16], the fp32
+ *                         (little-endian) per-token norms of the page's 16 slots, so one page
+ *                         of one head is one contiguous record.
+ *                         k_chunk = 8*D + 64 (TURBO4) or 6*D + 64 (TURBO3), v_chunk = 8*D + 64.
  *                         Stored value in the rotated domain: norm[t] * codebook[index];
  *                         the original vector is  x = diag(s) H x_rot / sqrt(D), H the
  *                         Sylvester-order D x D Hadamard matrix, s = sign_pattern.
  *   TURBO8 (KVD_TURBO8)   FP8 K + 4-bit V ("FP8 K + 4-bit V (Walsh-Hadamard)" in the formats
  *                         table; reading: K exactly as the FP8 format stores it -- not
  *                         rotated, one fp32 scale per KV head -- and V exactly as the Turbo
- *                         formats store it).  k_chunk = 16*D, v_chunk = 8*D bytes.
+ *                         formats store it, norms included).  k_chunk = 16*D,
+ *                         v_chunk = 8*D + 64 bytes.
  *
  * Query q: bf16 [num_seqs][n_q][num_q_heads][D] (n_q = 1: [num_seqs][num_q_heads][D]).
  * Output out: fp32 with the same shape, in the original (un-rotated) domain for every format.
@@ -160,10 +164,9 @@ size_t kvd_workspace_bytes(const kvd_dims* dims);
  *                range [lo, L) must be valid pool indices (others are never read)
  *   context_lens int32 [B]; 0 gives an all-zero output row
  *   fmt          a kvd_format
- *   scales       KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv], K scales then V;
- *                KVD_TURBO4/3: fp32 per-token norms [2][num_pool_blocks][Hkv][16], K then V;
- *                KVD_TURBO8: fp32 V norms [num_pool_blocks][Hkv][16] followed by the [Hkv]
- *                K scales (num_pool_blocks * Hkv * 16 + Hkv floats)
+ *   scales       KVD_FP8_E4M3: fp32 [2][Hkv], K scales then V; KVD_TURBO8: fp32 [Hkv], the K
+ *                scales; KVD_BF16 / KVD_TURBO4 / KVD_TURBO3: unused, may be NULL (the Turbo
+ *                per-token norms live in the cache chunks)
  *   codebook     KVD_TURBO4/3: fp32 levels, 2^kbits for K then 16 for V (kbits 4 or 3);
  *                KVD_TURBO8: the 16 V levels; else unused
  *   sign_pattern Turbo: fp32 [D] of +1.0 / -1.0; else unused
@@ -277,7 +280,7 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
  *   v1 = 0; codebook V: v0 = fp16 [h0 h1 l0 l1 h2 h3 l2 l3] of tokens 0..3, v1 of 4..7 (V
  *   levels, normaliser of the V levels).
  * Words [D, D + 16): fp32 K norms of the eight softmax tokens (Turbo4/3; else 0), then their
- *   V norms (codebook V; else 0).
+ *   V norms (codebook V; else 0), as stored after the chunks' indices.
  * A pair with a block-table entry outside the pool gets all-ones records. */
 int kvd_dequant_operands(const kvd_dims* dims, int fmt, const void* k_cache,
                          const void* v_cache, const float* scales, const float* codebook,
@@ -298,10 +301,9 @@ int kvd_dequant_operands(const kvd_dims* dims, int fmt, const void* k_cache,
  *                 block_table[b][(positions[b] + i) / 16], slot (positions[b] + i) % 16)
  *   n_new         tokens per sequence in this call (>= 0; 0 does nothing)
  *   k_cache, v_cache  the pools, updated in place (other tokens' bytes are preserved)
- *   scales        KVD_BF16: unused (may be NULL); KVD_FP8_E4M3: fp32 [2][Hkv] per-head scales
- *                 (read); KVD_TURBO4/3: fp32 per-token norms [2][num_pool_blocks][Hkv][16]
- *                 (written); KVD_TURBO8: the V norms (written) and K scales (read), laid out
- *                 as for kvd_decode_attn_paged
+ *   scales        KVD_FP8_E4M3: fp32 [2][Hkv] per-head scales; KVD_TURBO8: fp32 [Hkv] K scales;
+ *                 else unused, may be NULL (read only: Turbo norms are written into the
+ *                 chunks)
  *   codebook, sign_pattern  Turbo: as for kvd_decode_attn_paged; else unused
  * Codes, decided exactly (readings where the pages are silent):
  *   BF16  round to nearest even; NaN stored as 0x7FC0.
@@ -315,7 +317,7 @@ int kvd_dequant_operands(const kvd_dims* dims, int fmt, const void* k_cache,
  * overlap in time on different streams must not write the same page. */
 int kvd_append_kv(const kvd_dims* dims, int fmt, const float* k_new, const float* v_new,
                   const int32_t* block_table, const int32_t* positions, int32_t n_new,
-                  void* k_cache, void* v_cache, float* scales, const float* codebook,
+                  void* k_cache, void* v_cache, const float* scales, const float* codebook,
                   const float* sign_pattern, void* stream);
 
 /* A static, human-readable name for a status code. */

@@ -124,20 +124,33 @@ def spec(name: str, **overrides) -> Spec:
 # --------------------------------------------------------------------------------------------
 # Byte sizes of the paged layout (documented in include/kvdecode.h)
 # --------------------------------------------------------------------------------------------
-def k_chunk_bytes(fmt: str, d: int) -> int:
-    """Bytes of one (page, KV head) chunk of the K cache."""
+NORM_BYTES = 4 * BLOCK_SIZE   # the 16 fp32 per-token norms after a codebook chunk's indices
+
+
+def k_code_bytes(fmt: str, d: int) -> int:
+    """Bytes of stored K elements at the start of one (page, KV head) chunk."""
     return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 6 * d, "turbo8": 16 * d}[fmt]
 
 
-def v_chunk_bytes(fmt: str, d: int) -> int:
-    """Bytes of one (page, KV head) chunk of the V cache (Turbo V is always 4-bit)."""
+def v_code_bytes(fmt: str, d: int) -> int:
+    """Bytes of stored V elements at the start of one chunk (Turbo V is always 4-bit)."""
     return {"bf16": 32 * d, "fp8": 16 * d, "turbo4": 8 * d, "turbo3": 8 * d, "turbo8": 8 * d}[fmt]
 
 
+def k_chunk_bytes(fmt: str, d: int) -> int:
+    """Bytes of one (page, KV head) chunk of the K cache (codebook K: indices, then norms)."""
+    return k_code_bytes(fmt, d) + (NORM_BYTES if fmt in KV_BITS else 0)
+
+
+def v_chunk_bytes(fmt: str, d: int) -> int:
+    """Bytes of one (page, KV head) chunk of the V cache (codebook V: indices, then norms)."""
+    return v_code_bytes(fmt, d) + (NORM_BYTES if v_is_codebook(fmt) else 0)
+
+
 def kv_bytes_per_token_head(fmt: str, d: int) -> int:
-    """Algorithmic cache bytes the method must read per (token, KV head), K + V (+ norms)."""
-    norms = 8 if fmt in KV_BITS else (4 if fmt == "turbo8" else 0)
-    return (k_chunk_bytes(fmt, d) + v_chunk_bytes(fmt, d)) // BLOCK_SIZE + norms
+    """Algorithmic cache bytes the method must read per (token, KV head), K + V (norms
+    included)."""
+    return (k_chunk_bytes(fmt, d) + v_chunk_bytes(fmt, d)) // BLOCK_SIZE
 
 
 # --------------------------------------------------------------------------------------------
@@ -326,8 +339,8 @@ class Inputs:
     q: np.ndarray                 # uint16 [B, Hq, D] bf16 bits ([B, n_q, Hq, D] for n_q > 1)
     k_cache: np.ndarray           # uint8 [pool, Hkv, k_chunk_bytes]
     v_cache: np.ndarray           # uint8 [pool, Hkv, v_chunk_bytes]
-    scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo4/3: f32 [2, pool, Hkv, 16];
-                                  # turbo8: f32 [pool*Hkv*16 + Hkv] (V norms, then K scales);
+    scales: np.ndarray | None     # fp8: f32 [2, Hkv]; turbo8: f32 [Hkv] K scales; else None
+                                  # (codebook norms live inside the cache chunks);
                                   # bf16: None
     codebook: np.ndarray | None   # turbo4/3: f32 [2^kbits + 16] (K levels then V levels);
                                   # turbo8: f32 [16] (V levels)
@@ -526,8 +539,8 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
         ve = np.concatenate([ve, np.full((Hkv, pad, D), vfill, ve.dtype)], axis=1)
         ke = ke.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
         ve = ve.reshape(Hkv, npg, BLOCK_SIZE, D).transpose(1, 0, 2, 3)
-        k_cache[phys] = pack_k_pages(fmt, ke)
-        v_cache[phys] = pack_v_pages(fmt, ve)
+        k_cache[phys, :, : k_code_bytes(fmt, D)] = pack_k_pages(fmt, ke)
+        v_cache[phys, :, : v_code_bytes(fmt, D)] = pack_v_pages(fmt, ve)
         first_key = Lb - s.queries_per_seq + 1 - int(W[b])   # of the chunk's first query
         if poison_before_window and W[b] > 0 and first_key > 0:
             first_live = first_key // BLOCK_SIZE
@@ -544,10 +557,13 @@ def make_inputs(s: Spec, *, poison: bool = True, poison_before_window: bool = Fa
     with ThreadPoolExecutor(workers) as ex:
         list(ex.map(fill_seq, range(B)))
 
-    if fmt in KV_BITS:
-        scales = np.stack([knorm, vnorm])
-    elif fmt == "turbo8":
-        scales = np.concatenate([vnorm.reshape(-1), kscale]).astype(np.float32)
+    # per-token norms: 16 little-endian fp32 after the indices of each (page, KV head) chunk
+    if knorm is not None:
+        k_cache[:, :, k_code_bytes(fmt, D):] = knorm.astype("<f4").view(np.uint8).reshape(pool, Hkv, -1)
+    if vnorm is not None:
+        v_cache[:, :, v_code_bytes(fmt, D):] = vnorm.astype("<f4").view(np.uint8).reshape(pool, Hkv, -1)
+    if fmt == "turbo8":
+        scales = np.asarray(kscale, dtype=np.float32).copy()
     return Inputs(spec=s, q=q, k_cache=k_cache, v_cache=v_cache, scales=scales,
                   codebook=codebook_arr, sign=sgn, block_table=bt, context_lens=L, window=W,
                   softmax_scale=s.scale, softcap=np.float32(s.softcap), max_context_len=max_ctx)
@@ -562,17 +578,7 @@ def relayout(inp: Inputs, seed: int) -> Inputs:
     v = np.empty_like(inp.v_cache)
     k[new_of_old] = inp.k_cache
     v[new_of_old] = inp.v_cache
-    sc = inp.scales
-    if sc is not None and sc.ndim == 4:
-        sc = np.empty_like(inp.scales)
-        sc[:, new_of_old] = inp.scales
-    elif inp.spec.fmt == "turbo8":
-        hkv = inp.spec.num_kv_heads
-        vn = inp.scales[:-hkv].reshape(pool, hkv, BLOCK_SIZE)
-        moved = np.empty_like(vn)
-        moved[new_of_old] = vn
-        sc = np.concatenate([moved.reshape(-1), inp.scales[-hkv:]])
     bt = inp.block_table.copy()
     ok = bt >= 0
     bt[ok] = new_of_old[bt[ok]]
-    return dataclasses.replace(inp, k_cache=k, v_cache=v, scales=sc, block_table=bt)
+    return dataclasses.replace(inp, k_cache=k, v_cache=v, block_table=bt)

@@ -23,11 +23,12 @@ Readings taken where the pages are silent (the header of the library states the 
   * ALiBi (the "ALiBi slopes" feature of the attention.rs README): query head h at position
     L - 1 adds slope_h * (j - (L - 1)) to its logit for key j, after the softcap;
   * rotated codebook: stored vector = norm * codebook[idx] in the rotated domain; the original
-    vector is diag(s) H (that) / sqrt(D), H the Sylvester-order Hadamard matrix;
+    vector is diag(s) H (that) / sqrt(D), H the Sylvester-order Hadamard matrix; the 16 fp32
+    per-token norms of a page follow its index bytes inside the (page, KV head) chunk;
   * FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN) times one fp32 scale per KV head;
   * Turbo8 = K exactly as the FP8 format stores it (one scale per KV head, not rotated) and V
     exactly as Turbo4 stores it (rotated 4-bit codebook with per-token norms).  Its scale array
-    is [pool][Hkv][16] V norms followed by the [Hkv] K scales; its codebook is the 16 V levels.
+    is the [Hkv] K scales; its codebook is the 16 V levels.
 
 Everything here is fp64; bf16 / fp8 / codebook values are widened exactly.
 """
@@ -54,17 +55,29 @@ def elem_kind(fmt: str, which: str) -> str:
 def fp8_scale(fmt: str, scales, which: str, hk: int, hkv: int):
     """The fp32 dequantisation scale of an FP8-stored K or V of KV head hk (of hkv)."""
     sc = np.asarray(scales)
-    if fmt == "turbo8":                      # the last hkv floats are the K scales
-        return sc.reshape(-1)[sc.size - hkv + hk]
+    if fmt == "turbo8":                      # [Hkv]: the K scales
+        return sc.reshape(-1)[hk]
     return sc[0 if which == "k" else 1, hk]
 
 
-def norm_plane(fmt: str, scales, which: str, pool: int, hkv: int) -> np.ndarray:
-    """The [pool][Hkv][16] per-token norms of a codebook-stored K or V."""
-    sc = np.asarray(scales)
-    if fmt == "turbo8":
-        return sc.reshape(-1)[: pool * hkv * BLOCK].reshape(pool, hkv, BLOCK)
-    return sc[0 if which == "k" else 1]
+def code_bytes(fmt: str, which: str, d: int) -> int:
+    """Bytes of stored elements at the start of one (page, KV head) chunk: 16 tokens x D
+    elements of 16 (bf16), 8 (fp8) or 4 / 3 (codebook index) bits."""
+    kind = elem_kind(fmt, which)
+    if kind == "bf16":
+        return 32 * d
+    if kind == "fp8":
+        return 16 * d
+    bits = _FMT_BITS[fmt][0] if which == "k" and fmt in _FMT_BITS else 4
+    return 2 * bits * d
+
+
+def chunk_norms(fmt: str, which: str, cache: np.ndarray, d: int) -> np.ndarray:
+    """The per-token norms [pool][Hkv][16] of a codebook-stored K or V: 16 little-endian fp32
+    values right after each chunk's index bytes."""
+    c = code_bytes(fmt, which, d)
+    raw = np.ascontiguousarray(np.asarray(cache)[:, :, c: c + 4 * BLOCK])
+    return raw.view("<f4").reshape(cache.shape[0], cache.shape[1], BLOCK)
 
 
 # --------------------------------------------------------------------------------------------
@@ -115,6 +128,7 @@ def unpack_le(buf: np.ndarray, bits: int) -> np.ndarray:
 def _page_elems_k(fmt: str, chunk: np.ndarray, d: int) -> np.ndarray:
     """One K chunk (uint8 bytes) -> stored elements [16 tokens, D] (bf16 bits / fp8 codes /
     codebook indices), reading the layout the header documents."""
+    chunk = chunk[: code_bytes(fmt, "k", d)]
     if fmt == "bf16":     # [D/8][16 tokens][8] bf16
         x = chunk.view(np.uint16).reshape(d // 8, BLOCK, 8)
         return x.transpose(1, 0, 2).reshape(BLOCK, d)
@@ -130,6 +144,7 @@ def _page_elems_k(fmt: str, chunk: np.ndarray, d: int) -> np.ndarray:
 
 def _page_elems_v(fmt: str, chunk: np.ndarray, d: int) -> np.ndarray:
     """One V chunk -> stored elements [16 tokens, D]; V is stored transposed, [D][16]."""
+    chunk = chunk[: code_bytes(fmt, "v", d)]
     if fmt == "bf16":
         return chunk.view(np.uint16).reshape(d, BLOCK).T
     if fmt == "fp8":
@@ -150,11 +165,15 @@ def gather_stored(fmt: str, which: str, cache: np.ndarray, block_table_row: np.n
     return out
 
 
-def gather_norms(norms: np.ndarray, block_table_row: np.ndarray, hk: int, t0: int, t1: int):
-    """Per-token fp32 norms [pool][Hkv][16] of tokens [t0, t1), as float64."""
+def token_norms(fmt: str, which: str, cache: np.ndarray, block_table_row: np.ndarray, hk: int,
+                t0: int, t1: int, d: int) -> np.ndarray:
+    """Per-token fp32 norms of tokens [t0, t1) of a codebook-stored K or V (the 16 fp32 values
+    after each chunk's index bytes), as float32."""
     j = np.arange(t0, t1)
     phys = np.asarray(block_table_row)[j // BLOCK]
-    return norms[phys, hk, j % BLOCK].astype(np.float64)
+    c = code_bytes(fmt, which, d)
+    raw = np.ascontiguousarray(np.asarray(cache)[phys, hk, c: c + 4 * BLOCK])
+    return raw.view("<f4").reshape(len(j), BLOCK)[np.arange(len(j)), j % BLOCK]
 
 
 def unrotate(x_rot: np.ndarray, sign: np.ndarray) -> np.ndarray:
@@ -183,7 +202,7 @@ def gather_kv(fmt: str, which: str, cache, block_table_row, hk, t0, t1, d, *, sc
         return bf16_to_f64(stored)
     if kind == "fp8":
         return E4M3FN_TABLE[stored] * np.float64(np.float32(fp8_scale(fmt, scales, which, hk, hkv)))
-    norms = gather_norms(norm_plane(fmt, scales, which, pool, hkv), block_table_row, hk, t0, t1)
+    norms = token_norms(fmt, which, cache, block_table_row, hk, t0, t1, d).astype(np.float64)
     cb = codebooks(fmt, codebook)[0 if which == "k" else 1]
     return unrotate(norms[:, None] * cb.astype(np.float64)[stored], sign)
 
@@ -353,8 +372,6 @@ def dequant_gather(fmt, which, cache, scales, codebook, block_table_row, hk, t0,
     if kind == "fp8":
         sc = np.float32(fp8_scale(fmt, scales, which, hk, hkv))
         return E4M3FN_TABLE[stored].astype(np.float32) * sc
-    norms = norm_plane(fmt, scales, which, pool, hkv)
-    j = np.arange(t0, t0 + n)
-    nrm = norms[np.asarray(block_table_row)[j // BLOCK], hk, j % BLOCK].astype(np.float32)
+    nrm = token_norms(fmt, which, cache, block_table_row, hk, t0, t0 + n, d)
     cb = codebooks(fmt, codebook)[0 if which == "k" else 1].astype(np.float32)
     return nrm[:, None] * cb[stored]

@@ -53,7 +53,7 @@ def _k_elem(fmt, kc, phys, hk, nkv, slot, d, D):
         return ("v", _e4m3(int(kc[base + ((d // 16) * BLOCK + slot) * 16 + d % 16])))
     bits = 4 if fmt == "turbo4" else 3
     gbytes = 4 * bits                           # 32 indices per group
-    base = (phys * nkv + hk) * (D // 32) * BLOCK * gbytes
+    base = (phys * nkv + hk) * ((D // 32) * BLOCK * gbytes + 4 * BLOCK)   # + 16 fp32 norms
     grp = base + ((d // 32) * BLOCK + slot) * gbytes
     return ("i", _bits_le(kc[grp: grp + gbytes], (d % 32) * bits, bits))
 
@@ -64,8 +64,16 @@ def _v_elem(fmt, vc, phys, hk, nkv, slot, d, D):
         return ("v", _bf16(int(vc[off]), int(vc[off + 1])))
     if fmt == "fp8":
         return ("v", _e4m3(int(vc[(phys * nkv + hk) * 16 * D + d * BLOCK + slot])))
-    row = (phys * nkv + hk) * 8 * D + d * 8
+    row = (phys * nkv + hk) * (8 * D + 4 * BLOCK) + d * 8     # chunk: 8 D index bytes, 16 norms
     return ("i", _bits_le(vc[row: row + 8], slot * 4, 4))
+
+
+def _norm(fmt, which, cache_flat, phys, hk, nkv, slot, D):
+    """The fp32 norm of token `slot`, stored after the index bytes of its (page, KV head) chunk
+    (little-endian)."""
+    codes = (D * 4 if fmt == "turbo4" else D * 3) * 2 if which == "k" else 8 * D
+    off = (phys * nkv + hk) * (codes + 4 * BLOCK) + codes + 4 * slot
+    return Decimal(struct.unpack("<f", bytes(int(cache_flat[off + i]) for i in range(4)))[0])
 
 
 def _hadamard_entry(i: int, j: int) -> int:
@@ -81,18 +89,16 @@ def _token_vector(fmt, which, cache_flat, phys, hk, nkv, slot, D, scales, codebo
     if fmt == "fp8":
         s = _f32(scales[wi][hk])
         return [x * s for _, x in raw]
-    flat = [float(x) for x in scales.reshape(-1)] if fmt == "turbo8" else None
-    if fmt == "turbo8" and which == "k":       # K scale of head hk: the last nkv floats
-        s = _f32(flat[len(flat) - nkv + hk])
+    if fmt == "turbo8" and which == "k":       # K scale of head hk: scales = [Hkv]
+        s = _f32(scales.reshape(-1)[hk])
         return [x * s for _, x in raw]
     levels = [_f32(c) for c in codebook]
-    if fmt == "turbo8":                        # 16 V levels; V norms [pool][nkv][16] first
+    if fmt == "turbo8":                        # the 16 V levels
         table = levels[:16]
-        norm = _f32(flat[(phys * nkv + hk) * BLOCK + slot])
     else:
         kbits = 4 if fmt == "turbo4" else 3
         table = levels[: 1 << kbits] if which == "k" else levels[1 << kbits: (1 << kbits) + 16]
-        norm = _f32(scales[wi][phys][hk][slot])
+    norm = _norm(fmt, which, cache_flat, phys, hk, nkv, slot, D)
     rot = [norm * table[i] for _, i in raw]
     root = Decimal(D).sqrt()
     return [_f32(sign[d]) * sum(_hadamard_entry(d, e) * rot[e] for e in range(D)) / root

@@ -34,7 +34,8 @@ import math
 
 import numpy as np
 
-from .attention import BLOCK, _FMT_BITS, _page_elems_k, _page_elems_v, elem_kind, fp8_scale
+from .attention import (BLOCK, _FMT_BITS, _page_elems_k, _page_elems_v, code_bytes, elem_kind,
+                        fp8_scale)
 
 
 # --------------------------------------------------------------------------------------------
@@ -192,9 +193,9 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
     k_new, v_new: fp32 [B][T][Hkv][D]; new token i of sequence b is token positions[b] + i,
     stored in page block_table[b][(positions[b] + i) // 16], slot (positions[b] + i) % 16.
     Tokens whose page index lies past the block table row, or whose page id lies outside the
-    pool, are skipped.  Returns (k_cache, v_cache, scales); for the rotated formats the
-    per-token norms go to scales [2][pool][Hkv][16] (Turbo8: V norms to the [pool][Hkv][16]
-    head of its flat scale array)."""
+    pool, are skipped.  Returns (k_cache, v_cache, scales); for the rotated formats each
+    per-token norm goes to its slot of the 16 fp32 values after the chunk's indices (scales,
+    read for FP8 and Turbo8 K, is returned unchanged)."""
     k_cache = np.array(k_cache, copy=True)
     v_cache = np.array(v_cache, copy=True)
     scales = None if scales is None else np.array(scales, copy=True)
@@ -221,9 +222,9 @@ def append_tokens(fmt: str, k_new, v_new, block_table, positions, k_cache, v_cac
                     pack = _pack_k_chunk if which == "k" else _pack_v_chunk
                     elems = np.array(read(fmt, chunk, d), dtype=np.int64)
                     elems[slot] = el[0]
-                    cache[phys, hk] = pack(fmt, elems, d)
-                    if norm is not None and fmt == "turbo8":
-                        scales[(phys * Hkv + hk) * BLOCK + slot] = norm[0]
-                    elif norm is not None:
-                        scales[0 if which == "k" else 1, phys, hk, slot] = norm[0]
+                    c = code_bytes(fmt, which, d)
+                    cache[phys, hk, :c] = pack(fmt, elems, d)
+                    if norm is not None:    # fp32 little-endian, after the indices
+                        off = c + 4 * slot
+                        cache[phys, hk, off: off + 4] = np.array([norm[0]], "<f4").view(np.uint8)
     return k_cache, v_cache, scales

@@ -18,18 +18,23 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Bytes of one (page, KV head) chunk; codebook-stored K or V end with the page's 16 fp32
+// per-token norms (64 bytes).
 int64_t k_chunk_bytes(int fmt, int d) {
     switch (fmt) {
         case KVD_BF16: return 32LL * d;
         case KVD_FP8_E4M3:
         case KVD_TURBO8: return 16LL * d;   // Turbo8 K is stored as FP8 K
-        case KVD_TURBO4: return 8LL * d;
-        default: return 6LL * d;
+        case KVD_TURBO4: return 8LL * d + 64;
+        default: return 6LL * d + 64;
     }
 }
 int64_t v_chunk_bytes(int fmt, int d) {
-    return fmt == KVD_BF16 ? 32LL * d : (fmt == KVD_FP8_E4M3 ? 16LL * d : 8LL * d);
+    return fmt == KVD_BF16 ? 32LL * d : (fmt == KVD_FP8_E4M3 ? 16LL * d : 8LL * d + 64);
 }
+
+// Formats that read a scale array: FP8 ([2][Hkv]) and Turbo8 ([Hkv] K scales).
+bool needs_scales(int fmt) { return fmt == KVD_FP8_E4M3 || fmt == KVD_TURBO8; }
 
 struct Plan {
     int mode;        // kvd::PartMode
@@ -164,8 +169,8 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     int st = check_dims(d, fmt);
     if (st != KVD_OK) return st;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out) return KVD_ERR_NULL;
-    if (fmt == KVD_FP8_E4M3 && !scales) return KVD_ERR_NULL;
-    if (fmt >= KVD_TURBO4 && (!scales || !codebook || !sign_pattern)) return KVD_ERR_NULL;
+    if (needs_scales(fmt) && !scales) return KVD_ERR_NULL;
+    if (fmt >= KVD_TURBO4 && (!codebook || !sign_pattern)) return KVD_ERR_NULL;
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(block_table, 4) || !aligned(context_lens, 4) || (window && !aligned(window, 4)) ||
         (scales && !aligned(scales, 16)) || (codebook && !aligned(codebook, 4)) ||
@@ -300,7 +305,7 @@ int kvd_dequant_gather(const kvd_dims* d, int fmt, int is_v, const void* cache,
     int st = check_dims(d, fmt);
     if (st != KVD_OK) return st;
     if (!cache || !block_table || !out) return KVD_ERR_NULL;
-    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (needs_scales(fmt) && !scales) return KVD_ERR_NULL;
     if (fmt >= KVD_TURBO4 && !codebook) return KVD_ERR_NULL;
     if (!aligned(cache, 16) || !aligned(out, 4) || !aligned(block_table, 4) ||
         (scales && !aligned(scales, 4)))
@@ -340,7 +345,7 @@ int kvd_dequant_operands(const kvd_dims* d, int fmt, const void* k_cache, const 
     int st = check_dims(d, fmt);
     if (st != KVD_OK) return st;
     if (!k_cache || !v_cache || !block_table || !out) return KVD_ERR_NULL;
-    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (needs_scales(fmt) && !scales) return KVD_ERR_NULL;
     if (fmt >= KVD_TURBO4 && !codebook) return KVD_ERR_NULL;
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
         !aligned(block_table, 4) || (scales && !aligned(scales, 16)) ||
@@ -380,13 +385,13 @@ int kvd_dequant_operands(const kvd_dims* d, int fmt, const void* k_cache, const 
 
 int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v_new,
                   const int32_t* block_table, const int32_t* positions, int32_t n_new,
-                  void* k_cache, void* v_cache, float* scales, const float* codebook,
+                  void* k_cache, void* v_cache, const float* scales, const float* codebook,
                   const float* sign_pattern, void* stream) {
     int st = check_dims(d, fmt);
     if (st != KVD_OK) return st;
     if (n_new < 0) return KVD_ERR_SHAPE;
     if (!k_new || !v_new || !block_table || !positions || !k_cache || !v_cache) return KVD_ERR_NULL;
-    if (fmt != KVD_BF16 && !scales) return KVD_ERR_NULL;
+    if (needs_scales(fmt) && !scales) return KVD_ERR_NULL;
     if (fmt >= KVD_TURBO4 && (!codebook || !sign_pattern)) return KVD_ERR_NULL;
     if (!aligned(k_new, 8) || !aligned(v_new, 8) || !aligned(block_table, 4) ||
         !aligned(positions, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||

@@ -77,18 +77,17 @@ __device__ __forceinline__ uint32_t count_below(const double* mid, int n, double
 }
 
 // One token vector (this lane's part of it) into the LDS image of its page: K chunk at byte 0,
-// V chunk at byte k_chunk.  Writes the token's norm (codebook formats) to the scale array.
+// V chunk at byte k_chunk.  A codebook-stored token's fp32 norm goes to its slot of the 16
+// norms after the chunk's indices (chunk_bytes - 64).
 // mids: the level midpoints of K (row 0) and V (row 1), fp64, in LDS.
 __device__ __forceinline__ void encode_token(const AppendParams& p, int which, const float* src,
                                              uint8_t* chunk, const double (*mids)[16],
-                                             int t, int hk, size_t head, int lane) {
-    const size_t norm_plane = (size_t)p.pool * p.Hkv * kPageTokens;   // floats per norm plane
+                                             int t, int hk, int lane) {
     const bool t8 = p.fmt == KVD_TURBO8;
     const bool fp8 = p.fmt == KVD_FP8_E4M3 || (t8 && which == 0);   // Turbo8 K is FP8 K
     if (p.fmt == KVD_BF16 || fp8) {
-        // FP8: scales [2][Hkv]; Turbo8: the K scales follow the V norms
-        const float scale = !fp8 ? 1.0f
-                          : t8 ? p.scales[norm_plane + hk] : p.scales[which * p.Hkv + hk];
+        // FP8: scales [2][Hkv]; Turbo8: the [Hkv] K scales
+        const float scale = !fp8 ? 1.0f : t8 ? p.scales[hk] : p.scales[which * p.Hkv + hk];
         for (int d = lane; d < p.D; d += 64) {
             const float x = src[d];
             if (p.fmt == KVD_BF16) {
@@ -133,8 +132,8 @@ __device__ __forceinline__ void encode_token(const AppendParams& p, int which, c
 
     const int nmid = (which ? 16 : 1 << p.kbits) - 1;
     const uint32_t i0 = count_below(mids[which], nmid, u0), i1 = count_below(mids[which], nmid, u1);
-    if (lane == 0)   // norm planes K then V (Turbo8: the V plane only)
-        p.scales[(which && !t8 ? norm_plane : 0) + head * kPageTokens + t] = norm;
+    if (lane == 0)   // after the chunk's indices
+        reinterpret_cast<float*>(chunk + (which ? p.v_chunk : p.k_chunk) - 64)[t] = norm;
 
     if (which == 1) {   // V [D][8 B]: nibble t of rows e0 and e0 + 1 (words shared with the
                         // other waves' tokens: clear, then set, with LDS atomics)
@@ -214,8 +213,8 @@ __global__ __launch_bounds__(64 * kAppendWaves) void append_kernel(const AppendP
     if (t >= t_lo && t < t_hi) {
         const int64_t i = pg * kPageTokens + t - pos;            // index among the call's tokens
         const size_t row = ((size_t)b * p.T + (size_t)i) * p.Hkv + hk;
-        encode_token(p, 0, p.k_new + row * p.D, image, mids, t, hk, head, lane);
-        encode_token(p, 1, p.v_new + row * p.D, image + p.k_chunk, mids, t, hk, head, lane);
+        encode_token(p, 0, p.k_new + row * p.D, image, mids, t, hk, lane);
+        encode_token(p, 1, p.v_new + row * p.D, image + p.k_chunk, mids, t, hk, lane);
     }
     __syncthreads();
 

@@ -50,8 +50,8 @@ struct LaunchParams {
     const int32_t* bt;        // [B][max_blocks]
     const int32_t* ctx;       // [B]
     const int32_t* win;       // [B] or nullptr
-    const float* scales;      // fp8 [2][Hkv]; turbo4/3 norms [2][pool][Hkv][16];
-                              // turbo8 [pool][Hkv][16] V norms then [Hkv] K scales
+    const float* scales;      // fp8 [2][Hkv]; turbo8 [Hkv] K scales; else unused (the
+                              // codebook norms sit inside the cache chunks)
     const float* codebook;    // turbo levels (K then V; turbo8: V only)
     const float* sign;        // turbo [D]
     const float* alibi;       // [Hq] ALiBi slopes or nullptr
@@ -104,8 +104,7 @@ struct AppendParams {
     const int32_t* pos;       // [B] token index of each sequence's first new token
     uint8_t* k;               // K pool
     uint8_t* v;               // V pool
-    float* scales;            // FP8: [2][Hkv] (read); Turbo4/3: [2][pool][Hkv][16] (written);
-                              // Turbo8: [pool][Hkv][16] V norms (written), then [Hkv] K scales (read)
+    const float* scales;      // FP8: [2][Hkv]; Turbo8: [Hkv] K scales (read); else unused
     const float* codebook;    // codebook formats: K levels then 16 V levels (Turbo8: V levels)
     const float* sign;        // codebook formats: [D]
     int64_t k_chunk, v_chunk;

@@ -91,9 +91,15 @@ constexpr bool v_codebook() { return k_codebook<FMT>() || FMT == KVD_TURBO8; }
 template <int FMT>
 constexpr int v_table_base() { return k_codebook<FMT>() ? kKTableBytes : 0; }
 template <int FMT, int D>
-constexpr int k_chunk() { return FMT == KVD_BF16 ? 32 * D : k_fp8<FMT>() ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
+constexpr int k_code() { return FMT == KVD_BF16 ? 32 * D : k_fp8<FMT>() ? 16 * D : FMT == KVD_TURBO4 ? 8 * D : 6 * D; }
 template <int FMT, int D>
-constexpr int v_chunk() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : 8 * D; }
+constexpr int v_code() { return FMT == KVD_BF16 ? 32 * D : FMT == KVD_FP8_E4M3 ? 16 * D : 8 * D; }
+// Bytes of one (page, KV head) chunk: the stored elements, then (codebook-stored K or V) the 16
+// fp32 per-token norms of the page.
+template <int FMT, int D>
+constexpr int k_chunk() { return k_code<FMT, D>() + (k_codebook<FMT>() ? 64 : 0); }
+template <int FMT, int D>
+constexpr int v_chunk() { return v_code<FMT, D>() + (v_codebook<FMT>() ? 64 : 0); }
 
 // ------------------------------------------------------------------------------------------
 // small helpers
@@ -338,9 +344,10 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             r.v[i] = *reinterpret_cast<const uint32_t*>(vch + (16 * i + ln.n) * 8 + ln.v_pos0 / 2);
-        const size_t nb = (ln.v_sel ? headB : headA) * kPageTokens + ln.v_pos0;   // V norms first
-        r.vn0 = *reinterpret_cast<const f32x4*>(p.scales + nb);
-        r.vn1 = *reinterpret_cast<const f32x4*>(p.scales + nb + 4);
+        // the V norms of the lane's eight softmax tokens, after the V chunk's indices
+        const float* vn = reinterpret_cast<const float*>(vch + v_code<FMT, D>()) + ln.v_pos0;
+        r.vn0 = *reinterpret_cast<const f32x4*>(vn);
+        r.vn1 = *reinterpret_cast<const f32x4*>(vn + 4);
     } else {
         if constexpr (FMT == KVD_TURBO4) {   // 32-index group j of the lane's tokens
             const uint8_t* base = kch + 256 * ln.j + 16 * ln.a_pos;
@@ -355,12 +362,15 @@ __device__ __forceinline__ void load_pair(PairRaw<FMT, D>& r, const LaunchParams
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             r.v[i] = *reinterpret_cast<const uint32_t*>(vch + (16 * i + ln.n) * 8 + ln.v_pos0 / 2);
-        const size_t nb = (ln.v_sel ? headB : headA) * kPageTokens + ln.v_pos0;
-        const size_t voff = (size_t)p.pool * p.Hkv * kPageTokens;
-        r.kn0 = *reinterpret_cast<const f32x4*>(p.scales + nb);
-        r.kn1 = *reinterpret_cast<const f32x4*>(p.scales + nb + 4);
-        r.vn0 = *reinterpret_cast<const f32x4*>(p.scales + voff + nb);
-        r.vn1 = *reinterpret_cast<const f32x4*>(p.scales + voff + nb + 4);
+        // the K and V norms of the lane's eight softmax tokens (page v_sel), after the indices
+        // of that page's K and V chunks
+        const float* kn = reinterpret_cast<const float*>(
+            p.k + (ln.v_sel ? headB : headA) * (size_t)k_chunk<FMT, D>() + k_code<FMT, D>()) + ln.v_pos0;
+        const float* vn = reinterpret_cast<const float*>(vch + v_code<FMT, D>()) + ln.v_pos0;
+        r.kn0 = *reinterpret_cast<const f32x4*>(kn);
+        r.kn1 = *reinterpret_cast<const f32x4*>(kn + 4);
+        r.vn0 = *reinterpret_cast<const f32x4*>(vn);
+        r.vn1 = *reinterpret_cast<const f32x4*>(vn + 4);
     }
 }
 
@@ -552,13 +562,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // p.qt tiles ("virtual heads") of up to kMaxGroup rows, each processed like a KV head of its
     // own (its pages are read once per tile).
     // Units that read the same lines run on one XCD at the same time, so its L2 fetches each
-    // line once for all of them: the p.qt query tiles of a KV head read the same pages, and in
-    // the codebook formats KV heads 2j and 2j + 1 share every 128-byte line of per-token norms.
-    // With m such consecutive units, within every full block of 8m workgroups, unit
-    // m * x + j goes to linear id 8 * j + x (XCD x, dispatched in consecutive rounds).  A
-    // bijection on full blocks, the identity on the tail.
+    // line once for all of them: the p.qt query tiles of a KV head read the same pages.  With
+    // m such consecutive units, within every full block of 8m workgroups, unit m * x + j goes
+    // to linear id 8 * j + x (XCD x, dispatched in consecutive rounds).  A bijection on full
+    // blocks, the identity on the tail.
     int wg = blockIdx.x;
-    if (const int m = (kVcb ? 2 : 1) * p.qt; m > 1) {
+    if (const int m = p.qt; m > 1) {
         const int blk = 8 * m;
         if (wg < (int)gridDim.x / blk * blk) {
             const int r = wg % blk;
@@ -729,8 +738,8 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         if constexpr (FMT == KVD_FP8_E4M3) {   // scales [2][Hkv]: K then V
             zscale *= p.scales[hk];
             oscale = p.scales[p.Hkv + hk];
-        } else if constexpr (FMT == KVD_TURBO8) {   // K scales after the [pool][Hkv][16] V norms
-            zscale *= p.scales[(size_t)p.pool * p.Hkv * kPageTokens + hk];
+        } else if constexpr (FMT == KVD_TURBO8) {   // scales: the [Hkv] K scales
+            zscale *= p.scales[hk];
         }
     }
     const float cap_l2 = CAP ? p.softcap * kLog2e : 0.0f;      // cap in base-2 units
@@ -1203,7 +1212,6 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
     const size_t head = (size_t)phys * p.Hkv + p.kv_head;
     const uint8_t* ch = p.cache + head * p.chunk;
     float val;
-    const size_t norm_plane = (size_t)p.pool * p.Hkv * kPageTokens;   // floats per norm plane
     if (p.fmt == KVD_BF16) {
         const size_t off = p.is_v ? (size_t)d * 16 + pos : ((size_t)(d / 8) * 16 + pos) * 8 + d % 8;
         val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(ch)[off]);
@@ -1214,8 +1222,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
         const int e = off % 4;
         const uint32_t pair = bf[e / 2];
         val = bf16_bits_to_f32((e & 1) ? (pair >> 16) : (pair & 0xFFFFu));
-        // FP8: scales [2][Hkv]; Turbo8: the K scales follow the V norms
-        val *= p.fmt == KVD_TURBO8 ? p.scales[norm_plane + p.kv_head]
+        // FP8: scales [2][Hkv]; Turbo8: the [Hkv] K scales
+        val *= p.fmt == KVD_TURBO8 ? p.scales[p.kv_head]
                                    : p.scales[(p.is_v ? p.Hkv : 0) + p.kv_head];
     } else {
         uint32_t idx;
@@ -1230,13 +1238,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
             const int e = d % 32;
             idx = (tri_field(g3[0], g3[1], g3[2], e / 8) >> (3 * (e % 8))) & 7u;
         }
-        // levels: 2^kbits K then 16 V (Turbo8: the 16 V levels); norm planes K then V
-        // (Turbo8: the V plane only)
+        // levels: 2^kbits K then 16 V (Turbo8: the 16 V levels); the page's 16 fp32 norms
+        // follow the chunk's indices
         const bool t8 = p.fmt == KVD_TURBO8;
         const int kl = t8 ? 0 : 1 << p.kbits;
         const float lvl = p.codebook[(p.is_v ? kl : 0) + idx];
-        const size_t nb = (p.is_v && !t8 ? norm_plane : 0) + head * kPageTokens + pos;
-        val = p.scales[nb] * lvl;
+        val = reinterpret_cast<const float*>(ch + p.chunk - 64)[pos] * lvl;
     }
     p.out[i] = val;
 }

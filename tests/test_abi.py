@@ -175,6 +175,8 @@ def test_append_arg_errors():
     assert append_call(fmt=2, cb=None) == -1 and append_call(fmt=3, sign=None) == -1
     assert append_call(fmt=4, scales=None) == -1 and append_call(fmt=4, cb=None) == -1
     assert append_call(fmt=0, scales=None, cb=None, sign=None, n=0) == 0    # BF16 needs neither
+    assert append_call(fmt=2, scales=None, n=0) == 0     # Turbo4/3 norms live in the chunks
+    assert append_call(fmt=3, scales=None, n=0) == 0
     assert append_call(k=FAKE + 4) == -4 and append_call(kc=FAKE + 8) == -4
     assert append_call(n=0) == 0 and append_call(dims(num_seqs=0)) == 0    # nothing launched
 

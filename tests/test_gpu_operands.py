@@ -84,12 +84,11 @@ def expected_records(inp, b, hk, n_pairs):
     if vkind == "cb":
         vh, vl = _hilo_bits(vlev)
     e4m3_bf16 = _bf16_bits_of(oracle.E4M3FN_TABLE.astype(np.float32))
-    pool = inp.num_pool_blocks
-    kn = vn = None
+    kn = vn = None      # [pool][Hkv][16]: the norms after each chunk's indices
     if kkind == "cb":
-        kn = oracle.attention.norm_plane(fmt, inp.scales, "k", pool, s.num_kv_heads)
+        kn = oracle.attention.chunk_norms(fmt, "k", inp.k_cache, D)
     if vkind == "cb":
-        vn = oracle.attention.norm_plane(fmt, inp.scales, "v", pool, s.num_kv_heads)
+        vn = oracle.attention.chunk_norms(fmt, "v", inp.v_cache, D)
     W = D + 16
     out = np.zeros((n_pairs, 64, W), dtype=np.uint32)
     nan = np.zeros_like(out, dtype=bool)

@@ -106,9 +106,11 @@ def test_pack_unpack_random(bits, rng):
 
 
 def test_layout_sizes():
-    for fmt, kb, vb in [("bf16", 4096, 4096), ("fp8", 2048, 2048), ("turbo4", 1024, 1024),
-                        ("turbo3", 768, 1024), ("turbo8", 2048, 1024)]:
+    # codebook chunks: the indices, then 16 fp32 per-token norms (64 bytes)
+    for fmt, kb, vb in [("bf16", 4096, 4096), ("fp8", 2048, 2048), ("turbo4", 1088, 1088),
+                        ("turbo3", 832, 1088), ("turbo8", 2048, 1088)]:
         assert kvgen.k_chunk_bytes(fmt, 128) == kb and kvgen.v_chunk_bytes(fmt, 128) == vb
+        assert kb % 16 == 0 and vb % 16 == 0          # chunks stay 16-byte aligned
     # bytes per (token, KV head): 512 / 256 / 136 / 120 / 196 (Turbo8: 128 K + 64 V + 4 norm)
     assert [kvgen.kv_bytes_per_token_head(f, 128) for f in kvgen.FORMATS] == [512, 256, 136, 120, 196]
 
@@ -134,18 +136,28 @@ def test_relayout_same_logical_cache(fmt):
 
 def test_turbo8_scales_layout():
     """Turbo8: K bytes and K scales exactly as the FP8 format writes them for the same draws,
-    V bytes and V norms exactly as Turbo4 writes them; scales = V norms, then K scales."""
+    V chunks (indices and inline norms) exactly as Turbo4 writes them; scales = the K scales."""
     kw = dict(head_dim=128, num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None,
               ctx_range=(3, 70))
     t8 = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo8", **kw))
     f8 = kvgen.make_inputs(kvgen.spec("c1", fmt="fp8", **kw))
     t4 = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo4", **kw))
-    pool = t8.num_pool_blocks
-    assert t8.scales.shape == (pool * 2 * 16 + 2,)
-    assert np.array_equal(t8.k_cache, f8.k_cache) and np.array_equal(t8.scales[-2:], f8.scales[0])
+    assert t8.scales.shape == (2,) and t4.scales is None
+    assert np.array_equal(t8.k_cache, f8.k_cache) and np.array_equal(t8.scales, f8.scales[0])
     assert np.array_equal(t8.v_cache, t4.v_cache)
-    assert np.array_equal(t8.scales[:-2].reshape(pool, 2, 16), t4.scales[1], equal_nan=True)
     assert np.array_equal(t8.codebook, t4.codebook[16:])
+
+
+def test_inline_norms():
+    """The 16 fp32 values after a codebook chunk's indices are its tokens' norms: NaN on spare
+    pages and tail slots (poison), finite and positive on live tokens."""
+    inp = kvgen.make_inputs(kvgen.spec("c1", fmt="turbo4", head_dim=128, context=40))
+    nrm = inp.k_cache[:, :, 1024:].copy().view("<f4")           # [pool, Hkv, 16]
+    used = inp.block_table[0, :3]
+    assert np.isfinite(nrm[used[0]]).all() and (nrm[used[0]] > 0).all()
+    assert np.isfinite(nrm[used[2], 0, :8]).all() and np.isnan(nrm[used[2], 0, 8:]).all()
+    spare = [p for p in range(inp.num_pool_blocks) if p not in set(inp.block_table[0, :3].tolist())]
+    assert np.isnan(nrm[spare]).all()
 
 
 def test_poison_spare_and_tail():

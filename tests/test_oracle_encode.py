@@ -178,11 +178,13 @@ def test_append_then_gather(fmt, rng):
                                                scales=inp.scales, codebook=inp.codebook,
                                                sign=inp.sign)
                 assert np.array_equal(got, want)
-                if norm is not None:
-                    j = np.arange(pos[b], pos[b] + T)
-                    phys = inp.block_table[b][j // 16]
-                    plane = oa.norm_plane(fmt, sc2, which, inp.num_pool_blocks, 2)
-                    assert np.array_equal(plane[phys, hk, j % 16], norm)
+                if norm is not None:    # fp32 norms after each chunk's indices
+                    got_n = oa.token_norms(fmt, which, cache, inp.block_table[b], hk, pos[b],
+                                           pos[b] + T, 128)
+                    assert np.array_equal(got_n, norm)
+                    before_n = oa.token_norms(fmt, which, old, inp.block_table[b], hk, 0, pos[b], 128)
+                    after_n = oa.token_norms(fmt, which, cache, inp.block_table[b], hk, 0, pos[b], 128)
+                    assert np.array_equal(before_n, after_n, equal_nan=True)
                 before = oracle.gather_stored(fmt, which, old, inp.block_table[b], hk, 0, pos[b], 128)
                 after = oracle.gather_stored(fmt, which, cache, inp.block_table[b], hk, 0, pos[b], 128)
                 assert np.array_equal(before, after)

@@ -255,18 +255,16 @@ def test_planted_missing_sign(monkeypatch):
 
 
 def test_planted_turbo8_scale_of_wrong_head(monkeypatch):
-    """Turbo8 with two KV heads: the K scale of head 0 used for both heads, or the V norms
-    read from a [2][pool][Hkv][16]-style second plane, is caught by the brute force."""
+    """Turbo8 with two KV heads: the K scale of head 0 used for both heads, or the inline V norms
+    read one token off, is caught by the brute force."""
     inp = _tiny("turbo8", num_seqs=2, num_q_heads=4, num_kv_heads=2, context=None,
                 ctx_range=(3, 30))
     good = oa.fp8_scale
     monkeypatch.setattr(oa, "fp8_scale", lambda f, sc, w, hk, hkv: good(f, sc, w, 0, hkv))
     assert _brute_mismatch(inp)
     monkeypatch.setattr(oa, "fp8_scale", good)
-    pool = inp.num_pool_blocks
-    flat = np.asarray(inp.scales)
-    monkeypatch.setattr(oa, "norm_plane", lambda f, sc, w, p, h: np.roll(
-        flat[: pool * 2 * 16], 2).reshape(pool, 2, 16))
+    norms = oa.token_norms
+    monkeypatch.setattr(oa, "token_norms", lambda *a: np.roll(norms(*a), 1))
     assert _brute_mismatch(inp)
 
 
