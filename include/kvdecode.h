@@ -148,6 +148,14 @@ typedef struct kvd_dims {
                                     query rows of a KV head share one pass over its pages per
                                     16 rows.  Requires n_q <= max_context_len and
                                     num_seqs * n_q <= 65535. */
+    int32_t mean_context_len;    /* launch hint, results do not depend on it: the batch's mean
+                                    attended span in tokens (min(L, window + n_q - 1) for
+                                    windowed sequences, else L), as the caller's host-side
+                                    bookkeeping knows it; 0 = unknown, taken as
+                                    max_context_len.  Below max_context_len (a ragged batch)
+                                    the automatic run choice makes about 2.5 waves of work per
+                                    resident wavefront slot instead of one, so runs of unequal
+                                    sequences even out.  0 <= mean_context_len. */
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: slots for per-partition fp32 triples

@@ -63,7 +63,7 @@ class Dims(ctypes.Structure):
                 ("block_size", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
                 ("num_pool_blocks", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
                 ("partition_size", ctypes.c_int32), ("partitions_per_wave", ctypes.c_int32),
-                ("queries_per_seq", ctypes.c_int32)]
+                ("queries_per_seq", ctypes.c_int32), ("mean_context_len", ctypes.c_int32)]
 
 
 def library_path() -> str:

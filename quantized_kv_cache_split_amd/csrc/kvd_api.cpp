@@ -69,7 +69,12 @@ int device_cus() {
 // load pipeline), leaves a tail when it ends and writes one (m, l, o) triple per run, so runs
 // should be long; the chip should also be covered in one round.  The automatic choice splits
 // the page pairs of a batch whose sequences were all max_context_len long evenly over the
-// device's resident wave slots (runs of whole page pairs, at least one partition long).  Where
+// device's resident wave slots (runs of whole page pairs, at least one partition long).  With
+// a mean_context_len hint below max_context_len (a ragged batch) it splits the batch's mean
+// work over 2.5 rounds of the slots instead: sequences end at different times, and about 2.5
+// waves of work per slot let the dispatcher even them out (ragged 64 x U{1..32K} BF16 batch,
+// runs of 1 / 2 / 3 / 4 partitions, i.e. 5.2 / 2.6 / 1.8 / 1.5 rounds: 500.9 / 490.8 / 499.8 /
+// 508.0 us per partition launch on MI355X).  Where
 // the wide layout is built (one workgroup per CU) it is taken if runs of at most kMaxRunWide
 // partitions cover the chip in one round; otherwise runs are capped at kMaxRun partitions
 // (ragged batches, whose real work is smaller, do better with short runs).  Runs other than
@@ -88,14 +93,17 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     if (d->partitions_per_wave > 0) {
         tokens = (int64_t)d->partitions_per_wave * ps;
     } else {
-        const int64_t pairs = (d->max_context_len + pair_tokens - 1) / pair_tokens;
+        const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
+        const int64_t len = ragged ? d->mean_context_len : d->max_context_len;
+        const int64_t pairs = (len + pair_tokens - 1) / pair_tokens;
         const int64_t units = (int64_t)d->num_kv_heads * query_tiles(d) * d->num_seqs;
         auto run_for = [&](bool w) -> int64_t {
-            const int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w);
+            int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w);
+            if (ragged) slots = slots * 5 / 2;                        // 2.5 rounds of work
             const int64_t rp = (pairs * units + slots - 1) / slots;   // pairs per wave
             return rp * pair_tokens < ps ? ps : rp * pair_tokens;
         };
-        if (kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
+        if (!ragged && kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
             const int64_t t = run_for(true);
             if (t <= (int64_t)kvd::kMaxRunWide * ps) {
                 wide = true;
@@ -128,7 +136,7 @@ int check_dims(const kvd_dims* d, int fmt) {
     const int ps = d->partition_size;
     if (!(ps == 0 || ps == -1 || (ps > 0 && ps % kvd::kPageTokens == 0))) return KVD_ERR_SHAPE;
     if (d->num_seqs > 65535 || d->num_kv_heads > 65535) return KVD_ERR_SHAPE;   // grid limits
-    if (d->partitions_per_wave < 0) return KVD_ERR_SHAPE;
+    if (d->partitions_per_wave < 0 || d->mean_context_len < 0) return KVD_ERR_SHAPE;
     if (d->queries_per_seq < 0 || d->queries_per_seq > 65535) return KVD_ERR_SHAPE;
     if ((int64_t)d->num_seqs * queries(d) > 65535) return KVD_ERR_SHAPE;   // reduce grid rows
     if ((int64_t)queries(d) > d->max_context_len) return KVD_ERR_SHAPE;   // positions >= 0

@@ -92,7 +92,8 @@ def call(d=None, fmt=0, **over):
 @pytest.mark.parametrize("field,value", [("num_q_heads", 60), ("num_kv_heads", 0),
                                          ("head_dim", 96), ("block_size", 32),
                                          ("max_context_len", 0), ("max_context_len", 1 << 20),
-                                         ("partition_size", 100), ("partitions_per_wave", -1)])
+                                         ("partition_size", 100), ("partitions_per_wave", -1),
+                                         ("mean_context_len", -1)])
 def test_shape_errors(field, value):
     assert call(dims(**{field: value})) == -2
 
