@@ -14,6 +14,12 @@ dirty lines behind; a rewrite would leave write-backs that land inside the next 
 Prints ONE JSON line.  `value` = algorithmic KV bytes per call / mean call time.
 `roofline` = the partition kernel's algorithmic bytes / its mean duration against 8 TB/s.
 `cpu_baseline` = the fp64 oracle timed on this host's cores over a bounded sample.
+`other_formats` = the other formats' 32K workloads (BF16, Turbo4, Turbo3 by default), timed the
+same way in the same run with fewer steps.  `dtype` names the operand precision of the
+headline format's matrix products (accumulation is fp32 everywhere).
+
+`--read-probe` instead measures the HBM read ceiling (kvd_read_probe): a plain read stream and
+random-chunk reads of the paged layouts' chunk sizes.
 """
 from __future__ import annotations
 
@@ -54,6 +60,14 @@ def parse():
     ap.add_argument("--append", type=int, default=0, metavar="T",
                     help="instead of decode attention, time the KV append (quantize-on-write) "
                          "of T new tokens per sequence into the workload's cache")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="instead of decode attention, measure the HBM read ceiling: a plain "
+                         "read stream and random-chunk reads of the paged layouts' chunk sizes")
+    ap.add_argument("--formats", default="m-bf16,m-t4,m-t3",
+                    help="other 32K workloads timed after the headline one, in the same run "
+                         "(comma separated; empty = none)")
+    ap.add_argument("--format-steps", type=int, default=30,
+                    help="timed steps of each workload in --formats (warm-up: the same count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -203,49 +217,90 @@ def append_bench(args):
     print(json.dumps(res), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
-              "(the per-(sequence, KV head, partition) work would shard by sequence or KV head "
-              "with no exchange, see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
+def read_probe(args):
+    """HBM read ceiling on this GPU: chunks of a 4 GiB buffer read in order (a plain stream) or
+    in a random order (a paged cache's pages sit at random places in the pool), with the chunk
+    sizes of the paged layouts (1 KB Turbo4 page chunks ... 4 KB BF16) and 8 waves per CU."""
+    import torch
 
-    if args.copy_probe:
-        copy_probe(args.copy_probe, args.steps)
-        return
-    if args.append:
-        append_bench(args)
-        return
+    import quantized_kv_cache_split_amd as kvd
+    buf_bytes = 4 << 30
+    buf = torch.empty(buf_bytes, dtype=torch.uint8, device="cuda:0")
+    buf.fill_(1)
+    props = torch.cuda.get_device_properties(0)
+    sink = torch.empty(props.multi_processor_count * 32 * 64, dtype=torch.int32, device="cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(7)
+    cases = [("stream", 65536, 8, 16), ("stream", 65536, 8, 8)]
+    for cb in (1024, 2048, 4096):
+        for fl in (4, 8, 16):
+            cases.append(("random", cb, 8, fl))
+    res = []
+    for kind, cb, wpc, fl in cases:
+        n = buf_bytes // cb
+        ids = torch.arange(n, dtype=torch.int32) if kind == "stream" else \
+            torch.randperm(n, generator=g).to(torch.int32)
+        ids = ids.to("cuda:0")
+        for _ in range(3):
+            kvd.read_probe(buf, ids, cb, wpc, fl, sink)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in ev:
+            e[0].record()
+            kvd.read_probe(buf, ids, cb, wpc, fl, sink)
+            e[1].record()
+        torch.cuda.synchronize()
+        t = np.array([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+        med = float(np.median(t))
+        res.append({"order": kind, "chunk_bytes": cb, "waves_per_cu": wpc,
+                    "kb_in_flight_per_wave": fl, "bytes_per_launch": buf_bytes,
+                    "median_ms": round(med * 1e3, 4), "gbps": round(buf_bytes / med / 1e9, 1),
+                    "frac_of_8tbs": round(buf_bytes / med / 1e9 / HBM_PEAK_GBS, 4)})
+        print(json.dumps(res[-1]), flush=True)
+    best = {k: max(r["gbps"] for r in res if r["order"] == k) for k in ("stream", "random")}
+    print(json.dumps({"metric": "HBM read ceiling (kvd_read_probe)", "value": best["random"],
+                      "unit": "GB/s", "stream_gbps": best["stream"], "random_chunk_gbps": best["random"],
+                      "cases": res}), flush=True)
 
+
+# Operand precision of each format's matrix products (the accumulators are fp32 throughout).
+DTYPES = {
+    "bf16": "bf16 K/V/q operands, P as a bf16 hi+lo pair; fp32 accumulate",
+    "fp8": "bf16 operands (E4M3 K/V exactly), P as a bf16 hi+lo pair; fp32 accumulate",
+    "turbo8": "QK bf16 (E4M3 K exactly); PV fp16 (levels hi+lo, P' fp16); fp32 accumulate",
+    "turbo4": "fp16 operands (codebook levels and rotated q as hi+lo, P' fp16); fp32 accumulate",
+    "turbo3": "fp16 operands (codebook levels and rotated q as hi+lo, P' fp16); fp32 accumulate",
+}
+
+
+def time_workload(name, steps, warmup, partition_size=None, partitions_per_wave=0, flush=True):
+    """Generate workload `name` and time full calls and partition launches on cuda:0.
+    Returns a dict of the measurements (seconds arrays and sizes)."""
     import torch
 
     import kvgen
     import quantized_kv_cache_split_amd as kvd
     from kvgen.torch_io import dims_kwargs, to_torch
 
-    spec = kvgen.SPECS[args.workload]
+    spec = kvgen.SPECS[name]
     t_gen = time.perf_counter()
     inp = kvgen.make_inputs(spec)
     t_gen = time.perf_counter() - t_gen
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     t = to_torch(inp, dev)
-    ps = args.partition_size if args.partition_size is not None else spec.partition_size
-    dims = kvd.Dims(**dims_kwargs(inp, ps, args.partitions_per_wave))
+    ps = partition_size if partition_size is not None else spec.partition_size
+    dims = kvd.Dims(**dims_kwargs(inp, ps, partitions_per_wave))
     out = torch.empty(tuple(inp.q.shape), dtype=torch.float32, device=dev)   # [B, (n_q,) Hq, D]
     nws = kvd.workspace_bytes(dims)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev) if nws else None
-    flush = None if args.no_flush else torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    fl = torch.ones(64 << 20, dtype=torch.int64, device=dev) if flush else None
     sink = torch.empty(1, dtype=torch.int64, device=dev)
 
     def evict():   # read 512 MiB (no dirty lines), outside the timed events
-        if flush is not None:
-            torch.sum(flush, dim=0, keepdim=True, out=sink)
+        if fl is not None:
+            torch.sum(fl, dim=0, keepdim=True, out=sink)
     call_args = (dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
                  spec.fmt, t["scales"], t["codebook"], t["sign_pattern"],
                  float(inp.softmax_scale), t["window"], float(inp.softcap), out, ws)
-    kv_bytes = inp.kv_bytes()
 
     def step(ev=None):   # one full call, the entry point a caller uses
         if ev is not None:
@@ -261,24 +316,55 @@ def main():
         kvd.reduce_partitions(*call_args)
 
     def timed(fn):
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         w = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             evict()
             fn(events[i])
         torch.cuda.synchronize()
         w = time.perf_counter() - w
         return np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3, w   # seconds
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         evict()
         step()
     torch.cuda.synchronize()
     t_call, wall = timed(step)
     assert np.isfinite(out.cpu().numpy()).all(), "non-finite output"
     t_part, _ = timed(partition_step)
+    res = dict(spec=spec, inp=inp, ps=ps, t_call=t_call, t_part=t_part, wall=wall, t_gen=t_gen,
+               kv_bytes=inp.kv_bytes())
+    del t, out, ws, fl
+    torch.cuda.empty_cache()
+    return res
 
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not supported "
+              "(the per-(sequence, KV head, partition) work would shard by sequence or KV head "
+              "with no exchange, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
+    if args.append:
+        append_bench(args)
+        return
+
+    if args.read_probe:
+        read_probe(args)
+        return
+
+    import torch
+    torch.cuda.set_device(0)
+    m = time_workload(args.workload, args.steps, args.warmup, args.partition_size,
+                      args.partitions_per_wave, flush=not args.no_flush)
+    spec, inp, ps, t_call, t_part = m["spec"], m["inp"], m["ps"], m["t_call"], m["t_part"]
+    kv_bytes = m["kv_bytes"]
     mean_call = float(t_call.mean())
     value = kv_bytes / mean_call / 1e9
     achieved = kv_bytes / float(t_part.mean()) / 1e9
@@ -294,7 +380,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": DTYPES[spec.fmt],
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {spec.name}",
@@ -305,8 +391,6 @@ def main():
             "kv_format": KV_NAMES[spec.fmt], "block_size": 16,
             "partition_size": ps if ps else 512, "kv_bytes_per_step": kv_bytes,
             "queries_per_seq": spec.queries_per_seq,
-            "mfma_operands": "bf16 for BF16/FP8 K and V, fp16 for codebook K and V (Turbo8: "
-                             "bf16 QK, fp16 PV); fp32 accumulate",
         },
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "decode_tokens_per_s": round(spec.num_seqs * spec.queries_per_seq / mean_call, 1),
@@ -316,9 +400,24 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic},
-        "input_gen_s": round(t_gen, 1),
-        "timed_wall_s": round(wall, 3),
+        "input_gen_s": round(m["t_gen"], 1),
+        "timed_wall_s": round(m["wall"], 3),
     }
+    # the other formats' 32K workloads, timed in the same run (fewer steps)
+    others = {}
+    for name in [w for w in args.formats.split(",") if w and w != args.workload]:
+        o = time_workload(name, args.format_steps, args.format_steps, flush=not args.no_flush)
+        oc, op = float(o["t_call"].mean()), float(o["t_part"].mean())
+        others[name] = {"workload": o["spec"].name, "dtype": DTYPES[o["spec"].fmt],
+                        "kv_bytes_per_step": o["kv_bytes"], "steps": args.format_steps,
+                        "call_ms": round(oc * 1e3, 4), "partition_kernel_ms": round(op * 1e3, 4),
+                        "gbps": round(o["kv_bytes"] / oc / 1e9, 2),
+                        "frac_of_hbm_peak": round(o["kv_bytes"] / oc / 1e9 / HBM_PEAK_GBS, 4),
+                        "partition_kernel_frac": round(o["kv_bytes"] / op / 1e9 / HBM_PEAK_GBS, 4),
+                        "decode_tokens_per_s": round(o["spec"].num_seqs * o["spec"].queries_per_seq / oc, 1)}
+        del o
+    if others:
+        res["other_formats"] = others
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(res), flush=True)

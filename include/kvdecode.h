@@ -328,6 +328,20 @@ int kvd_append_kv(const kvd_dims* dims, int fmt, const float* k_new, const float
                   void* k_cache, void* v_cache, const float* scales, const float* codebook,
                   const float* sign_pattern, void* stream);
 
+/* Measurement export: an HBM read probe giving the decode kernels' practical ceiling.
+ * Reads n_chunks chunks of chunk_bytes (a power of two, >= 1024) from buf, chunk chunk_ids[c] (at
+ * byte chunk_ids[c] * chunk_bytes; ids outside the buffer read chunk 0) in list order, with
+ * device_CUs * waves_per_cu / 4 workgroups of four wavefronts (waves_per_cu a multiple of 4,
+ * 4..32).  Each wavefront takes loads_in_flight (1, 2, 4, 8 or 16) consecutive 1 KB pieces of
+ * the list per turn -- all issued before any is used -- then the pieces nwaves * loads_in_flight
+ * further on.  Consecutive ids make a plain read stream; a random permutation reads chunks at
+ * random places like a paged cache.  The data is folded into sink (uint32, at least
+ * device_CUs * waves_per_cu * 64 words, write-only) so nothing is skipped.  Asynchronous on
+ * stream; time it with events. */
+int kvd_read_probe(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int64_t n_chunks,
+                   int32_t chunk_bytes, int32_t waves_per_cu, int32_t loads_in_flight,
+                   uint32_t* sink, size_t sink_bytes, void* stream);
+
 /* A static, human-readable name for a status code. */
 const char* kvd_status_str(int status);
 

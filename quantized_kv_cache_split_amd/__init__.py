@@ -14,7 +14,8 @@ import os
 
 __all__ = ["Dims", "KvdError", "BF16", "FP8_E4M3", "TURBO4", "TURBO3", "TURBO8", "FORMATS",
            "workspace_bytes", "decode_attn_paged", "decode_attn_paged_noalloc", "decode_partitions", "reduce_partitions",
-           "dequant_gather", "dequant_operands", "append_kv", "status_str", "library_path", "load",
+           "dequant_gather", "dequant_operands", "append_kv", "read_probe", "status_str",
+           "library_path", "load",
            "hip_runtimes_mapped"]
 
 BF16, FP8_E4M3, TURBO4, TURBO3, TURBO8 = 0, 1, 2, 3, 4
@@ -133,6 +134,11 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p]
         lib.kvd_append_kv.restype = ctypes.c_int
+        lib.kvd_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+        lib.kvd_read_probe.restype = ctypes.c_int
         lib.kvd_status_str.argtypes = [ctypes.c_int]
         lib.kvd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -249,6 +255,17 @@ def dequant_operands(dims, fmt, k_cache, v_cache, scales, codebook, block_table,
     if st != 0:
         raise KvdError(st, "kvd_dequant_operands")
     return out
+
+
+def read_probe(buf, chunk_ids, chunk_bytes, waves_per_cu, loads_in_flight, sink, stream=None):
+    """HBM read probe (kvd_read_probe): read the chunks of the uint8 device tensor `buf` listed
+    in the int32 tensor `chunk_ids`."""
+    st = load().kvd_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(chunk_ids),
+                               chunk_ids.numel(), int(chunk_bytes), int(waves_per_cu),
+                               int(loads_in_flight), _ptr(sink), sink.numel() * sink.element_size(),
+                               _stream(stream))
+    if st != 0:
+        raise KvdError(st, "kvd_read_probe")
 
 
 def append_kv(dims, fmt, k_new, v_new, block_table, positions, n_new, k_cache, v_cache, scales,

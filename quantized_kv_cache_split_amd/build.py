@@ -9,7 +9,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkvdecode.so")
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("kvd_kernels.hip", "kvd_append.hip", "kvd_api.cpp")]
+SOURCES = [os.path.join(PKG, "csrc", f)
+           for f in ("kvd_kernels.hip", "kvd_append.hip", "kvd_probe.hip", "kvd_api.cpp")]
 ARCH = "gfx950"
 
 

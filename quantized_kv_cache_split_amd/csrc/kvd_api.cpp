@@ -436,6 +436,32 @@ int kvd_append_kv(const kvd_dims* d, int fmt, const float* k_new, const float* v
                                                                                 : KVD_ERR_HIP;
 }
 
+int kvd_read_probe(const void* buf, size_t buf_bytes, const int32_t* chunk_ids, int64_t n_chunks,
+                   int32_t chunk_bytes, int32_t waves_per_cu, int32_t loads_in_flight,
+                   uint32_t* sink, size_t sink_bytes, void* stream) {
+    if (!buf || !chunk_ids || !sink) return KVD_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(chunk_ids, 4) || !aligned(sink, 4)) return KVD_ERR_ALIGN;
+    if (chunk_bytes < 1024 || (chunk_bytes & (chunk_bytes - 1)) != 0 || n_chunks < 0 ||
+        buf_bytes < (size_t)chunk_bytes || waves_per_cu < 4 || waves_per_cu > 32 ||
+        waves_per_cu % 4 != 0 || !(loads_in_flight == 1 || loads_in_flight == 2 ||
+                                   loads_in_flight == 4 || loads_in_flight == 8 ||
+                                   loads_in_flight == 16))
+        return KVD_ERR_SHAPE;
+    const int blocks = device_cus() * waves_per_cu / 4;
+    if (sink_bytes < (size_t)blocks * 4 * 64 * sizeof(uint32_t)) return KVD_ERR_WORKSPACE;
+    if (n_chunks == 0) return KVD_OK;
+    kvd::ProbeParams p{};
+    p.buf = static_cast<const uint8_t*>(buf);
+    p.ids = chunk_ids;
+    p.sink = sink;
+    p.n = n_chunks;
+    p.buf_bytes = (int64_t)buf_bytes;
+    p.log2_pieces = 0;
+    while ((1024 << p.log2_pieces) < chunk_bytes) ++p.log2_pieces;
+    return kvd::launch_read_probe(p, blocks, loads_in_flight, static_cast<hipStream_t>(stream)) ==
+                   hipSuccess ? KVD_OK : KVD_ERR_HIP;
+}
+
 const char* kvd_status_str(int status) {
     switch (status) {
         case KVD_OK: return "ok";

@@ -112,6 +112,16 @@ struct AppendParams {
     int32_t ps;               // page slots per sequence: pages one sequence's T new tokens touch, at most
 };
 
+// Arguments of the HBM read probe (kvd_read_probe).
+struct ProbeParams {
+    const uint8_t* buf;
+    const int32_t* ids;       // chunk indices, read in this order
+    uint32_t* sink;           // one word per lane of every wave
+    int64_t n;                // chunks to read
+    int64_t buf_bytes;
+    int32_t log2_pieces;      // chunk = 1 KB << log2_pieces
+};
+
 // Launches `kernel` (which takes one parameter struct by value) and returns the status of this
 // launch alone.  hipGetLastError() after a triple-chevron launch would also report an error
 // left pending by any earlier, unrelated runtime call on the thread (the caller's, or another
@@ -133,5 +143,6 @@ hipError_t launch_operands(int fmt, const OperandParams& p, hipStream_t s);
 // with hipGetSymbolAddress on the first call per device, then cached).
 hipError_t noalloc_workspace(void** ptr);
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_read_probe(const ProbeParams& p, int blocks, int loads_in_flight, hipStream_t s);
 
 }  // namespace kvd
