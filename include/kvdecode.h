@@ -117,7 +117,9 @@ typedef enum kvd_status {
 /* Shapes.  Supported: block_size == 16; head_dim 64 or 128 for BF16/FP8, 128 for the Turbo
  * formats; num_q_heads a multiple of num_kv_heads.  A query group larger than 16 (MQA-like
  * shapes) is processed in tiles of 16 query heads, each tile reading its KV head's pages
- * again. */
+ * again.  Size limits (KVD_ERR_SHAPE beyond them): num_seqs, num_kv_heads <= 65535;
+ * num_seqs * n_q * num_q_heads < 2^31 query rows; the workspace of a split (its m, l and
+ * outputs for every row and partition) below 2^62 bytes. */
 typedef struct kvd_dims {
     int32_t num_seqs;            /* B */
     int32_t num_q_heads;         /* Hq */

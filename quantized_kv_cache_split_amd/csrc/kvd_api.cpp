@@ -81,7 +81,7 @@ int device_cus() {
 // one partition need partition boundaries on even pages (partition size a multiple of 32).  An
 // explicit partitions_per_wave R gives runs of R partitions in the two-workgroup layout.
 struct RunChoice {
-    int run_tokens;
+    int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
     bool wide;
 };
 RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
@@ -117,17 +117,32 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     }
     const int64_t span = (int64_t)pl.P * ps;
     if (tokens > span) tokens = span;
-    return {(int)tokens, wide};
+    return {tokens, wide};
 }
 
-// Shape checks shared by every entry point; fmt < 0 skips the format-specific ones.
-int check_dims(const kvd_dims* d, int fmt) {
+// Partition mode, partition size and partitions per sequence kept in the workspace (0 = no
+// split possible) for d's partition_size.
+struct Parts {
+    int mode, part_size, P;
+};
+Parts partitions(const kvd_dims* d) {
+    if (d->partition_size == -1) return {kvd::kPartNever, d->max_context_len, 0};
+    if (d->partition_size == 0) {
+        const int ps = kvd::kAutoPartition;
+        return {kvd::kPartAuto, ps,
+                d->max_context_len >= kvd::kAutoSplitMin
+                    ? (int)(((int64_t)d->max_context_len + ps - 1) / ps) : 0};
+    }
+    return {kvd::kPartFixed, d->partition_size,
+            (int)(((int64_t)d->max_context_len + d->partition_size - 1) / d->partition_size)};
+}
+
+// Shape checks that hold for every format.
+int check_shape(const kvd_dims* d) {
     if (!d) return KVD_ERR_NULL;
-    if (fmt >= 0 && (fmt < KVD_BF16 || fmt > KVD_TURBO8)) return KVD_ERR_FORMAT;
     if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1) return KVD_ERR_SHAPE;
     if (d->num_q_heads % d->num_kv_heads != 0) return KVD_ERR_SHAPE;
     if (d->head_dim != 64 && d->head_dim != 128) return KVD_ERR_SHAPE;
-    if (fmt >= KVD_TURBO4 && d->head_dim != 128) return KVD_ERR_SHAPE;
     if (d->block_size != kvd::kPageTokens) return KVD_ERR_SHAPE;
     if (d->max_blocks_per_seq < 1 || d->num_pool_blocks < 1) return KVD_ERR_SHAPE;
     if (d->max_context_len < 1 ||
@@ -140,25 +155,33 @@ int check_dims(const kvd_dims* d, int fmt) {
     if (d->queries_per_seq < 0 || d->queries_per_seq > 65535) return KVD_ERR_SHAPE;
     if ((int64_t)d->num_seqs * queries(d) > 65535) return KVD_ERR_SHAPE;   // reduce grid rows
     if ((int64_t)queries(d) > d->max_context_len) return KVD_ERR_SHAPE;   // positions >= 0
+    // query / output rows [B][n_q][Hq] are counted in int32
+    if ((int64_t)d->num_seqs * queries(d) * d->num_q_heads > 0x7FFFFFFFLL) return KVD_ERR_SHAPE;
+    // the workspace (fp32 m, l and D outputs per row and partition) must stay addressable
+    const unsigned __int128 slots = (unsigned __int128)((int64_t)d->num_seqs * queries(d)) *
+                                    (uint64_t)d->num_q_heads * (uint64_t)partitions(d).P;
+    if (slots * (uint64_t)(d->head_dim + 2) * sizeof(float) > ((unsigned __int128)1 << 62))
+        return KVD_ERR_SHAPE;
     return KVD_OK;
 }
 
+// Checks shared by every entry point that takes a format: the format itself, then the shape.
+int check_dims(const kvd_dims* d, int fmt) {
+    if (!d) return KVD_ERR_NULL;
+    if (fmt < KVD_BF16 || fmt > KVD_TURBO8) return KVD_ERR_FORMAT;
+    const int st = check_shape(d);
+    if (st != KVD_OK) return st;
+    if (fmt >= KVD_TURBO4 && d->head_dim != 128) return KVD_ERR_SHAPE;
+    return KVD_OK;
+}
+
+// Workspace plan of dims that passed check_shape.
 Plan make_plan(const kvd_dims* d) {
     Plan pl{};
-    if (d->partition_size == -1) {
-        pl.mode = kvd::kPartNever;
-        pl.part_size = d->max_context_len;
-        pl.P = 0;
-    } else if (d->partition_size == 0) {
-        pl.mode = kvd::kPartAuto;
-        pl.part_size = kvd::kAutoPartition;
-        pl.P = d->max_context_len >= kvd::kAutoSplitMin
-                   ? (d->max_context_len + pl.part_size - 1) / pl.part_size : 0;
-    } else {
-        pl.mode = kvd::kPartFixed;
-        pl.part_size = d->partition_size;
-        pl.P = (d->max_context_len + pl.part_size - 1) / pl.part_size;
-    }
+    const Parts pa = partitions(d);
+    pl.mode = pa.mode;
+    pl.part_size = pa.part_size;
+    pl.P = pa.P;
     const size_t rows = (size_t)d->num_seqs * queries(d) * d->num_q_heads * pl.P;
     const size_t ml = round_up(rows * sizeof(float), 256);
     pl.off_l = ml;
@@ -226,14 +249,14 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.P = pl.P;
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
     const RunChoice rc = choose_run(d, pl, fmt);
-    p.run_tokens = rc.run_tokens;
     const int waves = kvd::waves_per_group(fmt);
     // runs of a sequence, at most (one per partition)
     const int64_t runs = pl.P ? ((int64_t)pl.P * pl.part_size + rc.run_tokens - 1) / rc.run_tokens
                               : 0;
     // token indices of every run a workgroup can name must fit in int32
-    if (pl.P && (int64_t)pl.P * pl.part_size + (int64_t)waves * rc.run_tokens > 0x7FFFFFFFLL)
+    if (pl.P && (int64_t)pl.P * pl.part_size + waves * rc.run_tokens > 0x7FFFFFFFLL)
         return KVD_ERR_SHAPE;
+    p.run_tokens = (int32_t)rc.run_tokens;
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
 
@@ -260,7 +283,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
 extern "C" {
 
 size_t kvd_workspace_bytes(const kvd_dims* dims) {
-    if (check_dims(dims, -1) != KVD_OK) return 0;
+    if (check_shape(dims) != KVD_OK) return 0;
     return make_plan(dims).bytes;
 }
 

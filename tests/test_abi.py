@@ -105,6 +105,18 @@ def test_turbo_needs_d128():
 
 def test_format_error():
     assert call(fmt=7) == -3
+    assert call(fmt=-1) == -3 and call(fmt=-(1 << 31)) == -3   # negative formats too
+
+
+def test_size_limits():
+    # query rows [B][n_q][Hq] past int32, and a split workspace past 2^62 bytes
+    assert call(dims(num_seqs=65535, num_q_heads=1 << 16, num_kv_heads=1)) == -2
+    big = dims(num_seqs=4096, num_q_heads=1 << 19, num_kv_heads=1, max_blocks_per_seq=1 << 27,
+               max_context_len=(1 << 31) - 1, partition_size=16)
+    assert kvd.workspace_bytes(big) == 0 and call(big) == -2
+    # runs so long that their token indices would pass int32
+    assert call(dims(num_seqs=1, max_blocks_per_seq=1 << 27, max_context_len=(1 << 31) - 64,
+                     partition_size=1 << 20, partitions_per_wave=1 << 28)) == -2
 
 
 @pytest.mark.parametrize("arg", ["q", "k", "v", "bt", "ctx", "out"])
