@@ -266,9 +266,9 @@ def read_probe(args):
 DTYPES = {
     "bf16": "bf16 K/V/q operands, P as a bf16 hi+lo pair; fp32 accumulate",
     "fp8": "bf16 operands (E4M3 K/V exactly), P as a bf16 hi+lo pair; fp32 accumulate",
-    "turbo8": "QK bf16 (E4M3 K exactly); PV fp16 (levels hi+lo, P' fp16); fp32 accumulate",
-    "turbo4": "fp16 operands (codebook levels and rotated q as hi+lo, P' fp16); fp32 accumulate",
-    "turbo3": "fp16 operands (codebook levels and rotated q as hi+lo, P' fp16); fp32 accumulate",
+    "turbo8": "QK bf16 (E4M3 K exactly); PV fp16 (V levels and P' fp16); fp32 accumulate",
+    "turbo4": "fp16 operands (K levels and rotated q as hi+lo; V levels and P' fp16); fp32 accumulate",
+    "turbo3": "fp16 operands (K levels and rotated q as hi+lo; V levels and P' fp16); fp32 accumulate",
 }
 
 

@@ -261,7 +261,8 @@ int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cac
  * values (one thread per element, its own page addressing and index extraction; it shares the
  * FP8 -> bf16 decode and the 3-bit field selection with the attention kernel).  The attention
  * kernel never forms norm * codebook[index]: it factors the norm out and feeds the levels to
- * its matrix cores as fp16 hi + lo pairs; kvd_dequant_operands exports those operands.  Tokens
+ * its matrix cores in fp16 (K levels as hi + lo pairs, V levels rounded once);
+ * kvd_dequant_operands exports those operands.  Tokens
  * must lie in [0, 16 * max_blocks_per_seq). */
 int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cache,
                        const float* scales, const float* codebook, const int32_t* block_table,
@@ -285,10 +286,10 @@ int kvd_dequant_gather(const kvd_dims* dims, int fmt, int is_v, const void* cach
  *   x1 = 0.  Turbo4/3 K: x0 = fp16 [h0 .. h7], x1 = fp16 [l0 .. l7] of the eight elements,
  *   with (h, l) = (fp16(c), fp16(c - h)) of c = codebook level * 2^-E, 2^-E the power of two
  *   that puts the largest K level magnitude in [0.5, 1).
- * Words [D/2 + 8 t, D/2 + 8 t + 8), t = 0 .. D/16 - 1: PV tile t operands v0, v1 for head
- *   element d = 16 t + n and the lane's eight softmax tokens e: BF16 / FP8 v0 = bf16 values,
- *   v1 = 0; codebook V: v0 = fp16 [h0 h1 l0 l1 h2 h3 l2 l3] of tokens 0..3, v1 of 4..7 (V
- *   levels, normaliser of the V levels).
+ * Words [D/2 + 8 t, D/2 + 8 t + 8), t = 0 .. D/16 - 1: PV tile t operand v (4 words), then 4
+ *   zero words, for head element d = 16 t + n and the lane's eight softmax tokens e: BF16 /
+ *   FP8 v = bf16 values; codebook V: v = fp16 [c0 .. c7], c = fp16(V level * 2^-E), 2^-E the
+ *   power of two that puts the largest V level magnitude in [0.5, 1).
  * Words [D, D + 16): fp32 K norms of the eight softmax tokens (Turbo4/3; else 0), then their
  *   V norms (codebook V; else 0), as stored after the chunks' indices.
  * A pair with a block-table entry outside the pool gets all-ones records. */

@@ -25,11 +25,12 @@
 //           16-lane groups with two permlane swaps; the reference max moves lazily);
 //         - accumulates O^T += V^T P^T with the same MFMA shape.
 //       Operand precision: BF16 and FP8 K/V (and Turbo8 K) use exact bf16 operands and feed P
-//       as a bf16 hi + lo pair (2^-16 relative).  Codebook levels and the rotated query are
+//       as a bf16 hi + lo pair (2^-16 relative).  Codebook K levels and the rotated query are
 //       fp16 hi + lo pairs (about 2^-20 relative; plain fp16 levels or query would add a
-//       logit error that large logits turn into a visible output error) and P is rounded once
-//       to fp16 (2^-12, random), with power-of-two scalings that keep every fp16 value in
-//       range.
+//       logit error that large logits turn into a visible output error).  Codebook V levels
+//       and P are each rounded once to fp16 (2^-12 relative; the output error they add is
+//       relative to the row and independent of the logits' size).  Power-of-two scalings
+//       keep every fp16 value in range.
 //       The MFMA output layout of S^T (lane = query row, 4 lane groups x 4 rows = 16 tokens) is
 //       exactly the B-operand layout of P^T for the PV product once the pair's two pages are
 //       interleaved as below, so no data moves between the two products.
@@ -139,38 +140,34 @@ __device__ __forceinline__ u32x2 fp8x4_to_bf16(uint32_t w) {
     return u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Codebook pair tables.  Entry (i0 + n * i1), n = 16 (4-bit) or 8 (3-bit), holds the packed
-// fp16 dwords of the two levels (c[i0], c[i1]): hi = hi(c[i0]) | hi(c[i1]) << 16 and
-// lo = lo(c[i0]) | lo(c[i1]) << 16, with c ~= hi + lo.  Entries are 256 bytes apart, and each
-// table is stored kLutCopies = 32 times so that lane l reads copy l % 32: the lanes of one LDS
-// pass then hit different banks whatever the indices (a single shared table costs about 3.3x
-// more LDS cycles for random indices).  The address of entry b (a byte of the index word w) is
+// Codebook pair tables.  Entry (i0 + n * i1), n = 16 (4-bit) or 8 (3-bit), holds packed fp16
+// dwords of the two levels (c[i0], c[i1]).  Entries are 256 bytes apart, and each table is
+// stored kLutCopies = 32 times so that lane l reads copy l % 32: the lanes of one LDS pass then
+// hit different banks whatever the indices (a single shared table costs about 3.3x more LDS
+// cycles for random indices).  The address of entry b (a byte of the index word w) is
 // lanebase.byte0 | b << 8 | lanebase.byte2 << 16, one v_perm_b32.
 //
-// V table (after the K table, else at LDS byte 0): copy c of entry e is the 8-byte pair
-// {hi, lo} at e * 256 + c * 8 (lanebase = (l % 32) * 8).  Four reads give eight indices as the
-// "interleaved" MFMA operands a0 = {hi(e0,e1), lo(e0,e1), hi(e2,e3), lo(e2,e3)}, a1 the same
-// for e4..e7, i.e. fp16 k-slots [h0 h1 l0 l1 h2 h3 l2 l3]; against the repeated P operand
-// [p0 p1 p0 p1 p2 p3 p2 p3] one MFMA accumulates (hi + lo) * p for four tokens.
+// V table (after the K table, else at LDS byte 0): copy c of entry e is the dword
+// fp16(c[i0]) | fp16(c[i1]) << 16 at e * 256 + c * 4 (lanebase = (l % 32) * 4 plus the table's
+// offset; the upper half of each 256-byte row is unused).  Four reads give eight indices as one
+// MFMA operand, fp16 k-slots [c0 .. c7], against P' in the same slots.
 //
-// K table (codebook K, LDS byte 0): the two halves separately, copy c of entry e's hi dword at
+// K table (codebook K, LDS byte 0): levels as hi + lo fp16 pairs, hi = hi(c[i0]) | hi(c[i1]) << 16
+// and lo = lo(c[i0]) | lo(c[i1]) << 16 with c ~= hi + lo, the two halves stored separately:
+// copy c of entry e's hi dword at
 // e * 256 + c * 4 and of its lo dword kKLoOffset bytes further on (lanebase = (l % 32) * 4).
 // Eight reads give eight indices as two plain operands, k-slots [h0 .. h7] and [l0 .. l7], so
 // the query operand needs no repeated slots: hi * q_hi + lo * q_hi + hi * q_lo takes three MFMAs
 // per eight elements and 8 VGPRs of query per 32 elements.
-template <int K>
-__device__ __forceinline__ u32x2 lut_byte(const char* lds, uint32_t lanebase, uint32_t w) {
-    static_assert(K >= 0 && K < 4, "byte index");
-    const uint32_t addr = __builtin_amdgcn_perm(w, lanebase, (12u << 24) | (2u << 16) | ((4u + K) << 8));
-    return *reinterpret_cast<const u32x2*>(lds + addr);
-}
-// 8 4-bit indices (index e at bits 4e of w).
-__device__ __forceinline__ void lut_nib8(const char* lds, uint32_t lanebase, uint32_t w,
-                                         u32x4& a0, u32x4& a1) {
-    const u32x2 e0 = lut_byte<0>(lds, lanebase, w), e1 = lut_byte<1>(lds, lanebase, w);
-    const u32x2 e2 = lut_byte<2>(lds, lanebase, w), e3 = lut_byte<3>(lds, lanebase, w);
-    a0 = u32x4{e0[0], e0[1], e1[0], e1[1]};
-    a1 = u32x4{e2[0], e2[1], e3[0], e3[1]};
+// V table: 8 4-bit indices (index e at bits 4e of w) -> one operand.
+__device__ __forceinline__ u32x4 vlut_nib8(const char* lds, uint32_t lanebase, uint32_t w) {
+    u32x4 a;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t addr = __builtin_amdgcn_perm(w, lanebase, (12u << 24) | (2u << 16) | ((4u + k) << 8));
+        a[k] = *reinterpret_cast<const uint32_t*>(lds + addr);
+    }
+    return a;
 }
 // K table: 8 4-bit indices (index e at bits 4e of w) -> hi and lo operands.
 __device__ __forceinline__ void klut_nib8(const char* lds, uint32_t lanebase, uint32_t w,
@@ -404,21 +401,18 @@ __device__ __forceinline__ void k_operands(const PairRaw<FMT, D>& r, int s, cons
     }
 }
 
-// The A operand(s) of PV tile t (head elements 16t + n, the lane's eight tokens as k-slots).
-// BF16 / FP8 V: one bf16x8 operand in v0 (v1 zero).  Codebook V: two interleaved fp16 hi / lo
-// operands from the V pair table (v0 = tokens 0..3, v1 = 4..7).
+// The A operand of PV tile t (head elements 16t + n, the lane's eight tokens as k-slots):
+// bf16x8 for BF16 / FP8 V, fp16x8 from the V pair table for codebook V.
 template <int FMT, int D>
-__device__ __forceinline__ void v_operands(const PairRaw<FMT, D>& r, int t, const char* lds,
-                                           uint32_t vbase, u32x4& v0, u32x4& v1) {
+__device__ __forceinline__ u32x4 v_operand(const PairRaw<FMT, D>& r, int t, const char* lds,
+                                           uint32_t vbase) {
     if constexpr (FMT == KVD_BF16) {
-        v0 = r.v[t];
-        v1 = u32x4{0u, 0u, 0u, 0u};
+        return r.v[t];
     } else if constexpr (FMT == KVD_FP8_E4M3) {
         const u32x2 a0 = fp8x4_to_bf16(r.v[t][0]), a1 = fp8x4_to_bf16(r.v[t][1]);
-        v0 = u32x4{a0[0], a0[1], a1[0], a1[1]};
-        v1 = u32x4{0u, 0u, 0u, 0u};
+        return u32x4{a0[0], a0[1], a1[0], a1[1]};
     } else {
-        lut_nib8(lds + (v_table_base<FMT>() & 0xFFFF), vbase, r.v[t], v0, v1);
+        return vlut_nib8(lds + (v_table_base<FMT>() & 0xFFFF), vbase, r.v[t]);
     }
 }
 
@@ -458,7 +452,7 @@ __device__ __forceinline__ Levels load_levels(const float* codebook, int kbits, 
 // with the levels scaled by the power-of-two normalisers ksc / vsc.  NT threads (a multiple of
 // 256): thread t takes entry t % 256 and every (NT / 256)-th of its sixteen 16-byte slots
 // (K: slots 0..7 hold four hi copies each, 8..15 four lo copies, kKLoOffset - 128 bytes
-// further on; V: two {hi, lo} copies each).
+// further on; V: slots 0..7 hold four copies each, 8..15 are unused).
 // The slot order is staggered by entry, so the 16 lanes of a store pass write 16 different
 // 16-byte bank groups (entries are 256 bytes apart: the same slot of every entry would sit in
 // the same banks).
@@ -469,10 +463,11 @@ __device__ __forceinline__ void fill_tables(char* lds, int tid, const Levels& lv
     constexpr bool kKcb = k_codebook<FMT>();
     constexpr int kParts = NT / 256;
     const int e = tid & 255, part = tid >> 8;
-    uint32_t kh = 0u, kl = 0u, vh, vl;
+    uint32_t kh = 0u, kl = 0u;
     if constexpr (kKcb) f16_hilo(lv.k0 * ksc, lv.k1 * ksc, kh, kl);
-    f16_hilo(lv.v0 * vsc, lv.v1 * vsc, vh, vl);
-    const u32x4 khi = {kh, kh, kh, kh}, klo = {kl, kl, kl, kl}, vv = {vh, vl, vh, vl};
+    const f16x2 vp = {(_Float16)(lv.v0 * vsc), (_Float16)(lv.v1 * vsc)};
+    const uint32_t vh = __builtin_bit_cast(uint32_t, vp);
+    const u32x4 khi = {kh, kh, kh, kh}, klo = {kl, kl, kl, kl}, vv = {vh, vh, vh, vh};
     char* const vt = lds + v_table_base<FMT>();
 #pragma unroll
     for (int i = 0; i < (16 + kParts - 1) / kParts; ++i) {
@@ -482,7 +477,7 @@ __device__ __forceinline__ void fill_tables(char* lds, int tid, const Levels& lv
             if constexpr (kKcb)
                 *reinterpret_cast<u32x4*>(lds + e * 256 + slot * 16 + (slot < 8 ? 0 : kKLoOffset - 128)) =
                 slot < 8 ? khi : klo;
-            *reinterpret_cast<u32x4*>(vt + e * 256 + slot * 16) = vv;
+            if (slot < 8) *reinterpret_cast<u32x4*>(vt + e * 256 + slot * 16) = vv;
         }
     }
 }
@@ -647,7 +642,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     const int n = ln.n, j = ln.j;
     // table copy of this lane: 4-byte K halves at byte 0, 8-byte V pairs after the K table
     const uint32_t kbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
-    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 8u | (uint32_t)(v_table_base<FMT>() & 0x10000);
+    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u | (uint32_t)(v_table_base<FMT>() & 0x10000);
 
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
@@ -934,23 +929,17 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         l_run += psum;
 
         if constexpr (kVcb) {
-            // P' = p * vnorm / sigma, rounded once to fp16 (each value repeated to match the
-            // interleaved hi/lo V operand); the V levels keep their hi + lo precision
-            uint32_t ph[4];
+            // P' = p * vnorm / sigma, rounded once to fp16
+            u32x4 pb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f16x2 h = {(_Float16)(pe[2 * i] * (vn[2 * i] * inv_sig)),
                                  (_Float16)(pe[2 * i + 1] * (vn[2 * i + 1] * inv_sig))};
-                ph[i] = __builtin_bit_cast(uint32_t, h);
+                pb[i] = __builtin_bit_cast(uint32_t, h);
             }
-            const u32x4 pb0 = {ph[0], ph[0], ph[1], ph[1]}, pb1 = {ph[2], ph[2], ph[3], ph[3]};
 #pragma unroll
-            for (int t = 0; t < VT; ++t) {
-                u32x4 v0, v1;
-                v_operands<FMT, D>(r, t, lds_bytes, vbase, v0, v1);
-                oacc[t] = mfma_f16(v0, pb0, oacc[t]);
-                oacc[t] = mfma_f16(v1, pb1, oacc[t]);
-            }
+            for (int t = 0; t < VT; ++t)
+                oacc[t] = mfma_f16(v_operand<FMT, D>(r, t, lds_bytes, vbase), pb, oacc[t]);
         } else {
             u32x4 phi, plo;
 #pragma unroll
@@ -964,8 +953,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             }
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
-                u32x4 vop, vunused;
-                v_operands<FMT, D>(r, t, lds_bytes, vbase, vop, vunused);
+                const u32x4 vop = v_operand<FMT, D>(r, t, lds_bytes, vbase);
                 oacc[t] = mfma_bf16(vop, phi, oacc[t]);
                 oacc[t] = mfma_bf16(vop, plo, oacc[t]);
             }
@@ -1254,10 +1242,10 @@ __global__ __launch_bounds__(256) void gather_kernel(const GatherParams p) {
 // 512 threads (eight waves), the same table build as the partition kernel's codebook formats;
 // wave w of workgroup x takes page pair pair0 + 8x + w of one (sequence, KV head) (pages 2k and
 // 2k + 1 of the sequence), loads it with load_pair and the lane map of the partition kernel and
-// forms the QK and PV operands with k_operands / v_operands.  Record of lane l (D + 16 words):
-// for each QK step s: x0, x1, y0, y1; for each PV tile t: v0, v1; then K norms (8 floats of the
-// lane's eight softmax tokens), V norms (8), zero where the format has none.  A pair whose block
-// table entry lies outside the pool writes all-ones records.
+// forms the QK and PV operands with k_operands / v_operand.  Record of lane l (D + 16 words):
+// for each QK step s: x0, x1, y0, y1; for each PV tile t: v, then four zero words; then K norms
+// (8 floats of the lane's eight softmax tokens), V norms (8), zero where the format has none.
+// A pair whose block table entry lies outside the pool writes all-ones records.
 template <int FMT, int D>
 __global__ __launch_bounds__(512) void operand_kernel(const OperandParams op) {
     constexpr bool kKcb = k_codebook<FMT>();
@@ -1279,7 +1267,7 @@ __global__ __launch_bounds__(512) void operand_kernel(const OperandParams op) {
     const int pair = op.pair0 + k;
     const LaneMap ln = lane_map(lane);
     const uint32_t kbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u;
-    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 8u | (uint32_t)(v_table_base<FMT>() & 0x10000);
+    const uint32_t vbase = (uint32_t)(lane & (kLutCopies - 1)) * 4u | (uint32_t)(v_table_base<FMT>() & 0x10000);
     uint32_t* rec = op.out + ((size_t)k * 64 + lane) * W;
     const int32_t* btrow = p.bt + (size_t)op.seq * p.max_blocks;
     const int pa = btrow[2 * pair], pb = btrow[2 * pair + 1];
@@ -1298,10 +1286,8 @@ __global__ __launch_bounds__(512) void operand_kernel(const OperandParams op) {
     }
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-        u32x4 v0, v1;
-        v_operands<FMT, D>(r, t, lds_bytes, vbase, v0, v1);
-        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t) = v0;
-        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t + 4) = v1;
+        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t) = v_operand<FMT, D>(r, t, lds_bytes, vbase);
+        *reinterpret_cast<u32x4*>(rec + D / 2 + 8 * t + 4) = u32x4{0u, 0u, 0u, 0u};
     }
     f32x4 nrm[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     if constexpr (kKcb) { nrm[0] = r.kn0; nrm[1] = r.kn1; }

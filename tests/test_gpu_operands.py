@@ -44,14 +44,12 @@ def _hilo_bits(levels):
     return hi.view(np.uint16).astype(np.uint32), lo.view(np.uint16).astype(np.uint32)
 
 
-def _interleaved(idx8, hi, lo):
-    """Words [h0|h1, l0|l1, h2|h3, l2|l3] and the same for elements 4..7 of eight indices."""
-    words = []
-    for base in (0, 4):
-        i = idx8[base: base + 4]
-        words += [hi[i[0]] | hi[i[1]] << 16, lo[i[0]] | lo[i[1]] << 16,
-                  hi[i[2]] | hi[i[3]] << 16, lo[i[2]] | lo[i[3]] << 16]
-    return np.array(words, dtype=np.uint32)
+def _f16_bits(levels):
+    """fp16 bit patterns of each level scaled by 2^-E (largest magnitude in [0.5, 1)), rounded
+    once to nearest even."""
+    lv = np.asarray(levels, dtype=np.float32)
+    _, e = np.frexp(np.abs(lv).max())
+    return (lv * np.float32(2.0 ** -int(e))).astype(np.float16).view(np.uint16).astype(np.uint32)
 
 
 def _split(idx8, hi, lo):
@@ -78,11 +76,11 @@ def expected_records(inp, b, hk, n_pairs):
     vs = oracle.gather_stored(fmt, "v", inp.v_cache, inp.block_table[b], hk, 0, T, D)
     kkind, vkind = oracle.attention.elem_kind(fmt, "k"), oracle.attention.elem_kind(fmt, "v")
     klev, vlev = (oracle.attention.codebooks(fmt, inp.codebook) if vkind == "cb" else (None, None))
-    kh = kl = vh = vl = None
+    kh = kl = vh = None
     if kkind == "cb":
         kh, kl = _hilo_bits(klev)
     if vkind == "cb":
-        vh, vl = _hilo_bits(vlev)
+        vh = _f16_bits(vlev)
     e4m3_bf16 = _bf16_bits_of(oracle.E4M3FN_TABLE.astype(np.float32))
     kn = vn = None      # [pool][Hkv][16]: the norms after each chunk's indices
     if kkind == "cb":
@@ -127,7 +125,7 @@ def expected_records(inp, b, hk, n_pairs):
                         if np.isnan(oracle.E4M3FN_TABLE[codes[e]]):
                             nan[k, lane, w0 + e // 2] = True
                 else:
-                    rec[w0: w0 + 8] = _interleaved(vs[toks, d], vh, vl)
+                    rec[w0: w0 + 4] = _pairs_of_bits(vh[vs[toks, d]])
             phys = np.asarray(inp.block_table[b])[toks // 16]
             for plane, off in ((kn, D), (vn, D + 8)):
                 if plane is not None:
