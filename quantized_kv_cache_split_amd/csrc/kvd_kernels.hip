@@ -887,27 +887,31 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                 for (int t = 0; t < VT; ++t) { r.v[t][0] &= mb[0]; r.v[t][1] &= mb[1]; }
             }
         }
+        // maxima over the lane's eight tokens; m_true is reduced over the row's four lane
+        // groups only once, at the end of the walk
         float mloc = z[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, z[e]);
-        mloc = max_over_groups(mloc);
         m_true = fmaxf(m_true, mloc);
         // Lazy rescaling: the reference max m_run (and, for the codebook formats, the V-norm
         // reference sig_run) only moves when some query's new logits exceed it by more than
         // 2^kLazyLog2 (or a norm exceeds it kLazySig-fold), so P stays <= 2^8 (P' <= 2^12) and
-        // the accumulator rescale is skipped on almost every pair.  The choice is wave-uniform.
+        // the accumulator rescale is skipped on almost every pair.  The choice is wave-uniform
+        // (a ballot of the lanes' own tests); only a rescale needs the maxima over the row's
+        // four lane groups, which keep m_run and sig_run the same in all of them.
         bool grow = mloc > m_run + kLazyLog2;
         float vloc = 0.0f;
         if constexpr (kVcb) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) vloc = fmaxf(vloc, vn[e]);
-            vloc = max_over_groups(vloc);
             grow = grow || (vloc > sig_run * kLazySig);
         }
         // (chunks of queries: maxima are clamped to -FLT_MAX where they enter a difference: a
         // query row that has not seen a key yet keeps m = -inf, and -inf - -inf would be NaN;
         // with one query per sequence every computed pair holds a key of the range)
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            mloc = max_over_groups(mloc);
+            if constexpr (kVcb) vloc = max_over_groups(vloc);
             const float m_new = fmaxf(m_run, mloc);
             float f = MQ ? fast_exp2(fmaxf(m_run, -FLT_MAX) - fmaxf(m_new, -FLT_MAX))
                          : fast_exp2(m_run - m_new);
@@ -1035,6 +1039,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // no key of the run: m = -inf, l = 0, o = 0.
     if (si.split) {
         if (!live) return;
+        m_true = max_over_groups(m_true);
         float lt = l_run + __shfl_xor(l_run, 16);
         lt += __shfl_xor(lt, 32);
         const float osc = kVcb ? oscale * sig_run : oscale;

@@ -151,6 +151,23 @@ def test_ragged_window_softcap(fmt):
     assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} ragged+window+cap")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.09, -1.0])
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_zero_and_negative_softmax_scale(fmt, scale):
+    """A zero scale gives every attended key the same weight (the output is the mean of V); a
+    negative one reverses the logits' order.  Split and unsplit rows, with and without ALiBi,
+    and (BF16, Turbo4) with a softcap."""
+    inp = _small(fmt, context=None, ctx_range=(1, 3000), num_seqs=4, softmax_scale=scale)
+    assert_close(GpuBatch(inp).run(), _oracle(inp), f"{fmt} scale={scale}")
+    sl = _slopes(8)
+    assert_close(GpuBatch(inp, alibi=sl).run(),
+                 oracle.decode_attention(*oracle_args(inp), alibi=sl), f"{fmt} scale={scale} alibi")
+    if fmt in ("bf16", "turbo4"):
+        capped = _small(fmt, context=None, ctx_range=(1, 3000), num_seqs=4, softmax_scale=scale,
+                        softcap=2.0)
+        assert_close(GpuBatch(capped).run(), _oracle(capped), f"{fmt} scale={scale} cap 2")
+
+
 def test_large_logits_softcap():
     inp = _small("bf16", context=2000, softmax_scale=1.0, softcap=5.0)
     assert_close(GpuBatch(inp).run(), _oracle(inp), "bf16 cap 5, scale 1")
