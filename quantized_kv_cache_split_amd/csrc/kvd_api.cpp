@@ -53,6 +53,15 @@ int64_t query_rows(const kvd_dims* d) {
 int query_tiles(const kvd_dims* d) {
     return (int)((query_rows(d) + kvd::kMaxGroup - 1) / kvd::kMaxGroup);
 }
+// Query tiles one wave computes (two where a KV head has several tiles and the format has the
+// two-tile build), and the work units per KV head.
+int tiles_per_unit(const kvd_dims* d, int fmt) {
+    return query_tiles(d) >= 2 && kvd::tile_pairs_built(fmt, queries(d) > 1, false) ? 2 : 1;
+}
+int units_per_head(const kvd_dims* d, int fmt) {
+    const int nt = tiles_per_unit(d, fmt);
+    return (query_tiles(d) + nt - 1) / nt;
+}
 
 // Compute units of the current device (256 on MI355X when the query fails).
 int device_cus() {
@@ -96,14 +105,15 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
         const int64_t len = ragged ? d->mean_context_len : d->max_context_len;
         const int64_t pairs = (len + pair_tokens - 1) / pair_tokens;
-        const int64_t units = (int64_t)d->num_kv_heads * query_tiles(d) * d->num_seqs;
+        const int64_t units = (int64_t)d->num_kv_heads * units_per_head(d, fmt) * d->num_seqs;
         auto run_for = [&](bool w) -> int64_t {
             int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w);
             if (ragged) slots = slots * 5 / 2;                        // 2.5 rounds of work
             const int64_t rp = (pairs * units + slots - 1) / slots;   // pairs per wave
             return rp * pair_tokens < ps ? ps : rp * pair_tokens;
         };
-        if (!ragged && kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
+        if (!ragged && tiles_per_unit(d, fmt) == 1 &&
+            kvd::wide_layout_built(fmt, d->head_dim, queries(d) > 1)) {
             const int64_t t = run_for(true);
             if (t <= (int64_t)kvd::kMaxRunWide * ps) {
                 wide = true;
@@ -240,6 +250,8 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.g = d->num_q_heads / d->num_kv_heads;
     p.nq = queries(d);
     p.qt = query_tiles(d);
+    p.nt = tiles_per_unit(d, fmt);
+    p.qg = units_per_head(d, fmt);
     p.D = d->head_dim;
     p.max_blocks = d->max_blocks_per_seq;
     p.pool = d->num_pool_blocks;
@@ -265,7 +277,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     if (phases & kPhase1) {
         // `waves` waves per workgroup, one run per wave
         const int px = pl.P ? (int)((runs + waves - 1) / waves) : 1;
-        const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qt * d->num_seqs;
+        const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qg * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);
         e = kvd::launch_partitions(fmt, rc.wide, p, grid, s);

@@ -21,6 +21,10 @@ constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave 
 // cover the chip in one round (a large ragged batch balances better with short runs).
 constexpr int kMaxRunWide = 8;
 constexpr bool wide_layout_built(int fmt, int d, bool mq) { return fmt == 0 && d == 128 && !mq; }
+// Query tiles per wave: single-query BF16 / FP8 in the two-workgroup layout also have a build
+// in which one wave computes two 16-row query tiles of a KV head (query groups above 16 rows,
+// e.g. MQA), so the tiles share every page load and dequantisation.
+constexpr bool tile_pairs_built(int fmt, bool mq, bool wide) { return (fmt == 0 || fmt == 1) && !mq && !wide; }
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
 // the codebook formats (sharing conflict-free codebook tables: 130 KB for Turbo4 / Turbo3, one
 // workgroup per CU; 64 KB for Turbo8).  Measured on Turbo4 / Turbo3: twelve waves per workgroup
@@ -64,6 +68,8 @@ struct LaunchParams {
     int32_t B, Hq, Hkv, g, D;
     int32_t nq;               // queries per sequence (a chunk at the last positions; 1 = decode)
     int32_t qt;               // query tiles per KV head: ceil(nq * g / kMaxGroup)
+    int32_t nt;               // query tiles per work unit (1, or 2: tile_pairs_built)
+    int32_t qg;               // work units per KV head: ceil(qt / nt)
     int32_t max_blocks, pool, max_ctx;
     int32_t part_mode;        // PartMode
     int32_t part_size;        // tokens per partition (split sequences)

@@ -505,10 +505,12 @@ __device__ __forceinline__ LaneMap lane_map(int lane) {
 // its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
 // partitions.
-template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE>
+template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE, int NT>
 __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) void partition_kernel(const LaunchParams p) {
     constexpr bool kKcb = k_codebook<FMT>();   // rotated query, K table, K norms
     constexpr bool kVcb = v_codebook<FMT>();   // V table, V norms, output in the rotated domain
+    static_assert(NT == 1 || tile_pairs_built(FMT, MQ, WIDE), "query tiles per wave");
+    constexpr int kRows = NT * kMaxGroup;      // query rows of one work unit
     constexpr int kW = waves_per_group(FMT);   // waves per workgroup
     constexpr int kThr = 64 * kW;
     constexpr int KS = D / 32;   // QK MFMA steps (k = 32 head elements each)
@@ -523,6 +525,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // address 0 (K and V, 128 KB, one workgroup per CU for Turbo4 / Turbo3; V only, 64 KB, two
     // per CU for Turbo8), reused for the unsplit merge once every wave has finished its walk.
     constexpr int SR = kVcb ? kMaxGroup : stage_rows(D, WIDE);
+    static_assert(SR >= kRows, "merge rows of a unit");
     constexpr int SD = D + 4;
     struct Merge {
         float m[kW][SR];
@@ -554,28 +557,29 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // sequence); x fastest would pile the short sequences' work onto the XCDs of small x.
     // The query rows of one KV head are (query i of the chunk, head of the group), i-major:
     // p.nq * p.g rows (p.g for single-query decode).  More rows than kMaxGroup are split into
-    // p.qt tiles ("virtual heads") of up to kMaxGroup rows, each processed like a KV head of its
-    // own (its pages are read once per tile).
+    // p.qt MFMA tiles of up to kMaxGroup rows; a work unit ("virtual head") takes NT of them,
+    // so a KV head has p.qg = ceil(p.qt / NT) units, each processed like a KV head of its own
+    // (its pages are read once per unit; NT tiles share each load and dequantisation).
     // Units that read the same lines run on one XCD at the same time, so its L2 fetches each
-    // line once for all of them: the p.qt query tiles of a KV head read the same pages.  With
+    // line once for all of them: the p.qg units of a KV head read the same pages.  With
     // m such consecutive units, within every full block of 8m workgroups, unit m * x + j goes
     // to linear id 8 * j + x (XCD x, dispatched in consecutive rounds).  A bijection on full
     // blocks, the identity on the tail.
     int wg = blockIdx.x;
-    if (const int m = p.qt; m > 1) {
+    if (const int m = p.qg; m > 1) {
         const int blk = 8 * m;
         if (wg < (int)gridDim.x / blk * blk) {
             const int r = wg % blk;
             wg += (r & 7) * m + (r >> 3) - r;
         }
     }
-    const int nvh = p.Hkv * p.qt;
+    const int nvh = p.Hkv * p.qg;
     const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = wg / (nvh * p.B);
-    const int hk = vh / p.qt, qtile = vh - hk * p.qt;
+    const int hk = vh / p.qg, unit = vh - hk * p.qg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int rbase = qtile * kMaxGroup;                          // first row of the tile
-    const int g = min(kMaxGroup, (MQ ? p.nq : 1) * p.g - rbase);  // rows in the tile
+    const int rbase = unit * kRows;                           // first row of the unit
+    const int g = min(kRows, (MQ ? p.nq : 1) * p.g - rbase);  // rows in the unit
     const SeqInfo si = seq_info<MQ>(p, b);
     // q / out / workspace row (b, i, h) of tile row t (q and out are [B][nq][Hq][D]): row
     // rbase + t of the KV head is query i = (rbase + t) / g, head hk * g + (rbase + t) - i * g,
@@ -647,6 +651,10 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
+    // tile u of the unit: rows 16u + n (NT > 1 only for single-query BF16 / FP8)
+    bool tlive[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) tlive[u] = kMaxGroup * u + n < g;
     // the lane's query: index in the chunk, position, and the keys [row_lo, row_hi) it sees;
     // the keys every row of the tile sees: [tile_lo, tile_hi) (the unmasked fast path).  One
     // query per sequence: every row sees the sequence's whole range.
@@ -657,7 +665,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     const int tile_hi = MQ ? si.L - p.nq + rbase / p.g + 1 : si.L;
     const int tile_lo = MQ ? (si.W > 0 ? max(0, si.L - p.nq + (rbase + g - 1) / p.g + 1 - si.W) : 0)
                            : si.lo;
-    u32x4 qop[KS];                      // BF16 / FP8 K: q (bf16) for step s
+    u32x4 qop[NT][KS];                  // BF16 / FP8 K: q (bf16) of tile u for step s
     u32x4 qhi[kKcb ? KS : 1];           // codebook K: fp16 hi parts of q for step s
     u32x4 qlo[kKcb ? KS : 1];           // codebook K: fp16 lo parts
     float zscale;           // logit -> base-2 softmax argument (without per-token factors)
@@ -722,12 +730,15 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         }
         zscale = p.softmax_scale * kLog2e / (qs * ksc * sqrtf((float)D));
     } else {
-        const uint16_t* qptr = p.q + row_index(qn) * D;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int d0 = (FMT == KVD_BF16) ? 32 * s + 8 * j : 64 * (s / 2) + 16 * j + 8 * (s % 2);
-            const u32x4 w = *reinterpret_cast<const u32x4*>(qptr + d0);
-            qop[s] = qlive ? w : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < NT; ++u) {
+            const uint16_t* qptr = p.q + row_index(min(kMaxGroup * u + n, g - 1)) * D;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const int d0 = (FMT == KVD_BF16) ? 32 * s + 8 * j : 64 * (s / 2) + 16 * j + 8 * (s % 2);
+                const u32x4 w = *reinterpret_cast<const u32x4*>(qptr + d0);
+                qop[u][s] = tlive[u] ? w : u32x4{0u, 0u, 0u, 0u};
+            }
         }
         zscale = p.softmax_scale * kLog2e;
         if constexpr (FMT == KVD_FP8_E4M3) {   // scales [2][Hkv]: K then V
@@ -739,16 +750,26 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     }
     const float cap_l2 = CAP ? p.softcap * kLog2e : 0.0f;      // cap in base-2 units
     const float inv_cap_l2 = CAP ? 1.0f / cap_l2 : 0.0f;
-    // ALiBi slope of this lane's query head, in base-2 units (0 without ALiBi)
+    // ALiBi slope of the lane's query head in each tile, in base-2 units (0 without ALiBi)
     const bool alibi = p.alibi != nullptr;
-    const float slope_l2 = alibi ? p.alibi[hk * p.g + (rbase + qn - q_i * p.g)] * kLog2e : 0.0f;
+    float slope_l2[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+        slope_l2[u] = alibi ? p.alibi[hk * p.g + (rbase + min(kMaxGroup * u + n, g - 1) - q_i * p.g)] * kLog2e
+                            : 0.0f;
 
     // ---- state -------------------------------------------------------------------------
-    f32x4 oacc[VT];
+    f32x4 oacc[NT][VT];
+    float m_run[NT], l_run[NT];   // per tile: softmax reference max (base 2) and sum
+    float m_true[NT];             // per tile: the exact running max of the lane's logits
 #pragma unroll
-    for (int i = 0; i < VT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.0f;   // softmax reference max (base 2) and sum
-    float m_true = -INFINITY;                 // the exact running max of the logits
+    for (int u = 0; u < NT; ++u) {
+#pragma unroll
+        for (int i = 0; i < VT; ++i) oacc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[u] = -INFINITY;
+        l_run[u] = 0.0f;
+        m_true[u] = -INFINITY;
+    }
     constexpr float kSigInit = 1.17549435e-38f;
     constexpr float kLazyLog2 = 8.0f, kLazySig = 16.0f;
     float sig_run = kSigInit;   // reference V norm (codebook formats), 1 / sig_run
@@ -778,40 +799,47 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     };
 
     // ---- one pair's logits: S^T = K Q^T for its two 16-token tiles ------------------------
-    auto qk = [&](Raw& r, f32x4& sx, f32x4& sy) {
-        sx = f32x4{0.f, 0.f, 0.f, 0.f};
-        sy = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
+    // (one set of K operands per step serves all NT query tiles)
+    auto qk = [&](Raw& r, f32x4 (&sx)[NT], f32x4 (&sy)[NT]) {
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            sx[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sy[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if constexpr (!kKcb) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 u32x4 x0, x1, y0, y1;
                 k_operands<FMT, D>(r, s, lds_bytes, kbase, x0, x1, y0, y1);
-                sx = mfma_bf16(x0, qop[s], sx);
-                sy = mfma_bf16(y0, qop[s], sy);
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    sx[u] = mfma_bf16(x0, qop[u][s], sx[u]);
+                    sy[u] = mfma_bf16(y0, qop[u][s], sy[u]);
+                }
             }
         } else {
+            f32x4 sx2 = {0.f, 0.f, 0.f, 0.f}, sy2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 u32x4 x0, x1, y0, y1;
                 k_operands<FMT, D>(r, s, lds_bytes, kbase, x0, x1, y0, y1);
                 // k hi * q hi + k lo * q hi + k hi * q lo, two accumulator chains per tile
-                sx = mfma_f16(x0, qhi[s], sx);
+                sx[0] = mfma_f16(x0, qhi[s], sx[0]);
                 sx2 = mfma_f16(x1, qhi[s], sx2);
-                sy = mfma_f16(y0, qhi[s], sy);
+                sy[0] = mfma_f16(y0, qhi[s], sy[0]);
                 sy2 = mfma_f16(y1, qhi[s], sy2);
                 sx2 = mfma_f16(x0, qlo[s], sx2);
                 sy2 = mfma_f16(y0, qlo[s], sy2);
             }
-            sx += sx2;
-            sy += sy2;
+            sx[0] += sx2;
+            sy[0] += sy2;
         }
     };
 
     // ---- one pair: online softmax and PV, given its logits ----------------------------------
     // A pair index at or past npairs is a no-op: its token window is empty, so every logit
     // is -inf, no reference moves, p = 0 and the V values are zero.
-    auto finish = [&](Raw& r, int k, f32x4 sx, f32x4 sy) {
+    auto finish = [&](Raw& r, int k, const f32x4 (&sx)[NT], const f32x4 (&sy)[NT]) {
         const int pgA = pg0 + 2 * min(k, npairs - 1);
         const bool hasB = pgA + 1 < pg1;
         const int hi_k = k < npairs ? hi : lo;
@@ -819,25 +847,32 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                                    ((pgA + 2) * kPageTokens <= min(hi_k, tile_hi))
                              : (pgA * kPageTokens >= lo) && hasB && ((pgA + 2) * kPageTokens <= hi_k);
 
-        float z[8];
+        float z[NT][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { z[e] = sx[e] * zscale; z[4 + e] = sy[e] * zscale; }
+        for (int u = 0; u < NT; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { z[u][e] = sx[u][e] * zscale; z[u][4 + e] = sy[u][e] * zscale; }
         if constexpr (kKcb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { z[e] *= r.kn0[e]; z[4 + e] *= r.kn1[e]; }
+            for (int e = 0; e < 4; ++e) { z[0][e] *= r.kn0[e]; z[0][4 + e] *= r.kn1[e]; }
         }
         if constexpr (CAP) {   // cap * tanh(x / cap), evaluated in base-2 units
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float t = fast_exp2(2.0f * kLog2e * (z[e] * inv_cap_l2));
-                z[e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
-            }
+            for (int u = 0; u < NT; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float t = fast_exp2(2.0f * kLog2e * (z[u][e] * inv_cap_l2));
+                    z[u][e] = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + t));
+                }
         }
         if (alibi) {   // + slope * (j - q_pos) for the lane's tokens j = tok0 .. tok0 + 7
             const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
-            const float base = slope_l2 * (float)(tok0 - q_pos);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] += base + slope_l2 * (float)e;
+            for (int u = 0; u < NT; ++u) {
+                const float base = slope_l2[u] * (float)(tok0 - q_pos);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[u][e] += base + slope_l2[u] * (float)e;
+            }
         }
         float vn[8];   // V norms (codebook V)
         if constexpr (kVcb) {
@@ -857,7 +892,9 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                 const int t = tok0 + e;
                 const bool ok = (t >= lo) && (t < hi_k) && (ln.v_sel == 0 || hasB);
                 vmask |= (ok ? 1u : 0u) << e;
-                z[e] = (ok && (!MQ || (t >= row_lo && t < row_hi))) ? z[e] : -INFINITY;
+#pragma unroll
+                for (int u = 0; u < NT; ++u)
+                    z[u][e] = (ok && (!MQ || (t >= row_lo && t < row_hi))) ? z[u][e] : -INFINITY;
             }
             if constexpr (kVcb) {
                 // table levels are always finite, so zero norms (possibly NaN in unused slots)
@@ -889,17 +926,24 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         }
         // maxima over the lane's eight tokens; m_true is reduced over the row's four lane
         // groups only once, at the end of the walk
-        float mloc = z[0];
+        float mloc[NT];
+        bool grow = false;
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mloc = fmaxf(mloc, z[e]);
-        m_true = fmaxf(m_true, mloc);
+        for (int u = 0; u < NT; ++u) {
+            mloc[u] = z[u][0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mloc[u] = fmaxf(mloc[u], z[u][e]);
+            m_true[u] = fmaxf(m_true[u], mloc[u]);
+            grow = grow || mloc[u] > m_run[u] + kLazyLog2;
+        }
         // Lazy rescaling: the reference max m_run (and, for the codebook formats, the V-norm
         // reference sig_run) only moves when some query's new logits exceed it by more than
         // 2^kLazyLog2 (or a norm exceeds it kLazySig-fold), so P stays <= 2^8 (P' <= 2^12) and
         // the accumulator rescale is skipped on almost every pair.  The choice is wave-uniform
         // (a ballot of the lanes' own tests); only a rescale needs the maxima over the row's
-        // four lane groups, which keep m_run and sig_run the same in all of them.
-        bool grow = mloc > m_run + kLazyLog2;
+        // four lane groups, which keep m_run and sig_run the same in all of them.  With several
+        // query tiles, a tile moves its reference only when its own logits ask for it, exactly
+        // as a one-tile walk would.
         float vloc = 0.0f;
         if constexpr (kVcb) {
 #pragma unroll
@@ -910,62 +954,78 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         // query row that has not seen a key yet keeps m = -inf, and -inf - -inf would be NaN;
         // with one query per sequence every computed pair holds a key of the range)
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            mloc = max_over_groups(mloc);
-            if constexpr (kVcb) vloc = max_over_groups(vloc);
-            const float m_new = fmaxf(m_run, mloc);
-            float f = MQ ? fast_exp2(fmaxf(m_run, -FLT_MAX) - fmaxf(m_new, -FLT_MAX))
-                         : fast_exp2(m_run - m_new);
-            l_run *= f;
+            [[maybe_unused]] float fsig = 1.0f;   // sigma_old / sigma_new (codebook V)
             if constexpr (kVcb) {
+                vloc = max_over_groups(vloc);
                 const float sig_new = fmaxf(sig_run, vloc);
                 inv_sig = __builtin_amdgcn_rcpf(sig_new);
-                f *= sig_run * inv_sig;
+                fsig = sig_run * inv_sig;
                 sig_run = sig_new;
             }
 #pragma unroll
-            for (int t = 0; t < VT; ++t) oacc[t] *= f;
-            m_run = m_new;
-        }
-        float pe[8], psum = 0.0f;
-        const float m_ref = MQ ? fmaxf(m_run, -FLT_MAX) : m_run;
+            for (int u = 0; u < NT; ++u) {
+                if (NT > 1 && __builtin_amdgcn_ballot_w64(mloc[u] > m_run[u] + kLazyLog2) == 0)
+                    continue;
+                const float m_new = fmaxf(m_run[u], max_over_groups(mloc[u]));
+                float f = MQ ? fast_exp2(fmaxf(m_run[u], -FLT_MAX) - fmaxf(m_new, -FLT_MAX))
+                             : fast_exp2(m_run[u] - m_new);
+                l_run[u] *= f;
+                if constexpr (kVcb) f *= fsig;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { pe[e] = fast_exp2(z[e] - m_ref); psum += pe[e]; }
-        l_run += psum;
+                for (int t = 0; t < VT; ++t) oacc[u][t] *= f;
+                m_run[u] = m_new;
+            }
+        }
+        float pe[NT][8];
+#pragma unroll
+        for (int u = 0; u < NT; ++u) {
+            float psum = 0.0f;
+            const float m_ref = MQ ? fmaxf(m_run[u], -FLT_MAX) : m_run[u];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { pe[u][e] = fast_exp2(z[u][e] - m_ref); psum += pe[u][e]; }
+            l_run[u] += psum;
+        }
 
         if constexpr (kVcb) {
             // P' = p * vnorm / sigma, rounded once to fp16
             u32x4 pb;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const f16x2 h = {(_Float16)(pe[2 * i] * (vn[2 * i] * inv_sig)),
-                                 (_Float16)(pe[2 * i + 1] * (vn[2 * i + 1] * inv_sig))};
+                const f16x2 h = {(_Float16)(pe[0][2 * i] * (vn[2 * i] * inv_sig)),
+                                 (_Float16)(pe[0][2 * i + 1] * (vn[2 * i + 1] * inv_sig))};
                 pb[i] = __builtin_bit_cast(uint32_t, h);
             }
 #pragma unroll
             for (int t = 0; t < VT; ++t)
-                oacc[t] = mfma_f16(v_operand<FMT, D>(r, t, lds_bytes, vbase), pb, oacc[t]);
+                oacc[0][t] = mfma_f16(v_operand<FMT, D>(r, t, lds_bytes, vbase), pb, oacc[0][t]);
         } else {
-            u32x4 phi, plo;
+            u32x4 phi[NT], plo[NT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t a = __float_as_uint(pe[2 * i]), c = __float_as_uint(pe[2 * i + 1]);
-                const uint32_t ah = a & 0xFFFF0000u, ch = c & 0xFFFF0000u;
-                phi[i] = (a >> 16) | ch;
-                bf16x2 l = {(__bf16)(pe[2 * i] - __uint_as_float(ah)),
-                            (__bf16)(pe[2 * i + 1] - __uint_as_float(ch))};
-                plo[i] = __builtin_bit_cast(uint32_t, l);
-            }
+            for (int u = 0; u < NT; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a = __float_as_uint(pe[u][2 * i]), c = __float_as_uint(pe[u][2 * i + 1]);
+                    const uint32_t ah = a & 0xFFFF0000u, ch = c & 0xFFFF0000u;
+                    phi[u][i] = (a >> 16) | ch;
+                    bf16x2 l = {(__bf16)(pe[u][2 * i] - __uint_as_float(ah)),
+                                (__bf16)(pe[u][2 * i + 1] - __uint_as_float(ch))};
+                    plo[u][i] = __builtin_bit_cast(uint32_t, l);
+                }
+            // (one V operand per tile t serves all NT query tiles)
 #pragma unroll
             for (int t = 0; t < VT; ++t) {
                 const u32x4 vop = v_operand<FMT, D>(r, t, lds_bytes, vbase);
-                oacc[t] = mfma_bf16(vop, phi, oacc[t]);
-                oacc[t] = mfma_bf16(vop, plo, oacc[t]);
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    oacc[u][t] = mfma_bf16(vop, phi[u], oacc[u][t]);
+                    oacc[u][t] = mfma_bf16(vop, plo[u], oacc[u][t]);
+                }
             }
         }
     };
 
     auto compute = [&](Raw& r, int k) {
-        f32x4 sx, sy;
+        f32x4 sx[NT], sy[NT];
         qk(r, sx, sy);
         finish(r, k, sx, sy);
     };
@@ -1039,40 +1099,51 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // no key of the run: m = -inf, l = 0, o = 0.
     if (si.split) {
         if (!live) return;
-        m_true = max_over_groups(m_true);
-        float lt = l_run + __shfl_xor(l_run, 16);
-        lt += __shfl_xor(lt, 32);
         const float osc = kVcb ? oscale * sig_run : oscale;
-        const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
-        const float lx = lt > 0.0f ? lt * fast_exp2(m_run - m_true) : 0.0f;
-        if (qlive) {
-            const size_t slot = row_index(n) * p.P + run_slot;
 #pragma unroll
-            for (int t = 0; t < VT; ++t)
-                *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[t] * sc;
-            if (j == 0) {
-                p.ws_m[slot] = m_true;
-                p.ws_l[slot] = lx;
+        for (int u = 0; u < NT; ++u) {
+            const float mt = max_over_groups(m_true[u]);
+            float lt = l_run[u] + __shfl_xor(l_run[u], 16);
+            lt += __shfl_xor(lt, 32);
+            const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
+            const float lx = lt > 0.0f ? lt * fast_exp2(m_run[u] - mt) : 0.0f;
+            if (tlive[u]) {
+                const size_t slot = row_index(kMaxGroup * u + n) * p.P + run_slot;
+#pragma unroll
+                for (int t = 0; t < VT; ++t)
+                    *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[u][t] * sc;
+                if (j == 0) {
+                    p.ws_m[slot] = mt;
+                    p.ws_l[slot] = lx;
+                }
             }
         }
         return;
     }
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        l_run[u] += __shfl_xor(l_run[u], 16);
+        l_run[u] += __shfl_xor(l_run[u], 32);
+    }
     if constexpr (kVcb) oscale *= sig_run;
 
     // unsplit: merge the waves through LDS, then write the final rows (the codebook formats'
     // merge rows reuse the tables, so every wave must have finished its walk first)
     if constexpr (kVcb) __syncthreads();
-    if (qlive) {
-        if (j == 0) {
-            sm_m[wave][n] = m_run;
-            sm_l[wave][n] = l_run;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        if (tlive[u]) {
+            const int rr = kMaxGroup * u + n;
+            if (j == 0) {
+                sm_m[wave][rr] = m_run[u];
+                sm_l[wave][rr] = l_run[u];
+            }
+#pragma unroll
+            for (int t = 0; t < VT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sm_o[wave][rr * SD + 16 * t + 4 * j + r] = oacc[u][t][r] * oscale;
         }
-#pragma unroll
-        for (int t = 0; t < VT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm_o[wave][n * SD + 16 * t + 4 * j + r] = oacc[t][r] * oscale;
     }
     const bool wg_bad = __syncthreads_or(bad_ids ? 1 : 0) != 0;
     for (int i = tid; i < g * D; i += kThr) {
@@ -1322,16 +1393,23 @@ hipError_t launch_partitions_t(const LaunchParams& p, bool wide, dim3 grid, hipS
     constexpr int PF = prefetch_depth<FMT, false>();
     const dim3 block(64 * waves_per_group(FMT));
     if (p.nq > 1)
-        return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true, false>, grid, block, s, p)
-                                : launch_kernel(partition_kernel<FMT, D, false, PF, true, false>, grid, block, s, p);
+        return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true, false, 1>, grid, block, s, p)
+                                : launch_kernel(partition_kernel<FMT, D, false, PF, true, false, 1>, grid, block, s, p);
     if constexpr (wide_layout_built(FMT, D, false)) {
         constexpr int PFW = prefetch_depth<FMT, true>();
         if (wide)
-            return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PFW, false, true>, grid, block, s, p)
-                                    : launch_kernel(partition_kernel<FMT, D, false, PFW, false, true>, grid, block, s, p);
+            return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PFW, false, true, 1>, grid, block, s, p)
+                                    : launch_kernel(partition_kernel<FMT, D, false, PFW, false, true, 1>, grid, block, s, p);
     }
-    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, false, false>, grid, block, s, p)
-                            : launch_kernel(partition_kernel<FMT, D, false, PF, false, false>, grid, block, s, p);
+    if constexpr (tile_pairs_built(FMT, false, false)) {
+        // two query tiles per wave (the second tile's registers leave BF16 one pair in flight)
+        constexpr int PF2 = FMT == KVD_BF16 ? 1 : 2;
+        if (p.nt == 2)
+            return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF2, false, false, 2>, grid, block, s, p)
+                                    : launch_kernel(partition_kernel<FMT, D, false, PF2, false, false, 2>, grid, block, s, p);
+    }
+    return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, false, false, 1>, grid, block, s, p)
+                            : launch_kernel(partition_kernel<FMT, D, false, PF, false, false, 1>, grid, block, s, p);
 }
 template <int FMT, int D>
 hipError_t launch_reduce_t(const LaunchParams& p, hipStream_t s) {

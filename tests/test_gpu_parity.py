@@ -5,6 +5,7 @@ kernel's arithmetic; max abs error <= 2e-3 and row-normwise relative error <= 1e
 fp32-accumulated attention output.  Spare pages and tail slots are NaN-poisoned in every batch,
 so any read outside the attended range that reaches the arithmetic shows up.
 """
+import dataclasses
 import json
 import os
 
@@ -418,21 +419,53 @@ def test_large_group_alibi_runs(fmt):
                      f"{fmt} g=40 alibi run={run}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo3", "turbo8"])
 @pytest.mark.parametrize("run", [1, 2])
 def test_grouped_tiles_full_blocks_and_tail(fmt, run):
-    """Several query tiles per KV head (g = 24: two tiles) with a grid that holds full blocks of
-    the XCD grouping (8 * m workgroups, m = tiles per KV head, twice that for the codebook
-    formats) and a ragged tail that keeps the identity order.  Every unit must be computed once."""
-    inp = _small(fmt, num_q_heads=48, num_kv_heads=2, context=None, ctx_range=(1, 6000),
+    """Two work units per KV head with a grid that holds full blocks of the XCD grouping (8 * m
+    workgroups, m = units per KV head) and a ragged tail that keeps the identity order.  Every
+    unit must be computed once.  A unit is one 16-row query tile, or two for single-query BF16 /
+    FP8: there g = 40 makes three tiles, i.e. a unit of two tiles and one of a single live tile."""
+    pairs = fmt in ("bf16", "fp8")
+    g = 40 if pairs else 24
+    inp = _small(fmt, num_q_heads=2 * g, num_kv_heads=2, context=None, ctx_range=(1, 6000),
                  num_seqs=5, seed=11)
-    # workgroup count of the partition launch: ceil(runs / waves) x KV heads x tiles x sequences,
+    # workgroup count of the partition launch: ceil(runs / waves) x KV heads x units x sequences,
     # runs = ceil(partitions / run) (waves per workgroup: 4 BF16 / FP8, 8 codebook formats)
-    waves = 8 if fmt.startswith("turbo") else 4
+    waves = 4 if pairs else 8
     ps = 256
     n_part = -(-6000 // ps)
-    grid = -(-(-(-n_part // run)) // waves) * 2 * 2 * 5
-    m = 2 * (2 if fmt.startswith("turbo") else 1)
+    m = 2
+    grid = -(-(-(-n_part // run)) // waves) * 2 * m * 5
     assert grid >= 8 * m and grid % (8 * m) != 0, grid
     got = GpuBatch(inp, partition_size=ps, partitions_per_wave=run).run()
-    assert_close(got, _oracle(inp), f"{fmt} g=24 run={run} grid={grid}")
+    assert_close(got, _oracle(inp), f"{fmt} g={g} run={run} grid={grid}")
+
+
+def _group_subset(inp, heads):
+    """The batch with only the query heads `heads` (indices within each KV head's group): q rows
+    picked, caches, lengths and windows shared.  Returns it and the picked global head indices."""
+    s = inp.spec
+    cols = [hk * s.group + h for hk in range(s.num_kv_heads) for h in heads]
+    spec = dataclasses.replace(s, num_q_heads=len(cols))
+    return dataclasses.replace(inp, spec=spec, q=np.ascontiguousarray(inp.q[:, cols])), cols
+
+
+@pytest.mark.parametrize("ps,run", [(256, 2), (512, 1), (-1, 0)])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_tile_pairs_bit_identical_to_single_tiles(fmt, D, ps, run):
+    """Single-query BF16 / FP8 compute two 16-row query tiles per wave when a KV head has more
+    than 16 query heads.  The tiles share each page's loads and dequantisation and nothing else,
+    so every row must be bit-identical to a launch in which its tile is the whole query group
+    (one tile per wave), for split and unsplit rows, with and without ALiBi."""
+    inp = _small(fmt, head_dim=D, num_q_heads=48, num_kv_heads=2, context=None,
+                 ctx_range=(1, 4000), num_seqs=3, seed=5, softcap=30.0 if D == 64 else 0.0)
+    slopes = _slopes(48)
+    for sl in (None, slopes):
+        full = GpuBatch(inp, partition_size=ps, partitions_per_wave=run, alibi=sl).run()
+        for heads in (range(0, 16), range(16, 24)):
+            sub, cols = _group_subset(inp, heads)
+            part = GpuBatch(sub, partition_size=ps, partitions_per_wave=run,
+                            alibi=None if sl is None else sl[cols]).run()
+            assert np.array_equal(full[:, cols], part, equal_nan=True), (fmt, D, ps, list(heads))
