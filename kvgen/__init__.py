@@ -114,6 +114,7 @@ SPECS: dict[str, Spec] = {
     "mqa-fp8": Spec("fp8-e4m3-L32768-mqa64", 16, 64, 1, 128, "fp8", context=32768),
     "mqa-bf16": Spec("bf16-L32768-mqa64", 16, 64, 1, 128, "bf16", context=32768),
     "mqa-t4": Spec("turbo4-L32768-mqa64", 8, 64, 1, 128, "turbo4", context=32768),
+    "mqa-t8": Spec("turbo8-L32768-mqa64", 8, 64, 1, 128, "turbo8", context=32768),
 }
 
 
