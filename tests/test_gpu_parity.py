@@ -433,7 +433,7 @@ def test_grouped_tiles_full_blocks_and_tail(fmt, run):
     # workgroup count of the partition launch: ceil(runs / waves) x KV heads x units x sequences,
     # runs = ceil(partitions / run) (waves per workgroup: 4 BF16 / FP8, 8 codebook formats)
     waves = 4 if pairs else 8
-    ps = 256
+    ps = 320
     n_part = -(-6000 // ps)
     m = 2
     grid = -(-(-(-n_part // run)) // waves) * 2 * m * 5
