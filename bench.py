@@ -67,7 +67,7 @@ def parse():
                     help="other 32K workloads timed after the headline one, in the same run "
                          "(comma separated; empty = none)")
     ap.add_argument("--format-steps", type=int, default=30,
-                    help="timed steps of each workload in --formats (warm-up: the same count)")
+                    help="timed steps of each workload in --formats (warm-up: --warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -406,7 +406,7 @@ def main():
     # the other formats' 32K workloads, timed in the same run (fewer steps)
     others = {}
     for name in [w for w in args.formats.split(",") if w and w != args.workload]:
-        o = time_workload(name, args.format_steps, args.format_steps, flush=not args.no_flush)
+        o = time_workload(name, args.format_steps, args.warmup, flush=not args.no_flush)
         oc, op = float(o["t_call"].mean()), float(o["t_part"].mean())
         others[name] = {"workload": o["spec"].name, "dtype": DTYPES[o["spec"].fmt],
                         "kv_bytes_per_step": o["kv_bytes"], "steps": args.format_steps,
