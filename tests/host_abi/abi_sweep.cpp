@@ -160,6 +160,9 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     const int64_t nq = d.queries_per_seq > 1 ? d.queries_per_seq : 1;
     const int64_t g = d.num_q_heads / d.num_kv_heads;
     const int64_t qt = (nq * g + 15) / 16;
+    // single-query BF16 / FP8 with several tiles: two tiles per work unit
+    const int64_t nt = (qt >= 2 && nq == 1 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3)) ? 2 : 1;
+    const int64_t units = (qt + nt - 1) / nt;
     if (d.num_seqs == 0) {
         CHECK(r.calls[stub::kPartitions] == 0 && r.calls[stub::kReduce] == 0);
         return;
@@ -169,7 +172,7 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     if (!r.calls[stub::kPartitions] && !r.calls[stub::kReduce]) return;
     CHECK(r.fmt == fmt);
     CHECK(p.B == d.num_seqs && p.Hq == d.num_q_heads && p.Hkv == d.num_kv_heads);
-    CHECK(p.g == g && p.nq == nq && p.qt == qt && p.D == d.head_dim);
+    CHECK(p.g == g && p.nq == nq && p.qt == qt && p.nt == nt && p.qg == units && p.D == d.head_dim);
     CHECK(p.k_chunk == k_chunk(fmt, d.head_dim) && p.v_chunk == v_chunk(fmt, d.head_dim));
     CHECK(p.kbits == (fmt == KVD_TURBO3 ? 3 : 4));
     CHECK(p.max_ctx == d.max_context_len && p.max_blocks == d.max_blocks_per_seq);
@@ -199,9 +202,9 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     if (r.calls[stub::kPartitions]) {
         const int64_t runs = p.P > 0 ? ((int64_t)p.P * p.part_size + p.run_tokens - 1) / p.run_tokens : 0;
         const int64_t px = p.P > 0 ? (runs + waves - 1) / waves : 1;
-        CHECK((int64_t)r.grid.x == px * d.num_kv_heads * qt * d.num_seqs);
+        CHECK((int64_t)r.grid.x == px * d.num_kv_heads * units * d.num_seqs);
         CHECK(r.grid.x >= 1 && r.grid.x <= 0x7FFFFFFFu && r.grid.y == 1 && r.grid.z == 1);
-        CHECK(!r.wide || (fmt == KVD_BF16 && d.head_dim == 128 && nq == 1));
+        CHECK(!r.wide || (fmt == KVD_BF16 && d.head_dim == 128 && nq == 1 && nt == 1));
     }
 }
 
