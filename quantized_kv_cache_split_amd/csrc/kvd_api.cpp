@@ -87,8 +87,11 @@ int device_cus() {
 // the wide layout is built (one workgroup per CU) it is taken if runs of at most kMaxRunWide
 // partitions cover the chip in one round; otherwise runs are capped at kMaxRun partitions
 // (ragged batches, whose real work is smaller, do better with short runs).  Runs other than
-// one partition need partition boundaries on even pages (partition size a multiple of 32).  An
-// explicit partitions_per_wave R gives runs of R partitions in the two-workgroup layout.
+// one partition need partition boundaries on even pages (partition size a multiple of 32).  A
+// wave that computes two query tiles counts as two slots' work, so its runs are twice as long
+// (FP8 / BF16 16 x 32K with 64 query heads on one KV head, runs of 1 / 2 partitions: 52.4 /
+// 49.6 and 74.1 / 65.9 us per call).  An explicit partitions_per_wave R gives runs of R
+// partitions in the two-workgroup layout.
 struct RunChoice {
     int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
     bool wide;
@@ -107,7 +110,7 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         const int64_t pairs = (len + pair_tokens - 1) / pair_tokens;
         const int64_t units = (int64_t)d->num_kv_heads * units_per_head(d, fmt) * d->num_seqs;
         auto run_for = [&](bool w) -> int64_t {
-            int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w);
+            int64_t slots = (int64_t)device_cus() * kvd::waves_per_cu(w) / tiles_per_unit(d, fmt);
             if (ragged) slots = slots * 5 / 2;                        // 2.5 rounds of work
             const int64_t rp = (pairs * units + slots - 1) / slots;   // pairs per wave
             return rp * pair_tokens < ps ? ps : rp * pair_tokens;
