@@ -116,8 +116,9 @@ typedef enum kvd_status {
 
 /* Shapes.  Supported: block_size == 16; head_dim 64 or 128 for BF16/FP8, 128 for the Turbo
  * formats; num_q_heads a multiple of num_kv_heads.  A query group larger than 16 (MQA-like
- * shapes) is processed in tiles of 16 query heads, each tile reading its KV head's pages
- * again.  Size limits (KVD_ERR_SHAPE beyond them): num_seqs, num_kv_heads <= 65535;
+ * shapes) is processed in tiles of 16 query heads; single-query BF16 / FP8 compute two tiles
+ * per wavefront, which share its page loads, and other cases read a KV head's pages once per
+ * tile.  Size limits (KVD_ERR_SHAPE beyond them): num_seqs, num_kv_heads <= 65535;
  * num_seqs * n_q * num_q_heads < 2^31 query rows; the workspace of a split (its m, l and
  * outputs for every row and partition) below 2^62 bytes. */
 typedef struct kvd_dims {
@@ -139,9 +140,11 @@ typedef struct kvd_dims {
                                     0: auto -- the page pairs of a batch of max_context_len
                                     sequences split evenly over the device's resident
                                     wavefronts (whole 32-token pairs, at least one partition,
-                                    at most 4 partitions; single-query BF16 at head_dim 128
-                                    uses a layout with one workgroup per CU and runs of up to 8
-                                    partitions when that covers the device in one round);
+                                    at most 4 partitions; a wavefront computing two query
+                                    tiles counts twice; single-query BF16 at head_dim 128
+                                    with at most 16 query heads per KV head uses a layout with
+                                    one workgroup per CU and runs of up to 8 partitions when
+                                    that covers the device in one round);
                                     > 0: runs of that many partitions.  Capped at the
                                     partitions of max_context_len; runs are one partition when
                                     the partition size is not a multiple of 32.  >= 0. */
