@@ -316,8 +316,14 @@ def test_partials_match_oracle(fmt, run):
                 assert_close(o[b, rows, p].astype(np.float64), po, f"{fmt} partial b{b} h{hk} p{p}")
 
 
-def test_zero_length_and_bad_rows():
-    inp = _small("bf16", num_seqs=4, context=None, ctx_range=(50, 2000))
+@pytest.mark.parametrize("fmt,hq", [("bf16", 8), ("bf16", 48), ("fp8", 48), ("turbo4", 48)])
+def test_zero_length_and_bad_rows(fmt, hq):
+    """Zero-length rows are 0; a block-table entry outside the pool makes every row of its
+    sequence NaN (split and unsplit, one- and two-tile units: 48 query heads on 2 KV heads are
+    two 16-row tiles per KV head); the healthy sequence next to them is unaffected."""
+    # lengths 3321, 3142 (zeroed), 1457 (split), 580 (unsplit)
+    inp = _small(fmt, num_q_heads=hq, num_seqs=4, context=None, ctx_range=(50, 4000), seed=3)
+    assert list(inp.context_lens) == [3321, 3142, 1457, 580]
     inp.context_lens[1] = 0
     inp.block_table[2, 1] = inp.num_pool_blocks + 5        # out of the pool
     inp.block_table[3, 0] = -1
@@ -326,7 +332,7 @@ def test_zero_length_and_bad_rows():
     assert (gpu[1] == 0).all()
     assert np.isnan(gpu[2]).all() and np.isnan(gpu[3]).all()
     ref = oracle.decode_attention(*oracle_args(inp), seqs=[0])     # the healthy sequence only
-    assert_close(gpu[0:1], ref[0:1], "bf16 row next to error rows")
+    assert_close(gpu[0:1], ref[0:1], f"{fmt} hq={hq} row next to error rows")
 
 
 def test_context_above_bound_gives_nan():
