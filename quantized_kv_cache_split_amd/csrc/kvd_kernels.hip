@@ -574,7 +574,12 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         }
     }
     const int nvh = p.Hkv * p.qg;
-    const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = wg / (nvh * p.B);
+    // Run blocks are dispatched last block first: only long sequences have work in the high
+    // blocks, so in a ragged batch their runs start at once and the short sequences' runs (and
+    // the empty high blocks of short sequences, which exit at once) fill in behind them, as a
+    // longest-first schedule would; in a uniform batch the order changes nothing.
+    const int nxb = (int)gridDim.x / (nvh * p.B);
+    const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = nxb - 1 - wg / (nvh * p.B);
     const int hk = vh / p.qg, unit = vh - hk * p.qg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
