@@ -15,7 +15,10 @@ Prints ONE JSON line.  `value` = algorithmic KV bytes per call / mean call time.
 `roofline` = the partition kernel's algorithmic bytes / its mean duration against 8 TB/s.
 `cpu_baseline` = the fp64 oracle timed on this host's cores over a bounded sample.
 `other_formats` = the other formats' 32K workloads (BF16, Turbo4, Turbo3 by default), timed the
-same way in the same run with fewer steps.  `dtype` names the operand precision of the
+same way in the same run with fewer steps.  Their warm-up runs at least the W warm-up steps and
+at least `--settle-s` seconds of calls: measured from an idle GPU (as after the seconds of
+input generation), Turbo3 32K calls took 70 us for the first few steps, 80 us over the next
+thirty and 66 us from about the hundredth on, while FP8 32K calls were flat from the first.  `dtype` names the operand precision of the
 headline format's matrix products (accumulation is fp32 everywhere).
 
 `--read-probe` instead measures the HBM read ceiling (kvd_read_probe): a plain read stream and
@@ -66,6 +69,8 @@ def parse():
     ap.add_argument("--formats", default="m-bf16,m-t4,m-t3",
                     help="other 32K workloads timed after the headline one, in the same run "
                          "(comma separated; empty = none)")
+    ap.add_argument("--settle-s", type=float, default=0.1,
+                    help="least warm-up time (s) of each workload in --formats")
     ap.add_argument("--format-steps", type=int, default=30,
                     help="timed steps of each workload in --formats (warm-up: --warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -272,8 +277,10 @@ DTYPES = {
 }
 
 
-def time_workload(name, steps, warmup, partition_size=None, partitions_per_wave=0, flush=True):
-    """Generate workload `name` and time full calls and partition launches on cuda:0.
+def time_workload(name, steps, warmup, partition_size=None, partitions_per_wave=0, flush=True,
+                  settle_s=0.0):
+    """Generate workload `name` and time full calls and partition launches on cuda:0, after
+    `warmup` untimed steps (continued until `settle_s` seconds of them have run).
     Returns a dict of the measurements (seconds arrays and sizes)."""
     import torch
 
@@ -326,15 +333,19 @@ def time_workload(name, steps, warmup, partition_size=None, partitions_per_wave=
         w = time.perf_counter() - w
         return np.array([e[0].elapsed_time(e[1]) for e in events]) * 1e-3, w   # seconds
 
-    for _ in range(warmup):
+    n_warm, w0 = 0, time.perf_counter()
+    while n_warm < warmup or time.perf_counter() - w0 < settle_s:
         evict()
         step()
+        n_warm += 1
+        if settle_s and n_warm % 16 == 0:
+            torch.cuda.synchronize()   # the host stays within 16 steps of the GPU
     torch.cuda.synchronize()
     t_call, wall = timed(step)
     assert np.isfinite(out.cpu().numpy()).all(), "non-finite output"
     t_part, _ = timed(partition_step)
     res = dict(spec=spec, inp=inp, ps=ps, t_call=t_call, t_part=t_part, wall=wall, t_gen=t_gen,
-               kv_bytes=inp.kv_bytes())
+               kv_bytes=inp.kv_bytes(), warmup_steps=n_warm)
     del t, out, ws, fl
     torch.cuda.empty_cache()
     return res
@@ -406,10 +417,12 @@ def main():
     # the other formats' 32K workloads, timed in the same run (fewer steps)
     others = {}
     for name in [w for w in args.formats.split(",") if w and w != args.workload]:
-        o = time_workload(name, args.format_steps, args.warmup, flush=not args.no_flush)
+        o = time_workload(name, args.format_steps, args.warmup, flush=not args.no_flush,
+                          settle_s=args.settle_s)
         oc, op = float(o["t_call"].mean()), float(o["t_part"].mean())
         others[name] = {"workload": o["spec"].name, "dtype": DTYPES[o["spec"].fmt],
                         "kv_bytes_per_step": o["kv_bytes"], "steps": args.format_steps,
+                        "warmup_steps": o["warmup_steps"],
                         "call_ms": round(oc * 1e3, 4), "partition_kernel_ms": round(op * 1e3, 4),
                         "gbps": round(o["kv_bytes"] / oc / 1e9, 2),
                         "frac_of_hbm_peak": round(o["kv_bytes"] / oc / 1e9 / HBM_PEAK_GBS, 4),

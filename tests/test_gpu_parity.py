@@ -231,6 +231,20 @@ def test_partitions_per_wave_agree(fmt):
             assert np.abs(outs[ps, run] - outs[ps, 1]).max() <= MODE_AGREE[fmt], (ps, run)
 
 
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_reduce_block_boundaries(fmt):
+    """The reduce merges a row's triples in blocks of 16 (rows of at most 32 triples) or 64:
+    32-token partitions, one per run, give rows of n = 15 ... 129 triples around every block
+    edge."""
+    ns = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 129]
+    lengths = [n * 32 - 7 for n in ns]
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=len(ns), num_q_heads=8,
+                                       num_kv_heads=2, softcap=0.0),
+                            lengths=lengths, windows=[0] * len(ns))
+    out = GpuBatch(inp, partition_size=32, partitions_per_wave=1).run()
+    assert_close(out, _oracle(inp), f"{fmt} reduce blocks")
+
+
 # --------------------------------------------------------------------------------------------
 # structure: permutation invariance, poison, identities, partials, error rows
 # --------------------------------------------------------------------------------------------
