@@ -135,8 +135,9 @@ typedef struct kvd_dims {
                                     > 0: always split at that many tokens (a multiple of 16);
                                     -1: never split */
     int32_t partitions_per_wave; /* launch tuning: the run one wavefront walks through a split
-                                    sequence; it writes one triple for the run (results agree
-                                    to rounding: the online softmax groups its sums by run).
+                                    sequence; a workgroup's runs give one triple (results
+                                    agree to rounding: the online softmax groups its sums by
+                                    run and workgroup).
                                     0: auto -- the page pairs of a batch of max_context_len
                                     sequences split evenly over the device's resident
                                     wavefronts (whole 32-token pairs, at least one partition,
@@ -164,7 +165,7 @@ typedef struct kvd_dims {
 } kvd_dims;
 
 /* Bytes of device workspace kvd_decode_attn_paged needs: slots for per-partition fp32 triples
- * (the runs of a sequence write consecutive slots from its first partition's)
+ * (the workgroups of a sequence write consecutive slots from its first partition's)
  * m [B][n_q][Hq][P], l [B][n_q][Hq][P] and o [B][n_q][Hq][P][D], P = ceil(max_context_len /
  * partition size), each array starting on a 256-byte boundary.  Returns 0 for invalid dims. */
 size_t kvd_workspace_bytes(const kvd_dims* dims);
@@ -226,16 +227,17 @@ int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const voi
 
 /* Phase 1 alone (same arguments).  Wavefronts per (KV head, sequence) walk runs of T tokens
  * (partitions_per_wave > 0: T = that many partitions; 0: the automatic choice, a whole number
- * of 32-token page pairs of at least one partition), four wavefronts per workgroup (twelve for
- * Turbo4 / Turbo3, eight for Turbo8).  For a split sequence with attended range [lo, L), let p0
- * be the first partition the range touches (P tokens per partition); run k covers tokens
- * [p0*P + k*T, p0*P + (k+1)*T) intersected with [lo, L), and its one triple goes to the
- * workspace at (b, i, h, p0 + k):
+ * of 32-token page pairs of at least one partition), W = 4 wavefronts per workgroup (8 for
+ * the Turbo formats).  For a split sequence with attended range [lo, L), let p0 be the first
+ * partition the range touches (P tokens per partition); run k covers tokens
+ * [p0*P + k*T, p0*P + (k+1)*T) intersected with [lo, L), and workgroup x walks runs
+ * W*x .. W*x + W - 1.  Their keys j together give one triple at workspace slot
+ * (b, i, h, p0 + x):
  * m = max_j z_j * log2(e)  (base-2 units),  l = sum_j exp(z_j - max z),
  * o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the rotated domain for the Turbo
- * formats; the keys j are those of the run that query i sees, and a query that sees none of
- * them gets m = -inf, l = 0, o = 0.  Other slots are not written.  Sequences that are not split
- * get their final output row written here. */
+ * formats; the keys j are those of the workgroup's runs that query i sees, and a query that
+ * sees none of them gets m = -inf, l = 0, o = 0.  Other slots are not written.  Sequences that
+ * are not split get their final output row written here. */
 int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cache,
                           const void* v_cache, const int32_t* block_table,
                           const int32_t* context_lens, int fmt, const float* scales,
@@ -245,7 +247,7 @@ int kvd_decode_partitions(const kvd_dims* dims, const void* q, const void* k_cac
                           size_t workspace_bytes, void* stream);
 
 /* Phase 2 alone (same arguments, so the same run length R; reads the workspace phase 1
- * filled).  For each split (b, h), over its runs k: M = max_k m_k, w_k = l_k 2^(m_k - M),
+ * filled).  For each split (b, h), over its triples k: M = max_k m_k, w_k = l_k 2^(m_k - M),
  * out = sum_k w_k o_k / sum_k w_k, then (Turbo)
  * out <- diag(s) H out / sqrt(D).  Rows of sequences that are not split are left untouched. */
 int kvd_reduce_partitions(const kvd_dims* dims, const void* q, const void* k_cache,

@@ -496,13 +496,13 @@ __device__ __forceinline__ LaneMap lane_map(int lane) {
 // ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-// Grid ceil(runs / W) * Hkv * B (1-D), W waves per workgroup.  For a split sequence wave w of
-// workgroup x owns run W x + w (split_runs: p.run_tokens consecutive tokens from the first
-// attended partition's start, at least one partition), streams through it without draining
-// its load pipeline, and writes one triple for the whole run (the online softmax merges as it
-// goes) to slot plo + W x + w; the reduce merges the runs.  For an unsplit
-// sequence (workgroup 0 only) the four waves share the attended range (consecutive quarters of
-// its page pairs) and merge through LDS.  Page pairs start at even page indices, so when the
+// Grid ceil(runs / W) * Hkv * units * B (1-D), W waves per workgroup.  For a split sequence
+// wave w of workgroup x owns run W x + w (split_runs: p.run_tokens consecutive tokens from the
+// first attended partition's start, at least one partition) and streams through it without
+// draining its load pipeline (the online softmax merges as it goes); the workgroup merges its
+// W runs' triples through LDS into one, at slot plo + x, and the reduce merges the
+// workgroups'.  For an unsplit sequence (workgroup 0 only) the waves share the attended range
+// (consecutive parts of its page pairs) and merge through LDS into the final rows.  Page pairs start at even page indices, so when the
 // partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
 // partitions.
 template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE, int NT>
@@ -633,7 +633,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
         const int nruns = split_runs(p, si, plo, base);
         if (xb * kW >= nruns) return;
         const int i = xb * kW + wave;
-        run_slot = plo + i;
+        run_slot = plo + xb;
         lo = max(si.lo, base + i * p.run_tokens);
         hi = min(si.L, base + (i + 1) * p.run_tokens);
         part_end = min(hi, (lo / p.part_size + 1) * p.part_size);
@@ -1098,29 +1098,55 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     }
 
     // ---- results ---------------------------------------------------------------------------
-    // Split sequences: the run's triple, merged over its partitions, goes to the slot of its
-    // first partition: m = the exact max logit in base-2 units, l = the sum taken relative to
-    // it, o = O / l in output units (no reference choice affects them).  A query row that saw
-    // no key of the run: m = -inf, l = 0, o = 0.
+    // Split sequences: each wave's run gives a triple per query row -- m = the exact max logit
+    // in base-2 units, l = the sum taken relative to it, o = O / l in output units (no
+    // reference choice affects them; a row that saw no key of the run: m = -inf, l = 0, o = 0;
+    // a wave with no run gives that too).  The workgroup's waves stage them in LDS and merge
+    // them with the LSE rule into one triple for the workgroup's kW consecutive runs, written
+    // to its slot plo + xb: a quarter (an eighth for the codebook formats) of the workspace
+    // traffic of one triple per run, and of the reduce's reads.
     if (si.split) {
-        if (!live) return;
         const float osc = kVcb ? oscale * sig_run : oscale;
+        if constexpr (kVcb) __syncthreads();   // the staging rows reuse the tables
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
             const float mt = max_over_groups(m_true[u]);
             float lt = l_run[u] + __shfl_xor(l_run[u], 16);
             lt += __shfl_xor(lt, 32);
-            const float sc = bad_ids ? __builtin_nanf("") : (lt > 0.0f ? osc / lt : 0.0f);
+            const float sc = lt > 0.0f ? osc / lt : 0.0f;
             const float lx = lt > 0.0f ? lt * fast_exp2(m_run[u] - mt) : 0.0f;
             if (tlive[u]) {
-                const size_t slot = row_index(kMaxGroup * u + n) * p.P + run_slot;
+                const int rr = kMaxGroup * u + n;
+                if (j == 0) {
+                    sm_m[wave][rr] = mt;
+                    sm_l[wave][rr] = lx;
+                }
 #pragma unroll
                 for (int t = 0; t < VT; ++t)
-                    *reinterpret_cast<f32x4*>(p.ws_o + slot * D + 16 * t + 4 * j) = oacc[u][t] * sc;
-                if (j == 0) {
-                    p.ws_m[slot] = mt;
-                    p.ws_l[slot] = lx;
-                }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sm_o[wave][rr * SD + 16 * t + 4 * j + r] = oacc[u][t][r] * sc;
+            }
+        }
+        const bool wg_bad = __syncthreads_or(bad_ids ? 1 : 0) != 0;
+        for (int i = tid; i < g * D; i += kThr) {
+            const int r = i / D, d = i % D;
+            float M = sm_m[0][r];
+#pragma unroll
+            for (int w = 1; w < kW; ++w) M = fmaxf(M, sm_m[w][r]);
+            float wsum = 0.0f, acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kW; ++w) {   // l > 0 implies a finite m, so M is finite too
+                const float lw = sm_l[w][r];
+                const float sc = lw > 0.0f ? lw * fast_exp2(sm_m[w][r] - M) : 0.0f;
+                wsum += sc;
+                acc += sm_o[w][r * SD + d] * sc;
+            }
+            const size_t slot = row_index(r) * p.P + run_slot;
+            p.ws_o[slot * D + d] = wg_bad ? __builtin_nanf("") : (wsum > 0.0f ? acc / wsum : 0.0f);
+            if (d == 0) {
+                p.ws_m[slot] = M;
+                p.ws_l[slot] = wsum;
             }
         }
         return;
@@ -1181,14 +1207,14 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 // phase 2: log-sum-exp merge of the partition triples
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence x query of the chunk); lane l owns output elements
-// E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per run, at slots
-// plo .. plo + runs - 1 (split_runs).  Triples are taken KB at a time (KB = 16 when a row has
+// E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per workgroup of kW
+// runs, at slots plo .. plo + ceil(runs / kW) - 1 (split_runs).  Triples are taken KB at a time (KB = 16 when a row has
 // at most 32 of them, else 64): lane i < KB takes the (m, l) of triple base + i and every lane
 // loads its slice of all KB outputs, so a block costs one memory round trip.  The block's
 // weights are computed lane-parallel and broadcast with v_readlane; blocks after the first
-// rescale the running sums to the new maximum (online LSE).  The short block keeps a typical
-// row (16 or 32 triples) from issuing loads of clamped duplicate slots: C4 call 193.8 ->
-// 192.3 us, FP8 MQA 49.6 -> 48.6 us.
+// rescale the running sums to the new maximum (online LSE).  The short block spares a typical
+// row (4 to 16 triples) the loads of 48 or more clamped duplicate slots (with one triple per
+// run, 16 per row: C4 call 193.8 -> 192.3 us).
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     constexpr bool kVcb = v_codebook<FMT>();   // partial outputs are in the rotated domain
@@ -1196,8 +1222,9 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     const int hq = blockIdx.x, bi = blockIdx.y, b = bi / p.nq, lane = threadIdx.x;
     const SeqInfo si = seq_info<true>(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
+    constexpr int kW = waves_per_group(FMT);      // runs per workgroup, merged into one triple
     int p0, base0;
-    const int n = split_runs(p, si, p0, base0);   // runs (triples) of the sequence
+    const int n = (split_runs(p, si, p0, base0) + kW - 1) / kW;   // triples of the sequence
     const size_t row = (size_t)bi * p.Hq + hq;    // out / workspace row (b, query, head)
     const float* ms = p.ws_m + row * p.P + p0;
     const float* ls = p.ws_l + row * p.P + p0;

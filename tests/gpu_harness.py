@@ -128,13 +128,20 @@ def assert_close(gpu, ref, what=""):
     return ea, er
 
 
+def runs_per_triple(fmt):
+    """Runs whose triples the partition kernel merges into one workspace triple: the waves of
+    one workgroup (4 for BF16 / FP8, 8 for the codebook formats)."""
+    return 8 if fmt in ("turbo4", "turbo3", "turbo8") else 4
+
+
 def merge_runs(parts, part_size, run):
     """Group an oracle's per-partition triples [(lo, hi, m, l, o), ...] (in order, natural-log
-    m) into the runs of ``run`` consecutive partitions the partition kernel merges (runs start
-    at the first partition of the range), merging each run with the LSE rule:
+    m) into groups of ``run`` consecutive partitions the partition kernel merges into one
+    workspace triple (a workgroup's runs: partitions per run x runs_per_triple; groups start
+    at the first partition of the range), merging each group with the LSE rule:
     M = max m_i, l = sum l_i e^(m_i - M), o = sum l_i e^(m_i - M) o_i / l.  Rows with no key in a
-    run keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)]: run k of a range whose
-    first partition is p0 sits in workspace slot p0 + k."""
+    group keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)]: group k of a range
+    whose first partition is p0 sits in workspace slot p0 + k."""
     if not parts:
         return []
     p0 = parts[0][0] // part_size

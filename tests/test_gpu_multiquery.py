@@ -8,7 +8,7 @@ import pytest
 import kvgen
 import oracle
 from conftest import oracle_args
-from gpu_harness import GpuBatch, assert_close
+from gpu_harness import GpuBatch, assert_close, merge_runs, runs_per_triple
 
 pytestmark = pytest.mark.gpu
 
@@ -87,13 +87,19 @@ def test_multi_query_runs_agree(fmt):
 
 @pytest.mark.parametrize("fmt", ["bf16", "turbo4"])
 def test_multi_query_partials(fmt):
-    """Partition triples per (query, head) row, including rows that see no key of a partition
-    (a small window against 32-token partitions): m = -inf, l = 0, o = 0 there."""
-    # lengths 32k + 3 and 32k + 4: the last partition holds only the chunk's last 3 / 4 tokens,
-    # which its first queries do not see; window 40 also empties the first partition for some
+    """Workspace triples per (query, head) row, including rows that see no key of a triple:
+    m = -inf, l = 0, o = 0 there."""
+    # lengths 32k + 3 and 32k + 4: the last 32-token partition holds only the chunk's last 3 / 4
+    # tokens, which its first queries do not see.  One-partition runs, and a workgroup of W
+    # runs gives one triple, so the window makes the attended range W + 1 partitions long: the
+    # last triple then holds that last partition alone.
+    W = runs_per_triple(fmt)
+    win = {4: 100, 8: 230}[W]
     inp = kvgen.make_inputs(kvgen.spec("c1", fmt=fmt, head_dim=128, num_q_heads=8, num_kv_heads=2,
                                        pool_total=None, queries_per_seq=8, num_seqs=2),
-                            lengths=[355, 612], windows=[40, 40])
+                            lengths=[355, 612], windows=[win, win])
+    for L in (355, 612):   # first attended partition .. last: W + 1 of them
+        assert (L - 1) // 32 - (L - 8 + 1 - win) // 32 == W
     gb = GpuBatch(inp, partition_size=32, partitions_per_wave=1)
     gb.run_phase1()
     m, l, o = gb.partials()          # [B, n_q, Hq, P]
@@ -102,9 +108,9 @@ def test_multi_query_partials(fmt):
     empty = 0
     for b in range(s.num_seqs):
         for hk in range(s.num_kv_heads):
-            for lo_, hi_, pm, pl, po in oracle.multi_query_partials(*oracle_args(inp), 32, b, hk,
-                                                                    rotated=True):
-                p = lo_ // 32
+            parts = merge_runs(oracle.multi_query_partials(*oracle_args(inp), 32, b, hk,
+                                                           rotated=True), 32, runs_per_triple(fmt))
+            for p, lo_, hi_, pm, pl, po in parts:
                 gm = m[b, :, hk * g:(hk + 1) * g, p].reshape(-1).astype(np.float64)
                 gl = l[b, :, hk * g:(hk + 1) * g, p].reshape(-1).astype(np.float64)
                 go = o[b, :, hk * g:(hk + 1) * g, p].reshape(-1, s.head_dim).astype(np.float64)

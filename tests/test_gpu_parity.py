@@ -15,7 +15,7 @@ import pytest
 import kvgen
 import oracle
 from conftest import oracle_args
-from gpu_harness import GpuBatch, assert_close, merge_runs
+from gpu_harness import GpuBatch, assert_close, merge_runs, runs_per_triple
 
 pytestmark = pytest.mark.gpu
 
@@ -308,9 +308,10 @@ def test_partials_match_oracle(fmt, run):
     s = inp.spec
     for b in range(s.num_seqs):
         for hk in range(s.num_kv_heads):
-            # one triple per run of `run` partitions, at the slot of its first partition
+            # one triple per workgroup of runs of `run` partitions, at slot p0 + workgroup
             parts = merge_runs(oracle.partition_partials(*oracle_args(inp), 128, b, hk,
-                                                         rotated=True), 128, run)
+                                                         rotated=True), 128,
+                               run * runs_per_triple(fmt))
             for p, lo_, hi_, pm, pl, po in parts:
                 rows = slice(hk * s.group, hk * s.group + s.group)
                 m_nat = m[b, rows, p].astype(np.float64) * np.log(2.0)
@@ -410,9 +411,10 @@ def test_alibi_partials_match_oracle(fmt):
     s = inp.spec
     for b in range(s.num_seqs):
         for hk in range(s.num_kv_heads):
-            for lo_, hi_, pm, pl, po in oracle.partition_partials(*oracle_args(inp), 128, b, hk,
-                                                                  rotated=True, alibi=sl):
-                p = lo_ // 128
+            parts = merge_runs(oracle.partition_partials(*oracle_args(inp), 128, b, hk,
+                                                         rotated=True, alibi=sl), 128,
+                               runs_per_triple(fmt))
+            for p, lo_, hi_, pm, pl, po in parts:
                 rows = slice(hk * s.group, hk * s.group + s.group)
                 lse = m[b, rows, p].astype(np.float64) * np.log(2.0) + np.log(l[b, rows, p].astype(np.float64))
                 assert np.abs(lse - (pm + np.log(pl))).max() < 5e-3
