@@ -92,13 +92,34 @@ int device_cus() {
 // (FP8 / BF16 16 x 32K with 64 query heads on one KV head, runs of 1 / 2 partitions: 52.4 /
 // 49.6 and 74.1 / 65.9 us per call).  An explicit partitions_per_wave R gives runs of R
 // partitions in the two-workgroup layout.
+//
+// XCD skew.  In the BF16 / FP8 walks over random pages the odd XCDs of MI355X read more slowly
+// than the even ones (wave timelines of FP8 16 x 32K: even XCDs end their walks after 166-170
+// us, odd ones after 179-180 us, whichever KV heads they read; BF16 16 x 32K: 312-324 against
+// 346-353 us).  When the automatic choice covers the chip in one round with a single query
+// tile per KV head, runs of even run blocks (which the grid order puts on the even XCDs) are
+// made kRunSkewPermille / 1000 longer and those of odd blocks as much shorter, in whole page
+// pairs and never below one partition.
+constexpr int64_t kRunSkewPermille = 31;
 struct RunChoice {
     int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
     bool wide;
+    int64_t skew;         // LaunchParams::run_skew
 };
+// Run blocks of a split sequence whose attended range starts in its first partition and spans
+// `span` tokens (the kernels' run_blocks).
+int64_t run_blocks(int64_t span, int64_t run_tokens, int64_t skew, int waves) {
+    if (skew == 0) {
+        const int64_t runs = (span + run_tokens - 1) / run_tokens;
+        return (runs + waves - 1) / waves;
+    }
+    const int64_t two = 2 * waves * run_tokens;
+    const int64_t q = span / two, rem = span - q * two;
+    return 2 * q + (rem == 0 ? 0 : rem <= waves * (run_tokens + skew) ? 1 : 2);
+}
 RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     const int ps = pl.part_size;
-    if (!pl.P || ps % (2 * kvd::kPageTokens) != 0) return {ps, false};
+    if (!pl.P || ps % (2 * kvd::kPageTokens) != 0) return {ps, false, 0};
     const int64_t pair_tokens = 2 * kvd::kPageTokens;
     int64_t tokens;
     bool wide = false;
@@ -130,7 +151,16 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     }
     const int64_t span = (int64_t)pl.P * ps;
     if (tokens > span) tokens = span;
-    return {tokens, wide};
+    int64_t skew = 0;
+    const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
+    if (d->partitions_per_wave == 0 && !ragged && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3) &&
+        queries(d) == 1 && units_per_head(d, fmt) == 1 &&
+        span >= 2 * kvd::waves_per_group(fmt) * tokens) {
+        const int64_t pairs = tokens / pair_tokens;
+        const int64_t sp = (pairs * kRunSkewPermille + 500) / 1000;
+        if (sp > 0 && (pairs - sp) * pair_tokens >= ps) skew = sp * pair_tokens;
+    }
+    return {tokens, wide, skew};
 }
 
 // Partition mode, partition size and partitions per sequence kept in the workspace (0 = no
@@ -265,13 +295,16 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     p.kbits = fmt == KVD_TURBO3 ? 3 : 4;
     const RunChoice rc = choose_run(d, pl, fmt);
     const int waves = kvd::waves_per_group(fmt);
-    // runs of a sequence, at most (one per partition)
-    const int64_t runs = pl.P ? ((int64_t)pl.P * pl.part_size + rc.run_tokens - 1) / rc.run_tokens
-                              : 0;
+    // run blocks of a sequence, at most (skewed runs: an even number of them)
+    int64_t blocks = pl.P ? run_blocks((int64_t)pl.P * pl.part_size, rc.run_tokens, rc.skew, waves)
+                          : 0;
+    if (rc.skew) blocks += blocks & 1;
     // token indices of every run a workgroup can name must fit in int32
-    if (pl.P && (int64_t)pl.P * pl.part_size + waves * rc.run_tokens > 0x7FFFFFFFLL)
+    if (pl.P && (int64_t)pl.P * pl.part_size + (rc.skew ? 2 : 1) * waves * (rc.run_tokens + rc.skew) >
+                    0x7FFFFFFFLL)
         return KVD_ERR_SHAPE;
     p.run_tokens = (int32_t)rc.run_tokens;
+    p.run_skew = (int32_t)rc.skew;
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
 
@@ -279,7 +312,7 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
     hipError_t e = hipSuccess;
     if (phases & kPhase1) {
         // `waves` waves per workgroup, one run per wave
-        const int px = pl.P ? (int)((runs + waves - 1) / waves) : 1;
+        const int64_t px = pl.P ? blocks : 1;
         const int64_t wgs = (int64_t)px * d->num_kv_heads * p.qg * d->num_seqs;
         if (wgs > 0x7FFFFFFF) return KVD_ERR_SHAPE;
         const dim3 grid((unsigned)wgs);

@@ -76,6 +76,8 @@ struct LaunchParams {
     int32_t P;                // partitions per sequence in the workspace / grid
     int32_t kbits;            // turbo K index width (4 or 3)
     int32_t run_tokens;       // tokens of one wave's run (split sequences), >= part_size
+    int32_t run_skew;         // 0, or tokens added to the runs of even run blocks and taken
+                              // from those of odd ones (a multiple of 32; see run_blocks)
     float softmax_scale;
     float softcap;
 };

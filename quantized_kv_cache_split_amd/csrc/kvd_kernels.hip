@@ -261,14 +261,41 @@ __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
 
 // Runs of a split sequence.  A run is p.run_tokens consecutive tokens (a whole number of
 // partitions, or of page pairs covering at least one partition) counted from the first token
-// of the first partition the attended range touches (plo * part_size); run i covers
-// [base + i * run_tokens, base + (i + 1) * run_tokens) intersected with [lo, L), one wave walks
-// it, and its merged triple goes to workspace slot plo + i.  Returns the number of runs.
-__device__ __forceinline__ int split_runs(const LaunchParams& p, const SeqInfo& si, int& plo,
-                                          int& base) {
-    plo = si.lo / p.part_size;
-    base = plo * p.part_size;
-    return (si.L - base + p.run_tokens - 1) / p.run_tokens;
+// of the first partition the attended range touches (base = plo * part_size); a workgroup of
+// kw waves walks a block of kw consecutive runs, one per wave, and its merged triple goes to
+// workspace slot plo + (block index).  With p.run_skew = s > 0 the runs of even blocks are
+// T + s tokens long and those of odd blocks T - s (T = p.run_tokens): block x starts at
+// base + (x / 2) * 2 kw T + (x % 2) * kw (T + s).  Even blocks run on the even XCDs (see the
+// grid order), which read the random pages of a BF16 / FP8 cache faster.
+struct RunBlocks {
+    int plo, base, n;   // first partition, its first token, blocks of the sequence
+};
+__device__ __forceinline__ RunBlocks run_blocks(const LaunchParams& p, const SeqInfo& si, int kw) {
+    RunBlocks r;
+    r.plo = si.lo / p.part_size;
+    r.base = r.plo * p.part_size;
+    const int span = si.L - r.base;
+    if (p.run_skew == 0) {
+        const int runs = (span + p.run_tokens - 1) / p.run_tokens;
+        r.n = (runs + kw - 1) / kw;
+    } else {
+        const int64_t two = 2LL * kw * p.run_tokens;   // tokens of an even and an odd block
+        const int64_t q = span / two, rem = span - q * two;
+        r.n = (int)(2 * q) + (rem == 0 ? 0 : rem <= (int64_t)kw * (p.run_tokens + p.run_skew) ? 1 : 2);
+    }
+    return r;
+}
+// First token and run length of block x.
+__device__ __forceinline__ void block_runs(const LaunchParams& p, int base, int x, int kw,
+                                           int64_t& start, int& len) {
+    if (p.run_skew == 0) {
+        start = base + (int64_t)x * kw * p.run_tokens;
+        len = p.run_tokens;
+        return;
+    }
+    const int tf = p.run_tokens + p.run_skew;
+    start = base + (int64_t)(x >> 1) * 2 * kw * p.run_tokens + (int64_t)(x & 1) * kw * tf;
+    len = (x & 1) ? p.run_tokens - p.run_skew : tf;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -496,14 +523,15 @@ __device__ __forceinline__ LaneMap lane_map(int lane) {
 // ------------------------------------------------------------------------------------------
 // phase 1: partitioned attention
 // ------------------------------------------------------------------------------------------
-// Grid ceil(runs / W) * Hkv * units * B (1-D), W waves per workgroup.  For a split sequence
-// wave w of workgroup x owns run W x + w (split_runs: p.run_tokens consecutive tokens from the
-// first attended partition's start, at least one partition) and streams through it without
-// draining its load pipeline (the online softmax merges as it goes); the workgroup merges its
-// W runs' triples through LDS into one, at slot plo + x, and the reduce merges the
-// workgroups'.  For an unsplit sequence (workgroup 0 only) the waves share the attended range
-// (consecutive parts of its page pairs) and merge through LDS into the final rows.  Page pairs start at even page indices, so when the
-// partition size is a multiple of 32 tokens (required for R > 1) no pair straddles two
+// Grid (run blocks) * Hkv * units * B (1-D), W waves per workgroup.  For a split sequence
+// wave w of the workgroup of run block x owns the block's run w (run_blocks / block_runs:
+// whole page pairs from the first attended partition's start, at least one partition) and
+// streams through it without draining its load pipeline (the online softmax merges as it
+// goes); the workgroup merges its W runs' triples through LDS into one, at slot plo + x, and
+// the reduce merges the blocks'.  For an unsplit sequence (block 0 only) the waves share the
+// attended range (consecutive parts of its page pairs) and merge through LDS into the final
+// rows.  Page pairs start at even page indices, so when the partition size is a multiple of
+// 32 tokens (required for runs of more than one partition) no pair straddles two
 // partitions.
 template <int FMT, int D, bool CAP, int PF, bool MQ, bool WIDE, int NT>
 __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) void partition_kernel(const LaunchParams p) {
@@ -579,7 +607,20 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // the empty high blocks of short sequences, which exit at once) fill in behind them, as a
     // longest-first schedule would; in a uniform batch the order changes nothing.
     const int nxb = (int)gridDim.x / (nvh * p.B);
-    const int vh = wg % nvh, b = (wg / nvh) % p.B, xb = nxb - 1 - wg / (nvh * p.B);
+    int vh, b, xb;
+    if (p.run_skew == 0) {
+        vh = wg % nvh;
+        b = (wg / nvh) % p.B;
+        xb = nxb - 1 - wg / (nvh * p.B);
+    } else {
+        // skewed runs (p.qg == 1, nxb even): the block index's parity is the workgroup id's,
+        // so the even blocks, with the longer runs, land on the even XCDs (workgroups reach
+        // the XCDs round-robin by id); blocks go out in pairs, last pair first
+        const int rest = wg >> 1;
+        vh = rest % nvh;
+        b = (rest / nvh) % p.B;
+        xb = 2 * (nxb / 2 - 1 - rest / (nvh * p.B)) + (wg & 1);
+    }
     const int hk = vh / p.qg, unit = vh - hk * p.qg;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -629,13 +670,14 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // split waves also track their workspace slot and the next partition boundary
     int lo, hi, part_end = 0, run_slot = 0;
     if (si.split) {
-        int plo, base;
-        const int nruns = split_runs(p, si, plo, base);
-        if (xb * kW >= nruns) return;
-        const int i = xb * kW + wave;
-        run_slot = plo + xb;
-        lo = max(si.lo, base + i * p.run_tokens);
-        hi = min(si.L, base + (i + 1) * p.run_tokens);
+        const RunBlocks rb = run_blocks(p, si, kW);
+        if (xb >= rb.n) return;
+        int64_t start;
+        int len;
+        block_runs(p, rb.base, xb, kW, start, len);
+        run_slot = rb.plo + xb;
+        lo = (int)max((int64_t)si.lo, start + (int64_t)wave * len);
+        hi = (int)min((int64_t)si.L, start + (int64_t)(wave + 1) * len);
         part_end = min(hi, (lo / p.part_size + 1) * p.part_size);
     } else {
         if (xb != 0) return;
@@ -1208,7 +1250,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
 // ------------------------------------------------------------------------------------------
 // One wave per (query head, sequence x query of the chunk); lane l owns output elements
 // E*l .. E*l + E - 1 (E = D / 64).  The partition kernel wrote one triple per workgroup of kW
-// runs, at slots plo .. plo + ceil(runs / kW) - 1 (split_runs).  Triples are taken KB at a time (KB = 16 when a row has
+// runs, at slots plo .. plo + blocks - 1 (run_blocks).  Triples are taken KB at a time (KB = 16 when a row has
 // at most 32 of them, else 64): lane i < KB takes the (m, l) of triple base + i and every lane
 // loads its slice of all KB outputs, so a block costs one memory round trip.  The block's
 // weights are computed lane-parallel and broadcast with v_readlane; blocks after the first
@@ -1223,8 +1265,8 @@ __global__ __launch_bounds__(64) void reduce_kernel(const LaunchParams p) {
     const SeqInfo si = seq_info<true>(p, b);
     if (si.bad || si.L == 0 || !si.split) return;
     constexpr int kW = waves_per_group(FMT);      // runs per workgroup, merged into one triple
-    int p0, base0;
-    const int n = (split_runs(p, si, p0, base0) + kW - 1) / kW;   // triples of the sequence
+    const RunBlocks rb = run_blocks(p, si, kW);
+    const int p0 = rb.plo, n = rb.n;              // first slot, triples of the sequence
     const size_t row = (size_t)bi * p.Hq + hq;    // out / workspace row (b, query, head)
     const float* ms = p.ws_m + row * p.P + p0;
     const float* ls = p.ws_l + row * p.P + p0;

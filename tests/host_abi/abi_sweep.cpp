@@ -23,6 +23,7 @@ namespace {
 int failures = 0;
 char where[512];
 long accepted[7];   // sweep calls that reached a launch, by stub::Kind
+long skewed;        // checked partition launches with skewed runs
 
 #define CHECK(cond)                                                                            \
     do {                                                                                       \
@@ -200,8 +201,28 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
         CHECK(p.part_mode == kvd::kPartNever);
     }
     if (r.calls[stub::kPartitions]) {
-        const int64_t runs = p.P > 0 ? ((int64_t)p.P * p.part_size + p.run_tokens - 1) / p.run_tokens : 0;
-        const int64_t px = p.P > 0 ? (runs + waves - 1) / waves : 1;
+        // run blocks per sequence: W runs of T tokens each, or with a skew s > 0 alternately
+        // W runs of T + s and W of T - s, an even number of blocks
+        int64_t px = 1;
+        if (p.P > 0) {
+            const int64_t span = (int64_t)p.P * p.part_size, T = p.run_tokens, sk = p.run_skew;
+            if (sk == 0) {
+                px = ((span + T - 1) / T + waves - 1) / waves;
+            } else {
+                CHECK(sk > 0 && sk % 32 == 0 && T - sk >= p.part_size && T % 32 == 0);
+                CHECK(nq == 1 && units == 1 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3));
+                CHECK(d.partitions_per_wave == 0 &&
+                      !(d.mean_context_len > 0 && d.mean_context_len < d.max_context_len));
+                const int64_t two = 2 * waves * T, q = span / two, rem = span - q * two;
+                px = 2 * q + (rem == 0 ? 0 : rem <= waves * (T + sk) ? 1 : 2);
+                px += px & 1;
+                CHECK(px / 2 * two >= span);
+                ++skewed;
+            }
+            CHECK(span + (sk ? 2 : 1) * waves * (T + sk) <= 0x7FFFFFFFLL);
+        } else {
+            CHECK(p.run_skew == 0);
+        }
         CHECK((int64_t)r.grid.x == px * d.num_kv_heads * units * d.num_seqs);
         CHECK(r.grid.x >= 1 && r.grid.x <= 0x7FFFFFFFu && r.grid.y == 1 && r.grid.z == 1);
         CHECK(!r.wide || (fmt == KVD_BF16 && d.head_dim == 128 && nq == 1 && nt == 1));
@@ -442,8 +463,8 @@ int main(int argc, char** argv) {
         return 1;
     }
     printf("abi_sweep: %ld sweep cases, all checks passed; launches reached: partitions %ld, "
-           "reduce %ld, gather %ld, operands %ld, append %ld, probe %ld\n", iters,
+           "reduce %ld, gather %ld, operands %ld, append %ld, probe %ld; skewed runs %ld\n", iters,
            accepted[stub::kPartitions], accepted[stub::kReduce], accepted[stub::kGather],
-           accepted[stub::kOperands], accepted[stub::kAppend], accepted[stub::kProbe]);
+           accepted[stub::kOperands], accepted[stub::kAppend], accepted[stub::kProbe], skewed);
     return 0;
 }

@@ -24,14 +24,14 @@ def _need_gpu():
         pytest.skip("no GPU")
 
 
-def _bench_like_run(inp):
+def _bench_like_run(inp, mean_hint=True):
     """The two calls bench.py times, with its dims (automatic partitioning and runs)."""
     import torch
     import quantized_kv_cache_split_amd as kvd
     from kvgen.torch_io import dims_kwargs, to_torch
 
     t = to_torch(inp, "cuda:0")
-    dims = kvd.Dims(**dims_kwargs(inp, inp.spec.partition_size, 0))
+    dims = kvd.Dims(**dims_kwargs(inp, inp.spec.partition_size, 0, mean_hint=mean_hint))
     out = torch.full(tuple(inp.q.shape), float("nan"), dtype=torch.float32, device="cuda:0")
     nws = kvd.workspace_bytes(dims)
     ws = torch.empty(max(nws, 256), dtype=torch.uint8, device="cuda:0") if nws else None
@@ -91,6 +91,26 @@ def test_full_size_ragged_window_cap():
              int(np.argmin(L)), int(np.argsort(L)[len(L) // 2])}
     pairs = [(b, hk) for b in sorted(picks) for hk in (0, inp.spec.num_kv_heads - 1)]
     _check(inp, gpu, pairs, "c3")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
+def test_skewed_runs_ragged_without_hint(fmt):
+    """The FP8 / BF16 32K batch shape (16 sequences, 64 query / 8 KV heads) without a mean-length
+    hint takes the uniform-batch run choice, whose runs alternate between longer (even run
+    blocks) and shorter (odd) ones; here the sequences have unequal lengths and windows, so
+    blocks end inside a sequence, exactly at its end, one token past it, and start from a
+    window's first partition.  FP8 on MI355X: runs of 2048 +- 64 tokens, blocks of 8448 and
+    7936 tokens, ends at 8448, 16384, 24832 and 32768.  Every sequence's first and last KV head
+    is checked against the oracle."""
+    lengths = [32768, 8448, 8449, 16385, 24833, 1000, 30000, 20000, 32767, 24832, 16384, 9000,
+               5000, 31000, 12000, 32768]
+    windows = [0, 0, 0, 0, 0, 0, 5000, 12000, 0, 0, 0, 0, 0, 4096, 0, 1]
+    inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt), lengths=lengths, windows=windows,
+                            poison_before_window=True)
+    gpu = _bench_like_run(inp, mean_hint=False)
+    assert np.isfinite(gpu).all()
+    pairs = [(b, hk) for b in range(len(lengths)) for hk in (0, inp.spec.num_kv_heads - 1)]
+    _check(inp, gpu, pairs, f"{fmt} skewed runs")
 
 
 @pytest.mark.parametrize("fmt,L", [("fp8", 1 << 20), ("turbo4", 1 << 18), ("bf16", 3 * (1 << 17) + 5)])
