@@ -98,9 +98,11 @@ int device_cus() {
 // us, odd ones after 179-180 us, whichever KV heads they read; BF16 16 x 32K: 312-324 against
 // 346-353 us).  When the automatic choice covers the chip in one round with a single query
 // tile per KV head, runs of even run blocks (which the grid order puts on the even XCDs) are
-// made kRunSkewPermille / 1000 longer and those of odd blocks as much shorter, in whole page
-// pairs and never below one partition.
-constexpr int64_t kRunSkewPermille = 31;
+// made run_skew_permille / 1000 longer and those of odd blocks as much shorter, in whole page
+// pairs and never below one partition.  Measured optimum: 31-45 per mille in the two-workgroup
+// layout (FP8 16 x 32K call 193.6 -> 190.3 us at 31, 193.5 at 100), 70 in the wide one (BF16
+// 16 x 32K 368 -> 357.4 us; 360.9 at 31, 360.0 at 100).
+constexpr int64_t run_skew_permille(bool wide) { return wide ? 70 : 31; }
 struct RunChoice {
     int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
     bool wide;
@@ -157,7 +159,7 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         queries(d) == 1 && units_per_head(d, fmt) == 1 &&
         span >= 2 * kvd::waves_per_group(fmt) * tokens) {
         const int64_t pairs = tokens / pair_tokens;
-        const int64_t sp = (pairs * kRunSkewPermille + 500) / 1000;
+        const int64_t sp = (pairs * run_skew_permille(wide) + 500) / 1000;
         if (sp > 0 && (pairs - sp) * pair_tokens >= ps) skew = sp * pair_tokens;
     }
     return {tokens, wide, skew};
