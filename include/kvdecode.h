@@ -145,7 +145,9 @@ typedef struct kvd_dims {
                                     tiles counts twice; single-query BF16 at head_dim 128
                                     with at most 16 query heads per KV head uses a layout with
                                     one workgroup per CU and runs of up to 8 partitions when
-                                    that covers the device in one round);
+                                    that covers the device in one round; BF16 / FP8 runs
+                                    alternate slightly longer and shorter between workgroups
+                                    that run on the faster and the slower XCDs);
                                     > 0: runs of that many partitions.  Capped at the
                                     partitions of max_context_len; runs are one partition when
                                     the partition size is not a multiple of 32.  >= 0. */
@@ -231,7 +233,10 @@ int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const voi
  * the Turbo formats).  For a split sequence with attended range [lo, L), let p0 be the first
  * partition the range touches (P tokens per partition); run k covers tokens
  * [p0*P + k*T, p0*P + (k+1)*T) intersected with [lo, L), and workgroup x walks runs
- * W*x .. W*x + W - 1.  Their keys j together give one triple at workspace slot
+ * W*x .. W*x + W - 1.  (The automatic choice may instead alternate run lengths T + s in even
+ * workgroups and T - s in odd ones, s a multiple of 32 and T - s at least a partition, so
+ * workgroup x starts at p0*P + (x/2)*2*W*T + (x%2)*W*(T + s); BF16 / FP8, one query tile per
+ * KV head, no ragged-length hint.)  Their keys j together give one triple at workspace slot
  * (b, i, h, p0 + x):
  * m = max_j z_j * log2(e)  (base-2 units),  l = sum_j exp(z_j - max z),
  * o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the rotated domain for the Turbo
