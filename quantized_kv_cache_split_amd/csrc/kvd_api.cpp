@@ -75,8 +75,8 @@ int device_cus() {
 
 // Tokens each wave of the partition kernel walks (its run), and the kernel's layout.  A wave
 // pays a fixed start-up (query staging, the block-table -> page-load latency chain, filling its
-// load pipeline), leaves a tail when it ends and writes one (m, l, o) triple per run, so runs
-// should be long; the chip should also be covered in one round.  The automatic choice splits
+// load pipeline) and leaves a tail when it ends, so runs should be long; the chip should also
+// be covered in one round.  The automatic choice splits
 // the page pairs of a batch whose sequences were all max_context_len long evenly over the
 // device's resident wave slots (runs of whole page pairs, at least one partition long).  With
 // a mean_context_len hint below max_context_len (a ragged batch) it splits the batch's mean

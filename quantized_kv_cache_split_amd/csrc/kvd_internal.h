@@ -26,8 +26,8 @@ constexpr bool wide_layout_built(int fmt, int d, bool mq) { return fmt == 0 && d
 // e.g. MQA), so the tiles share every page load and dequantisation.
 constexpr bool tile_pairs_built(int fmt, bool mq, bool wide) { return (fmt == 0 || fmt == 1) && !mq && !wide; }
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
-// the codebook formats (sharing conflict-free codebook tables: 130 KB for Turbo4 / Turbo3, one
-// workgroup per CU; 64 KB for Turbo8).  Measured on Turbo4 / Turbo3: twelve waves per workgroup
+// the codebook formats (sharing conflict-free codebook tables: 132 KB for Turbo4 / Turbo3, 141 KB
+// of LDS with the query rows, one workgroup per CU; 64 KB for Turbo8).  Measured on Turbo4 / Turbo3: twelve waves per workgroup
 // (three per SIMD, one page pair in flight) ran 1-4% slower than eight with two pairs in flight.
 constexpr int waves_per_group(int fmt) { return fmt >= 2 ? 8 : 4; }
 // Waves per SIMD the partition kernel is compiled for (its register budget: 512 / this).
@@ -37,7 +37,7 @@ constexpr int waves_per_simd(bool wide) { return wide ? 1 : 2; }
 constexpr int waves_per_cu(bool wide) { return wide ? 4 : 8; }
 // Rows of the per-wave LDS merge area of the BF16 / FP8 partition kernel (the unsplit merge
 // uses the first kMaxGroup).  Its size is what holds the kernel at two workgroups per CU
-// (67.6 KB each at D = 128) or one in the wide layout (137 KB).
+// (68.9 KB each at D = 128) or one in the wide layout (137 KB).
 constexpr int stage_rows(int d, bool wide) { return (wide ? 8192 : 4096) / d; }
 
 enum PartMode : int32_t { kPartAuto = 0, kPartFixed = 1, kPartNever = 2 };

@@ -6,12 +6,13 @@
 // reduce"; 512-token partitions; fp32 per-partition max, sum and output) and the attention.rs
 // README (Split-K decode for every cache format from 1024 tokens on, one shared float reduce):
 //
-//   partition_kernel<FMT, D, CAP, PF, MQ, WIDE>  a 1-D grid of workgroups (4 waves for BF16 /
-//       FP8, two per CU, or one per CU in the WIDE layout of single-query BF16; 8 for the
-//       codebook formats) over (partition slot, sequence, KV head x query tile).
-//       For a split sequence each wave walks a run of consecutive partitions of one (sequence,
-//       KV head, query tile) and writes one (m, l, o) triple for the run; an unsplit
-//       sequence's pages are shared by the workgroup's waves, which merge through LDS.  A wave
+//   partition_kernel<FMT, D, CAP, PF, MQ, WIDE, NT>  a 1-D grid of workgroups (4 waves for
+//       BF16 / FP8, two per CU, or one per CU in the WIDE layout of single-query BF16; 8 for
+//       the codebook formats) over (run block, sequence, KV head x unit of NT query tiles).
+//       For a split sequence each wave walks a run of consecutive page pairs of one (sequence,
+//       KV head, unit), and the workgroup merges its waves' runs into one (m, l, o) triple;
+//       an unsplit sequence's pages are shared by the workgroup's waves, which merge through
+//       LDS into the final rows.  A wave
 //       walks pairs of 16-token pages, software-pipelined: PF pairs' loads are in flight while
 //       it computes, and the block-table entries ahead of them come in with scalar loads.  Per
 //       pair it
@@ -35,9 +36,13 @@
 //       exactly the B-operand layout of P^T for the PV product once the pair's two pages are
 //       interleaved as below, so no data moves between the two products.
 //   reduce_kernel<FMT, D>    one wave per (query head, sequence x query of the chunk): LSE
-//       merge of the partition triples, then (codebook V) the inverse rotation diag(s) H / sqrt(D).
-//   gather_kernel            test export: dequantised values through the block table with the
-//       same page addressing, index unpacking and FP8 decode as the attention kernel.
+//       merge of the run blocks' triples, then (codebook V) the inverse rotation
+//       diag(s) H / sqrt(D).
+//   gather_kernel            test export: dequantised values through the block table, one
+//       thread per element with its own page addressing and index unpacking (the FP8 decode
+//       and the 3-bit field extraction are the attention kernel's).
+//   operand_kernel           test export: the attention kernel's own page loads, lane map,
+//       FP8 decode and pair-table reads, writing every lane's MFMA operands and norms.
 //
 // MFMA 16x16x32 operand layout used throughout (lane = 0..63, n = lane % 16, j = lane / 16):
 //   A operand: row n, 8 consecutive k-slots of group j;  B operand: column n, same k-slots;
