@@ -154,7 +154,7 @@ typedef struct kvd_dims {
     int32_t queries_per_seq;     /* n_q: queries per sequence, a chunk at the last n_q positions
                                     (above); 0 or 1: single-query decode.  The n_q * Hq / Hkv
                                     query rows of a KV head share one pass over its pages per
-                                    16 rows.  Requires n_q <= max_context_len and
+                                    16 rows (32 for BF16 / FP8).  Requires n_q <= max_context_len and
                                     num_seqs * n_q <= 65535. */
     int32_t mean_context_len;    /* launch hint, results do not depend on it: the batch's mean
                                     attended span in tokens (min(L, window + n_q - 1) for

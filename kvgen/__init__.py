@@ -107,6 +107,9 @@ SPECS: dict[str, Spec] = {
     # per KV head fill one MFMA tile, so the cache is read once for all of them.
     "mq-fp8": Spec("fp8-e4m3-L32768-gqa8-q2", 16, 64, 8, 128, "fp8", context=32768,
                    queries_per_seq=2),
+    # a longer chunk: 8 queries x 8 heads = 64 rows, four 16-row tiles per KV head
+    "mq8-fp8": Spec("fp8-e4m3-L32768-gqa8-q8", 16, 64, 8, 128, "fp8", context=32768,
+                    queries_per_seq=8),
     "mq-t4": Spec("turbo4-L32768-q4", 8, 32, 8, 128, "turbo4", context=32768, queries_per_seq=4),
     "mq-t3": Spec("turbo3-L32768-q4", 8, 32, 8, 128, "turbo3", context=32768, queries_per_seq=4),
     # Multi-query attention (one KV head for all 64 query heads) at 32K: four 16-row query

@@ -21,10 +21,13 @@ constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave 
 // cover the chip in one round (a large ragged batch balances better with short runs).
 constexpr int kMaxRunWide = 8;
 constexpr bool wide_layout_built(int fmt, int d, bool mq) { return fmt == 0 && d == 128 && !mq; }
-// Query tiles per wave: single-query BF16 / FP8 in the two-workgroup layout also have a build
-// in which one wave computes two 16-row query tiles of a KV head (query groups above 16 rows,
-// e.g. MQA), so the tiles share every page load and dequantisation.
-constexpr bool tile_pairs_built(int fmt, bool mq, bool wide) { return (fmt == 0 || fmt == 1) && !mq && !wide; }
+// Query tiles per wave: BF16 / FP8 in the two-workgroup layout also have a build in which one
+// wave computes two 16-row query tiles of a KV head (more than 16 rows per KV head: query
+// groups above 16, e.g. MQA, or a chunk of queries times the group), so the tiles share every
+// page load and dequantisation.
+constexpr bool tile_pairs_built(int fmt, bool /*mq: both builds*/, bool wide) {
+    return (fmt == 0 || fmt == 1) && !wide;
+}
 // Waves per workgroup of the partition kernel: 4 for BF16 / FP8 (two workgroups per CU), 8 for
 // the codebook formats (sharing conflict-free codebook tables: 132 KB for Turbo4 / Turbo3, 141 KB
 // of LDS with the query rows, one workgroup per CU; 64 KB for Turbo8).  Measured on Turbo4 / Turbo3: twelve waves per workgroup

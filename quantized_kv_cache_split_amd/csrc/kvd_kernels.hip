@@ -703,17 +703,21 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     // ---- query operand (B of the QK product): lane (n, j), step s -------------------------
     const int qn = min(n, g - 1);          // clamp the address; rows n >= g are zeroed
     const bool qlive = n < g;
-    // tile u of the unit: rows 16u + n (NT > 1 only for single-query BF16 / FP8)
+    // tile u of the unit: rows 16u + n (NT > 1 only for BF16 / FP8)
     bool tlive[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) tlive[u] = kMaxGroup * u + n < g;
-    // the lane's query: index in the chunk, position, and the keys [row_lo, row_hi) it sees;
-    // the keys every row of the tile sees: [tile_lo, tile_hi) (the unmasked fast path).  One
-    // query per sequence: every row sees the sequence's whole range.
-    const int q_i = MQ ? (rbase + qn) / p.g : 0;
-    const int q_pos = MQ ? si.L - p.nq + q_i : si.L - 1;
-    const int row_hi = MQ ? q_pos + 1 : si.L;
-    const int row_lo = MQ ? (si.W > 0 ? max(0, row_hi - si.W) : 0) : si.lo;
+    // the lane's query in tile u: index in the chunk, position, and the keys
+    // [row_lo, row_hi) it sees; the keys every row of the unit sees: [tile_lo, tile_hi) (the
+    // unmasked fast path).  One query per sequence: every row sees the sequence's whole range.
+    int q_i[NT], q_pos[NT], row_lo[NT], row_hi[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        q_i[u] = MQ ? (rbase + min(kMaxGroup * u + n, g - 1)) / p.g : 0;
+        q_pos[u] = MQ ? si.L - p.nq + q_i[u] : si.L - 1;
+        row_hi[u] = MQ ? q_pos[u] + 1 : si.L;
+        row_lo[u] = MQ ? (si.W > 0 ? max(0, row_hi[u] - si.W) : 0) : si.lo;
+    }
     const int tile_hi = MQ ? si.L - p.nq + rbase / p.g + 1 : si.L;
     const int tile_lo = MQ ? (si.W > 0 ? max(0, si.L - p.nq + (rbase + g - 1) / p.g + 1 - si.W) : 0)
                            : si.lo;
@@ -807,7 +811,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
     float slope_l2[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u)
-        slope_l2[u] = alibi ? p.alibi[hk * p.g + (rbase + min(kMaxGroup * u + n, g - 1) - q_i * p.g)] * kLog2e
+        slope_l2[u] = alibi ? p.alibi[hk * p.g + (rbase + min(kMaxGroup * u + n, g - 1) - q_i[u] * p.g)] * kLog2e
                             : 0.0f;
 
     // ---- state -------------------------------------------------------------------------
@@ -921,7 +925,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
             const int tok0 = (pgA + ln.v_sel) * kPageTokens + ln.v_pos0;
 #pragma unroll
             for (int u = 0; u < NT; ++u) {
-                const float base = slope_l2[u] * (float)(tok0 - q_pos);
+                const float base = slope_l2[u] * (float)(tok0 - q_pos[u]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[u][e] += base + slope_l2[u] * (float)e;
             }
@@ -946,7 +950,7 @@ __global__ __launch_bounds__(64 * waves_per_group(FMT), waves_per_simd(WIDE)) vo
                 vmask |= (ok ? 1u : 0u) << e;
 #pragma unroll
                 for (int u = 0; u < NT; ++u)
-                    z[u][e] = (ok && (!MQ || (t >= row_lo && t < row_hi))) ? z[u][e] : -INFINITY;
+                    z[u][e] = (ok && (!MQ || (t >= row_lo[u] && t < row_hi[u]))) ? z[u][e] : -INFINITY;
             }
             if constexpr (kVcb) {
                 // table levels are always finite, so zero norms (possibly NaN in unused slots)
@@ -1480,9 +1484,19 @@ template <int FMT, int D>
 hipError_t launch_partitions_t(const LaunchParams& p, bool wide, dim3 grid, hipStream_t s) {
     constexpr int PF = prefetch_depth<FMT, false>();
     const dim3 block(64 * waves_per_group(FMT));
-    if (p.nq > 1)
+    if (p.nq > 1) {
+        if constexpr (tile_pairs_built(FMT, true, false)) {
+            // a chunk of queries with more than 16 rows per KV head: two query tiles per wave
+            // (FP8 C4 shape with 8 queries per sequence, 64 rows per KV head: 367 us per call
+            // with one tile per wave, 271 us with two at one pair in flight, 257 us at two)
+            constexpr int PFQ = FMT == KVD_BF16 ? 1 : 2;
+            if (p.nt == 2)
+                return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PFQ, true, false, 2>, grid, block, s, p)
+                                        : launch_kernel(partition_kernel<FMT, D, false, PFQ, true, false, 2>, grid, block, s, p);
+        }
         return p.softcap > 0.0f ? launch_kernel(partition_kernel<FMT, D, true, PF, true, false, 1>, grid, block, s, p)
                                 : launch_kernel(partition_kernel<FMT, D, false, PF, true, false, 1>, grid, block, s, p);
+    }
     if constexpr (wide_layout_built(FMT, D, false)) {
         constexpr int PFW = prefetch_depth<FMT, true>();
         if (wide)

@@ -161,8 +161,8 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     const int64_t nq = d.queries_per_seq > 1 ? d.queries_per_seq : 1;
     const int64_t g = d.num_q_heads / d.num_kv_heads;
     const int64_t qt = (nq * g + 15) / 16;
-    // single-query BF16 / FP8 with several tiles: two tiles per work unit
-    const int64_t nt = (qt >= 2 && nq == 1 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3)) ? 2 : 1;
+    // BF16 / FP8 with several tiles per KV head: two tiles per work unit
+    const int64_t nt = (qt >= 2 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3)) ? 2 : 1;
     const int64_t units = (qt + nt - 1) / nt;
     if (d.num_seqs == 0) {
         CHECK(r.calls[stub::kPartitions] == 0 && r.calls[stub::kReduce] == 0);

@@ -67,12 +67,14 @@ def test_multi_query_window_alibi_cap(fmt, ps):
     assert_close(gpu, _oracle(inp, sl), f"{fmt} mq window alibi ps={ps}")
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8", "turbo4", "turbo8"])
-def test_multi_query_runs_agree(fmt):
-    """Partitions per wave change the launch and the grouping of the sums (one triple per run
-    and query row), not the result."""
+@pytest.mark.parametrize("fmt,hq", [("bf16", 8), ("fp8", 8), ("turbo4", 8), ("turbo8", 8),
+                                    ("bf16", 16), ("fp8", 16)])
+def test_multi_query_runs_agree(fmt, hq):
+    """Partitions per wave change the launch and the grouping of the sums (one triple per
+    workgroup and query row), not the result.  With 16 query heads on 2 KV heads the 4 x 8
+    rows of a KV head are two tiles, which BF16 / FP8 compute in one wave."""
     lengths, windows = [5000, 1100, 2600, 40], [1100, 0, 333, 0]
-    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=4, num_q_heads=8, num_kv_heads=2,
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, num_seqs=4, num_q_heads=hq, num_kv_heads=2,
                                        softcap=0.0, queries_per_seq=4),
                             lengths=lengths, windows=windows, poison_before_window=True)
     ref = _oracle(inp)
