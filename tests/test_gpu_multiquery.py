@@ -67,6 +67,23 @@ def test_multi_query_window_alibi_cap(fmt, ps):
     assert_close(gpu, _oracle(inp, sl), f"{fmt} mq window alibi ps={ps}")
 
 
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_multi_query_tile_pairs(fmt, D, cap):
+    """Chunks with more than 16 rows per KV head run two query tiles per wave for BF16 / FP8
+    (3 queries x 8 heads = 24 rows here): both head dims, with and without a softcap, ragged
+    lengths, windows on half the sequences (each query its own window), split and unsplit
+    rows, with and without ALiBi."""
+    inp = kvgen.make_inputs(kvgen.spec("c3", fmt=fmt, head_dim=D, num_seqs=4, num_q_heads=16,
+                                       num_kv_heads=2, ctx_range=(8, 3000), window=900,
+                                       queries_per_seq=3, softcap=cap),
+                            poison_before_window=True)
+    for sl in (None, _slopes(16)):
+        gpu = GpuBatch(inp, alibi=sl).run()
+        assert_close(gpu, _oracle(inp, sl), f"{fmt} D={D} cap={cap} mq tile pairs alibi={sl is not None}")
+
+
 @pytest.mark.parametrize("fmt,hq", [("bf16", 8), ("fp8", 8), ("turbo4", 8), ("turbo8", 8),
                                     ("bf16", 16), ("fp8", 16)])
 def test_multi_query_runs_agree(fmt, hq):
