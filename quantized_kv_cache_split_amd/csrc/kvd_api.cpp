@@ -156,7 +156,7 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     int64_t skew = 0;
     const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
     if (d->partitions_per_wave == 0 && !ragged && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3) &&
-        queries(d) == 1 && units_per_head(d, fmt) == 1 &&
+        units_per_head(d, fmt) == 1 &&
         span >= 2 * kvd::waves_per_group(fmt) * tokens) {
         const int64_t pairs = tokens / pair_tokens;
         const int64_t sp = (pairs * run_skew_permille(wide) + 500) / 1000;

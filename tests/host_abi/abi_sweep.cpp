@@ -210,7 +210,7 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
                 px = ((span + T - 1) / T + waves - 1) / waves;
             } else {
                 CHECK(sk > 0 && sk % 32 == 0 && T - sk >= p.part_size && T % 32 == 0);
-                CHECK(nq == 1 && units == 1 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3));
+                CHECK(units == 1 && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3));
                 CHECK(d.partitions_per_wave == 0 &&
                       !(d.mean_context_len > 0 && d.mean_context_len < d.max_context_len));
                 const int64_t two = 2 * waves * T, q = span / two, rem = span - q * two;

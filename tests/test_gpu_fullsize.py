@@ -93,24 +93,25 @@ def test_full_size_ragged_window_cap():
     _check(inp, gpu, pairs, "c3")
 
 
-@pytest.mark.parametrize("fmt", ["fp8", "bf16"])
-def test_skewed_runs_ragged_without_hint(fmt):
+@pytest.mark.parametrize("fmt,nq", [("fp8", 1), ("bf16", 1), ("fp8", 2), ("bf16", 2)])
+def test_skewed_runs_ragged_without_hint(fmt, nq):
     """The FP8 / BF16 32K batch shape (16 sequences, 64 query / 8 KV heads) without a mean-length
     hint takes the uniform-batch run choice, whose runs alternate between longer (even run
     blocks) and shorter (odd) ones; here the sequences have unequal lengths and windows, so
     blocks end inside a sequence, exactly at its end, one token past it, and start from a
     window's first partition.  FP8 on MI355X: runs of 2048 +- 64 tokens, blocks of 8448 and
-    7936 tokens, ends at 8448, 16384, 24832 and 32768.  Every sequence's first and last KV head
-    is checked against the oracle."""
+    7936 tokens, ends at 8448, 16384, 24832 and 32768.  With 2 queries per sequence (16 rows per
+    KV head, one tile) the chunk path takes the same runs.  Every sequence's first and last KV
+    head is checked against the oracle."""
     lengths = [32768, 8448, 8449, 16385, 24833, 1000, 30000, 20000, 32767, 24832, 16384, 9000,
                5000, 31000, 12000, 32768]
     windows = [0, 0, 0, 0, 0, 0, 5000, 12000, 0, 0, 0, 0, 0, 4096, 0, 1]
-    inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt), lengths=lengths, windows=windows,
-                            poison_before_window=True)
+    inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt, queries_per_seq=nq), lengths=lengths,
+                            windows=windows, poison_before_window=True)
     gpu = _bench_like_run(inp, mean_hint=False)
     assert np.isfinite(gpu).all()
     pairs = [(b, hk) for b in range(len(lengths)) for hk in (0, inp.spec.num_kv_heads - 1)]
-    _check(inp, gpu, pairs, f"{fmt} skewed runs")
+    _check(inp, gpu, pairs, f"{fmt} nq={nq} skewed runs")
 
 
 @pytest.mark.parametrize("fmt,L", [("fp8", 1 << 20), ("turbo4", 1 << 18), ("bf16", 3 * (1 << 17) + 5)])
