@@ -30,7 +30,7 @@ def _batch(fmt, seed):
                                         softcap=0.0, seed=seed))
 
 
-def _replays_match(gb, capture, eager):
+def _replays_match(gb, capture, eager, before=None):
     import torch
     other = GpuBatch(_batch(gb.inp.spec.fmt, 99))
     g = torch.cuda.CUDAGraph()
@@ -38,6 +38,8 @@ def _replays_match(gb, capture, eager):
         capture()
     for i in range(3):
         gb.out.fill_(float("nan"))
+        if before is not None:
+            before()
         other.run()                      # eager work between the replays
         torch.cuda.synchronize()
         g.replay()
@@ -66,3 +68,45 @@ def test_graph_replays_noalloc_entry_point(fmt):
     torch.cuda.synchronize()
     assert (gb.out.double().cpu().numpy().view(np.uint64) == eager.view(np.uint64)).all()
     _replays_match(gb, lambda: gb.kvd.decode_attn_paged_noalloc(*args), eager)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "bf16", "turbo4", "turbo8"])
+def test_graph_replays_append_then_decode(fmt):
+    """One serving step -- quantize each sequence's newest token into the paged cache, then
+    decode over the cache -- captured as one graph.  Before every replay the caches are put
+    back as they were before the eager step, so the replay's own append must write the token
+    the decode then attends to; each replay matches the eager step bit for bit."""
+    import torch
+    from kvgen.torch_io import dims_kwargs
+    inp = _batch(fmt, 13)
+    gb = GpuBatch(inp)
+    s = inp.spec
+    rng = np.random.default_rng(17)
+    kn = torch.from_numpy(rng.standard_normal((s.num_seqs, 1, s.num_kv_heads, s.head_dim))
+                          .astype(np.float32)).to("cuda:0")
+    vn = torch.from_numpy(rng.standard_normal((s.num_seqs, 1, s.num_kv_heads, s.head_dim))
+                          .astype(np.float32)).to("cuda:0")
+    assert (inp.context_lens >= 1).all()
+    pos = torch.from_numpy((inp.context_lens - 1).astype(np.int32)).to("cuda:0")
+    adims = gb.kvd.Dims(**dims_kwargs(inp, 0))
+    t = gb.t
+    args = gb._args()
+
+    def step():
+        gb.kvd.append_kv(adims, fmt, kn, vn, t["block_table"], pos, 1, t["k_cache"],
+                         t["v_cache"], t["scales"], t["codebook"], t["sign_pattern"])
+        gb.kvd.decode_attn_paged(*args)
+
+    k0, v0 = t["k_cache"].clone(), t["v_cache"].clone()
+    before_step = gb.run()
+    step()
+    torch.cuda.synchronize()
+    eager = gb.out.double().cpu().numpy()
+    assert np.isfinite(eager).all()
+    assert not np.array_equal(eager, before_step)      # the appended token changes the output
+
+    def restore():
+        t["k_cache"].copy_(k0)
+        t["v_cache"].copy_(v0)
+
+    _replays_match(gb, step, eager, before=restore)
