@@ -147,7 +147,9 @@ typedef struct kvd_dims {
                                     one workgroup per CU and runs of up to 8 partitions when
                                     that covers the device in one round; BF16 / FP8 runs
                                     alternate slightly longer and shorter between workgroups
-                                    that run on the faster and the slower XCDs);
+                                    that run on the faster and the slower XCDs, and with two
+                                    workgroups per CU the half dispatched first gets slightly
+                                    longer runs);
                                     > 0: runs of that many partitions.  Capped at the
                                     partitions of max_context_len; runs are one partition when
                                     the partition size is not a multiple of 32.  >= 0. */
@@ -236,8 +238,13 @@ int kvd_decode_attn_paged_noalloc(const kvd_dims* dims, const void* q, const voi
  * W*x .. W*x + W - 1.  (The automatic choice may instead alternate run lengths T + s in even
  * workgroups and T - s in odd ones, s a multiple of 32 and T - s at least a partition, so
  * workgroup x starts at p0*P + (x/2)*2*W*T + (x%2)*W*(T + s); BF16 / FP8, one query tile per
- * KV head, no ragged-length hint.)  Their keys j together give one triple at workspace slot
- * (b, i, h, p0 + x):
+ * KV head, no ragged-length hint.  Where that grid is also exactly two workgroups per CU and
+ * holds an even number Y of workgroup pairs (2y, 2y + 1) per sequence, both runs of the pairs
+ * y >= Y/2, which go out first, are a tokens longer and those of pairs y < Y/2 a shorter, a a
+ * multiple of 32 and T - s - a at least a partition: pair y starts at p0*P + 2*W*y*(T - a)
+ * for y <= Y/2 and at p0*P + W*Y*(T - a) + 2*W*(y - Y/2)*(T + a) beyond, and its odd
+ * workgroup starts W*(T + s + a) (y >= Y/2) or W*(T + s - a) tokens after its even one.)
+ * Their keys j together give one triple at workspace slot (b, i, h, p0 + x):
  * m = max_j z_j * log2(e)  (base-2 units),  l = sum_j exp(z_j - max z),
  * o[d] = sum_j exp(z_j - max z) v_j[d] / l  -- with o in the rotated domain for the Turbo
  * formats; the keys j are those of the workgroup's runs that query i sees, and a query that

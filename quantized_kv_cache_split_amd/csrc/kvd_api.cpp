@@ -102,11 +102,22 @@ int device_cus() {
 // pairs and never below one partition.  Measured optimum: 31-45 per mille in the two-workgroup
 // layout (FP8 16 x 32K call 193.6 -> 190.3 us at 31, 193.5 at 100), 70 in the wide one (BF16
 // 16 x 32K 368 -> 357.4 us; 360.9 at 31, 360.0 at 100).
+//
+// Early skew.  When such a grid holds exactly two workgroups per CU (two-workgroup layout),
+// the workgroups each CU receives second (the grid's second half) end about 4 us after those
+// it receives first.  Then both runs of the block pairs the grid dispatches first are made
+// early_skew_permille / 1000 longer and those of the other pairs as much shorter (an even
+// number of pairs, so a full sequence still ends with its last pair).  Measured on FP8 16 x 32K
+// (single query, and 2 queries per sequence): 31 per mille (64 tokens on 2048-token runs),
+// calls 190.1 -> 189.1 us and 192.6 -> 191.4 us; 16: 189.6 and 192.1; 47: 191.6 and 194.2;
+// 62: 193.4 and 196.2.
 constexpr int64_t run_skew_permille(bool wide) { return wide ? 70 : 31; }
+constexpr int64_t early_skew_permille = 31;
 struct RunChoice {
     int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
     bool wide;
     int64_t skew;         // LaunchParams::run_skew
+    int64_t early;        // LaunchParams::early_skew
 };
 // Run blocks of a split sequence whose attended range starts in its first partition and spans
 // `span` tokens (the kernels' run_blocks).
@@ -121,7 +132,7 @@ int64_t run_blocks(int64_t span, int64_t run_tokens, int64_t skew, int waves) {
 }
 RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     const int ps = pl.part_size;
-    if (!pl.P || ps % (2 * kvd::kPageTokens) != 0) return {ps, false, 0};
+    if (!pl.P || ps % (2 * kvd::kPageTokens) != 0) return {ps, false, 0, 0};
     const int64_t pair_tokens = 2 * kvd::kPageTokens;
     int64_t tokens;
     bool wide = false;
@@ -162,7 +173,18 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         const int64_t sp = (pairs * run_skew_permille(wide) + 500) / 1000;
         if (sp > 0 && (pairs - sp) * pair_tokens >= ps) skew = sp * pair_tokens;
     }
-    return {tokens, wide, skew};
+    int64_t early = 0;
+    if (skew && !wide) {
+        int64_t blocks = run_blocks(span, tokens, skew, kvd::waves_per_group(fmt));
+        blocks += blocks & 1;
+        const int64_t wgs = blocks * d->num_kv_heads * units_per_head(d, fmt) * d->num_seqs;
+        const int64_t pairs = tokens / pair_tokens;
+        const int64_t ep = (pairs * early_skew_permille + 500) / 1000;
+        if (blocks % 4 == 0 && wgs == 2LL * device_cus() && ep > 0 &&
+            tokens - skew - ep * pair_tokens >= ps)
+            early = ep * pair_tokens;
+    }
+    return {tokens, wide, skew, early};
 }
 
 // Partition mode, partition size and partitions per sequence kept in the workspace (0 = no
@@ -307,6 +329,8 @@ int run(int phases, const kvd_dims* d, const void* q, const void* k_cache, const
         return KVD_ERR_SHAPE;
     p.run_tokens = (int32_t)rc.run_tokens;
     p.run_skew = (int32_t)rc.skew;
+    p.early_skew = (int32_t)rc.early;
+    p.run_pairs = (int32_t)(blocks / 2);
     p.softmax_scale = softmax_scale;
     p.softcap = softcap;
 

@@ -81,6 +81,9 @@ struct LaunchParams {
     int32_t run_tokens;       // tokens of one wave's run (split sequences), >= part_size
     int32_t run_skew;         // 0, or tokens added to the runs of even run blocks and taken
                               // from those of odd ones (a multiple of 32; see run_blocks)
+    int32_t early_skew;       // 0, or tokens added to every run of the block pairs the grid
+                              // dispatches first and taken from the others (run_skew > 0 only)
+    int32_t run_pairs;        // run block pairs per sequence in the grid (early_skew > 0)
     float softmax_scale;
     float softcap;
 };

@@ -271,10 +271,25 @@ __device__ __forceinline__ SeqInfo seq_info(const LaunchParams& p, int b) {
 // workspace slot plo + (block index).  With p.run_skew = s > 0 the runs of even blocks are
 // T + s tokens long and those of odd blocks T - s (T = p.run_tokens): block x starts at
 // base + (x / 2) * 2 kw T + (x % 2) * kw (T + s).  Even blocks run on the even XCDs (see the
-// grid order), which read the random pages of a BF16 / FP8 cache faster.
+// grid order), which read the random pages of a BF16 / FP8 cache faster.  With also
+// p.early_skew = e > 0 (the grid holds exactly two workgroups per CU and an even number
+// 2H = p.run_pairs of block pairs) both runs of pairs H .. 2H - 1, which the grid dispatches
+// first, are e tokens longer, and those of pairs 0 .. H - 1 e tokens shorter: the pairs are
+// 2 kw (T + e) and 2 kw (T - e) tokens long.
 struct RunBlocks {
     int plo, base, n;   // first partition, its first token, blocks of the sequence
 };
+// Length of the runs of the even block of pair q, and the pair's first token past base.
+__device__ __forceinline__ int even_run(const LaunchParams& p, int q) {
+    const int e = q >= (p.run_pairs >> 1) ? p.early_skew : -p.early_skew;
+    return p.run_tokens + p.run_skew + e;
+}
+__device__ __forceinline__ int64_t pair_start(const LaunchParams& p, int kw, int q) {
+    const int64_t H = p.run_pairs >> 1;
+    const int64_t late = 2LL * kw * (p.run_tokens - p.early_skew);
+    const int64_t early = 2LL * kw * (p.run_tokens + p.early_skew);
+    return q <= H ? q * late : H * late + (q - H) * early;
+}
 __device__ __forceinline__ RunBlocks run_blocks(const LaunchParams& p, const SeqInfo& si, int kw) {
     RunBlocks r;
     r.plo = si.lo / p.part_size;
@@ -283,10 +298,20 @@ __device__ __forceinline__ RunBlocks run_blocks(const LaunchParams& p, const Seq
     if (p.run_skew == 0) {
         const int runs = (span + p.run_tokens - 1) / p.run_tokens;
         r.n = (runs + kw - 1) / kw;
-    } else {
+    } else if (p.early_skew == 0) {
         const int64_t two = 2LL * kw * p.run_tokens;   // tokens of an even and an odd block
         const int64_t q = span / two, rem = span - q * two;
         r.n = (int)(2 * q) + (rem == 0 ? 0 : rem <= (int64_t)kw * (p.run_tokens + p.run_skew) ? 1 : 2);
+    } else if (span <= 0) {
+        r.n = 0;
+    } else {
+        // the pair holding the range's last token, then whether its odd block is reached
+        const int64_t H = p.run_pairs >> 1;
+        const int64_t late = 2LL * kw * (p.run_tokens - p.early_skew);
+        const int64_t early = 2LL * kw * (p.run_tokens + p.early_skew);
+        const int q = (int)(span <= H * late ? (span + late - 1) / late - 1
+                                             : H + (span - H * late + early - 1) / early - 1);
+        r.n = 2 * q + (span - pair_start(p, kw, q) <= (int64_t)kw * even_run(p, q) ? 1 : 2);
     }
     return r;
 }
@@ -298,9 +323,15 @@ __device__ __forceinline__ void block_runs(const LaunchParams& p, int base, int 
         len = p.run_tokens;
         return;
     }
-    const int tf = p.run_tokens + p.run_skew;
-    start = base + (int64_t)(x >> 1) * 2 * kw * p.run_tokens + (int64_t)(x & 1) * kw * tf;
-    len = (x & 1) ? p.run_tokens - p.run_skew : tf;
+    if (p.early_skew == 0) {
+        const int tf = p.run_tokens + p.run_skew;
+        start = base + (int64_t)(x >> 1) * 2 * kw * p.run_tokens + (int64_t)(x & 1) * kw * tf;
+        len = (x & 1) ? p.run_tokens - p.run_skew : tf;
+        return;
+    }
+    const int q = x >> 1, ev = even_run(p, q);
+    start = base + pair_start(p, kw, q) + (int64_t)(x & 1) * kw * ev;
+    len = (x & 1) ? ev - 2 * p.run_skew : ev;
 }
 
 // ------------------------------------------------------------------------------------------

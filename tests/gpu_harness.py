@@ -134,31 +134,48 @@ def runs_per_triple(fmt):
     return 8 if fmt in ("turbo4", "turbo3", "turbo8") else 4
 
 
+def _merge_group(g):
+    """LSE merge of triples [(lo, hi, m, l, o), ...] (natural-log m): M = max m_i,
+    l = sum l_i e^(m_i - M), o = sum l_i e^(m_i - M) o_i / l; rows with no key keep m = -inf,
+    l = 0, o = 0."""
+    ms = np.array([x[2] for x in g], dtype=np.float64)
+    ls = np.array([x[3] for x in g], dtype=np.float64)
+    os_ = np.array([x[4] for x in g], dtype=np.float64)
+    M = ms.max(axis=0)
+    safe = np.where(np.isfinite(M), M, 0.0)
+    w = np.where(ls > 0, ls * np.exp(np.where(ls > 0, ms, 0.0) - safe), 0.0)
+    L = w.sum(axis=0)
+    O = np.einsum("pr,prd->rd", w, os_) / np.where(L > 0, L, 1.0)[:, None]
+    return M, L, O
+
+
 def merge_runs(parts, part_size, run):
     """Group an oracle's per-partition triples [(lo, hi, m, l, o), ...] (in order, natural-log
     m) into groups of ``run`` consecutive partitions the partition kernel merges into one
     workspace triple (a workgroup's runs: partitions per run x runs_per_triple; groups start
-    at the first partition of the range), merging each group with the LSE rule:
-    M = max m_i, l = sum l_i e^(m_i - M), o = sum l_i e^(m_i - M) o_i / l.  Rows with no key in a
-    group keep m = -inf, l = 0, o = 0.  Returns [(slot, lo, hi, m, l, o)]: group k of a range
-    whose first partition is p0 sits in workspace slot p0 + k."""
+    at the first partition of the range), merging each group with the LSE rule (_merge_group).
+    Returns [(slot, lo, hi, m, l, o)]: group k of a range whose first partition is p0 sits in
+    workspace slot p0 + k."""
     if not parts:
         return []
     p0 = parts[0][0] // part_size
     groups = {}
     for lo, hi, m, l, o in parts:
         groups.setdefault((lo // part_size - p0) // run, []).append((lo, hi, m, l, o))
-    out = []
-    for k in sorted(groups):
-        g = groups[k]
-        ms = np.array([x[2] for x in g], dtype=np.float64)
-        ls = np.array([x[3] for x in g], dtype=np.float64)
-        os_ = np.array([x[4] for x in g], dtype=np.float64)
-        M = ms.max(axis=0)
-        safe = np.where(np.isfinite(M), M, 0.0)
-        w = np.where(ls > 0, ls * np.exp(np.where(ls > 0, ms, 0.0) - safe), 0.0)
-        L = w.sum(axis=0)
-        O = np.einsum("pr,prd->rd", w, os_) / np.where(L > 0, L, 1.0)[:, None]
-        out.append((p0 + k, g[0][0], g[-1][1], M, L, O))
-    return out
+    return [(p0 + k, groups[k][0][0], groups[k][-1][1], *_merge_group(groups[k]))
+            for k in sorted(groups)]
+
+
+def merge_blocks(parts, starts):
+    """Group an oracle's triples over short token ranges (in order, each inside one block) by
+    the workgroup block holding them -- block x covers tokens [starts[x], starts[x + 1]) -- and
+    merge each group (_merge_group).  Returns [(x, lo, hi, m, l, o)] for the blocks that hold
+    any of the ranges."""
+    groups = {}
+    for lo, hi, m, l, o in parts:
+        x = int(np.searchsorted(starts, lo, side="right")) - 1
+        assert 0 <= x < len(starts) - 1 and hi <= starts[x + 1], (lo, hi, starts)
+        groups.setdefault(x, []).append((lo, hi, m, l, o))
+    return [(x, groups[x][0][0], groups[x][-1][1], *_merge_group(groups[x]))
+            for x in sorted(groups)]
 

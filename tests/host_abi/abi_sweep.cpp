@@ -24,6 +24,7 @@ int failures = 0;
 char where[512];
 long accepted[7];   // sweep calls that reached a launch, by stub::Kind
 long skewed;        // checked partition launches with skewed runs
+long early;         // ... of which also with early-skewed block pairs
 
 #define CHECK(cond)                                                                            \
     do {                                                                                       \
@@ -202,7 +203,9 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     }
     if (r.calls[stub::kPartitions]) {
         // run blocks per sequence: W runs of T tokens each, or with a skew s > 0 alternately
-        // W runs of T + s and W of T - s, an even number of blocks
+        // W runs of T + s and W of T - s, an even number of blocks; with an early skew e > 0
+        // as well, the grid is two workgroups per CU and holds an even number of block pairs,
+        // half of them e tokens longer per run and half e shorter
         int64_t px = 1;
         if (p.P > 0) {
             const int64_t span = (int64_t)p.P * p.part_size, T = p.run_tokens, sk = p.run_skew;
@@ -217,11 +220,21 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
                 px = 2 * q + (rem == 0 ? 0 : rem <= waves * (T + sk) ? 1 : 2);
                 px += px & 1;
                 CHECK(px / 2 * two >= span);
+                CHECK(p.run_pairs == px / 2);
                 ++skewed;
+                if (p.early_skew != 0) {
+                    const int64_t e = p.early_skew;
+                    const int cus = stub::device_cus > 0 ? stub::device_cus : 256;
+                    CHECK(e > 0 && e % 32 == 0 && T - sk - e >= p.part_size && !r.wide);
+                    CHECK(px % 4 == 0 &&
+                          px * d.num_kv_heads * units * d.num_seqs == 2LL * cus);
+                    ++early;
+                }
             }
+            if (sk == 0) CHECK(p.early_skew == 0);
             CHECK(span + (sk ? 2 : 1) * waves * (T + sk) <= 0x7FFFFFFFLL);
         } else {
-            CHECK(p.run_skew == 0);
+            CHECK(p.run_skew == 0 && p.early_skew == 0);
         }
         CHECK((int64_t)r.grid.x == px * d.num_kv_heads * units * d.num_seqs);
         CHECK(r.grid.x >= 1 && r.grid.x <= 0x7FFFFFFFu && r.grid.y == 1 && r.grid.z == 1);
@@ -463,8 +476,10 @@ int main(int argc, char** argv) {
         return 1;
     }
     printf("abi_sweep: %ld sweep cases, all checks passed; launches reached: partitions %ld, "
-           "reduce %ld, gather %ld, operands %ld, append %ld, probe %ld; skewed runs %ld\n", iters,
+           "reduce %ld, gather %ld, operands %ld, append %ld, probe %ld; skewed runs %ld, "
+           "early-skewed %ld\n", iters,
            accepted[stub::kPartitions], accepted[stub::kReduce], accepted[stub::kGather],
-           accepted[stub::kOperands], accepted[stub::kAppend], accepted[stub::kProbe], skewed);
+           accepted[stub::kOperands], accepted[stub::kAppend], accepted[stub::kProbe], skewed,
+           early);
     return 0;
 }

@@ -12,7 +12,7 @@ import pytest
 import kvgen
 import oracle
 from conftest import oracle_args
-from gpu_harness import assert_close
+from gpu_harness import GpuBatch, assert_close, merge_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -99,12 +99,15 @@ def test_skewed_runs_ragged_without_hint(fmt, nq):
     hint takes the uniform-batch run choice, whose runs alternate between longer (even run
     blocks) and shorter (odd) ones; here the sequences have unequal lengths and windows, so
     blocks end inside a sequence, exactly at its end, one token past it, and start from a
-    window's first partition.  FP8 on MI355X: runs of 2048 +- 64 tokens, blocks of 8448 and
-    7936 tokens, ends at 8448, 16384, 24832 and 32768.  With 2 queries per sequence (16 rows per
-    KV head, one tile) the chunk path takes the same runs.  Every sequence's first and last KV
-    head is checked against the oracle."""
-    lengths = [32768, 8448, 8449, 16385, 24833, 1000, 30000, 20000, 32767, 24832, 16384, 9000,
-               5000, 31000, 12000, 32768]
+    window's first partition.  FP8 on MI355X: runs of 2048 +- 64 tokens, and since the grid is
+    two workgroups per CU, the block pair dispatched first has runs 64 tokens longer and the
+    other pair 64 shorter: blocks of 8192, 7680, 8704 and 8192 tokens, ends at 8192, 15872,
+    24576 and 32768 (lengths 8448, 16384 and 24832 were ends of the layout without the early
+    pair's extra tokens).  With 2 queries per sequence (16 rows per KV head, one tile) the chunk
+    path takes the same runs, for BF16 too.  Every sequence's first and last KV head is checked
+    against the oracle."""
+    lengths = [32768, 8192, 8193, 15873, 24577, 1000, 30000, 20000, 32767, 24576, 15872, 8448,
+               16384, 31000, 24832, 32768]
     windows = [0, 0, 0, 0, 0, 0, 5000, 12000, 0, 0, 0, 0, 0, 4096, 0, 1]
     inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt, queries_per_seq=nq), lengths=lengths,
                             windows=windows, poison_before_window=True)
@@ -112,6 +115,55 @@ def test_skewed_runs_ragged_without_hint(fmt, nq):
     assert np.isfinite(gpu).all()
     pairs = [(b, hk) for b in range(len(lengths)) for hk in (0, inp.spec.num_kv_heads - 1)]
     _check(inp, gpu, pairs, f"{fmt} nq={nq} skewed runs")
+
+
+def _header_block_starts(T, s, a, W, Y):
+    """Token starts of the workgroup blocks of a full sequence in the skewed automatic run
+    layout kvd_decode_partitions documents -- W runs of T + s tokens in even workgroups and of
+    T - s in odd ones; with an early skew a > 0, Y (even) workgroup pairs of which pairs
+    y >= Y/2 take runs a longer and the others a shorter -- followed by the last block's end."""
+    st = []
+    for y in range(Y):
+        p = 2 * W * y * (T - a) if y <= Y // 2 else W * Y * (T - a) + 2 * W * (y - Y // 2) * (T + a)
+        st += [p, p + W * (T + s + (a if y >= Y // 2 else -a))]
+    return st + [st[-1] + W * (T - s + (a if Y - 1 >= Y // 2 else -a))]
+
+
+@pytest.mark.parametrize("fmt,layout", [("fp8", (2048, 64, 64, 2)), ("bf16", (4096, 288, 0, 1))])
+def test_skewed_partials_follow_header_layout(fmt, layout):
+    """Phase 1 alone on the 16 x 32K batch shape (64 query / 8 KV heads) with the automatic run
+    choice: each workgroup's triple in the workspace holds exactly the keys of the token range
+    the documented skewed layout gives that workgroup.  On MI355X (256 CUs) FP8 takes runs of
+    2048 +- 64 tokens in a grid of two workgroups per CU, the pair dispatched first 64 tokens
+    longer per run (blocks start at 0, 8192, 15872, 24576); BF16 takes the one-workgroup-per-CU
+    layout with runs of 4096 +- 288 (blocks at 0 and 17536, inside a partition).  The oracle's
+    triples over 32-token ranges are merged per block; the slots past the last block stay
+    unwritten."""
+    import torch
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("the run choice asserted here is the one for 256 CUs")
+    T, s, a, Y = layout
+    starts = _header_block_starts(T, s, a, 4, Y)
+    assert starts[-1] == 32768
+    inp = kvgen.make_inputs(kvgen.spec("c4", fmt=fmt))
+    assert (inp.window == 0).all() and (inp.context_lens == 32768).all()
+    gb = GpuBatch(inp)
+    gb.run_phase1()
+    m, l, o = gb.partials()
+    g = inp.spec.group
+    for b, hk in _pairs(inp, 2, 2, 5):
+        rows = slice(hk * g, hk * g + g)
+        blocks = merge_blocks(oracle.partition_partials(*oracle_args(inp), 32, b, hk), starts)
+        assert [x for x, *_ in blocks] == list(range(len(starts) - 1))
+        for x, lo, hi, pm, pl, po in blocks:
+            m_nat = m[b, rows, x].astype(np.float64) * np.log(2.0)
+            assert (np.abs(m_nat - pm) <= 1e-4).all(), (x, np.abs(m_nat - pm))
+            lse = m_nat + np.log(l[b, rows, x].astype(np.float64))
+            assert (np.abs(lse - (pm + np.log(pl))) <= 3e-4).all(), (x, lse, pm + np.log(pl))
+            assert_close(o[b, rows, x].astype(np.float64), po, f"{fmt} block {x} b{b} h{hk}")
+        assert np.isnan(m[b, rows, len(starts) - 1:]).all()
+    del gb
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("fmt,L", [("fp8", 1 << 20), ("turbo4", 1 << 18), ("bf16", 3 * (1 << 17) + 5)])
