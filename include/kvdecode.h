@@ -175,7 +175,9 @@ typedef struct kvd_dims {
 size_t kvd_workspace_bytes(const kvd_dims* dims);
 
 /* Decode attention, both phases (partition kernel, then the reduce kernel when any sequence
- * is split).
+ * is split).  When every split sequence is one workgroup's walk (a single run block, below),
+ * nothing is merged across workgroups: the partition kernel writes the final rows as for an
+ * unsplit sequence and the reduce is not launched.
  *   q            bf16 [B][n_q][Hq][D]
  *   k_cache      K pool in `fmt`'s layout (above);  v_cache  V pool
  *   block_table  int32 [B][max_blocks_per_seq]; entries for the pages holding the attended
@@ -194,7 +196,8 @@ size_t kvd_workspace_bytes(const kvd_dims* dims);
  *   alibi_slopes fp32 [Hq] per-query-head ALiBi slopes, or NULL for none
  *   out          fp32 [B][n_q][Hq][D]; must not alias any input
  *   workspace    >= kvd_workspace_bytes(dims) bytes, 256-byte aligned; contents on entry do
- *                not matter; on return it holds the partials of split sequences
+ *                not matter; on return it holds the partials of split sequences (untouched
+ *                when each sequence is a single run block)
  *   stream       hipStream_t
  * All pointers 16-byte aligned. */
 int kvd_decode_attn_paged(const kvd_dims* dims, const void* q, const void* k_cache,

@@ -25,6 +25,7 @@ char where[512];
 long accepted[7];   // sweep calls that reached a launch, by stub::Kind
 long skewed;        // checked partition launches with skewed runs
 long early;         // ... of which also with early-skewed block pairs
+long single;        // checked decode launches whose sequences are one run block each
 
 #define CHECK(cond)                                                                            \
     do {                                                                                       \
@@ -170,7 +171,8 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
         return;
     }
     CHECK(r.calls[stub::kPartitions] == (phase1 ? 1 : 0));
-    CHECK(r.calls[stub::kReduce] == (phase2 && p.P > 0 ? 1 : 0));
+    CHECK(r.calls[stub::kReduce] <= (phase2 && p.P > 0 ? 1 : 0));
+    if (!phase1) CHECK(r.calls[stub::kReduce] == (phase2 && p.P > 0 ? 1 : 0));
     if (!r.calls[stub::kPartitions] && !r.calls[stub::kReduce]) return;
     CHECK(r.fmt == fmt);
     CHECK(p.B == d.num_seqs && p.Hq == d.num_q_heads && p.Hkv == d.num_kv_heads);
@@ -237,6 +239,11 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
             CHECK(p.run_skew == 0 && p.early_skew == 0);
         }
         CHECK((int64_t)r.grid.x == px * d.num_kv_heads * units * d.num_seqs);
+        // both phases with one run block per sequence: the unsplit path, no reduce
+        const bool one_block = phase2 && p.P > 0 && px == 1;
+        CHECK(r.calls[stub::kReduce] == (phase2 && p.P > 0 && !one_block ? 1 : 0));
+        if (p.P > 0) CHECK((p.part_mode == kvd::kPartNever) == one_block);
+        if (one_block) ++single;
         CHECK(r.grid.x >= 1 && r.grid.x <= 0x7FFFFFFFu && r.grid.y == 1 && r.grid.z == 1);
         CHECK(!r.wide || (fmt == KVD_BF16 && d.head_dim == 128 && nq == 1 && nt == 1));
     }
@@ -477,9 +484,9 @@ int main(int argc, char** argv) {
     }
     printf("abi_sweep: %ld sweep cases, all checks passed; launches reached: partitions %ld, "
            "reduce %ld, gather %ld, operands %ld, append %ld, probe %ld; skewed runs %ld, "
-           "early-skewed %ld\n", iters,
+           "early-skewed %ld, one-block %ld\n", iters,
            accepted[stub::kPartitions], accepted[stub::kReduce], accepted[stub::kGather],
            accepted[stub::kOperands], accepted[stub::kAppend], accepted[stub::kProbe], skewed,
-           early);
+           early, single);
     return 0;
 }

@@ -53,5 +53,6 @@ def test_c_abi_under_asan_ubsan(sweep_exe, seed):
     assert res.returncode == 0, (res.stdout + res.stderr)[-4000:]
     assert "all checks passed" in res.stdout
     assert int(res.stdout.split("skewed runs ")[1].split(",")[0]) > 0, res.stdout
-    assert int(res.stdout.split("early-skewed ")[1].split()[0]) > 0, res.stdout
+    assert int(res.stdout.split("early-skewed ")[1].split(",")[0]) > 0, res.stdout
+    assert int(res.stdout.split("one-block ")[1].split()[0]) > 0, res.stdout
     assert "runtime error" not in res.stderr and "AddressSanitizer" not in res.stderr

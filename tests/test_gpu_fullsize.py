@@ -25,7 +25,8 @@ def _need_gpu():
 
 
 def _bench_like_run(inp, mean_hint=True):
-    """The two calls bench.py times, with its dims (automatic partitioning and runs)."""
+    """The call bench.py times (kvd_decode_attn_paged), with its dims (automatic partitioning
+    and runs)."""
     import torch
     import quantized_kv_cache_split_amd as kvd
     from kvgen.torch_io import dims_kwargs, to_torch
@@ -38,8 +39,7 @@ def _bench_like_run(inp, mean_hint=True):
     args = (dims, t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["context_lens"],
             inp.spec.fmt, t["scales"], t["codebook"], t["sign_pattern"], float(inp.softmax_scale),
             t["window"], float(inp.softcap), out, ws)
-    kvd.decode_partitions(*args)
-    kvd.reduce_partitions(*args)
+    kvd.decode_attn_paged(*args)
     torch.cuda.synchronize()
     res = out.double().cpu().numpy()
     del t, out, ws

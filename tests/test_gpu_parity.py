@@ -298,6 +298,33 @@ def test_uniform_v():
     assert np.abs(gpu + 1.25).max() < 1e-5
 
 
+@pytest.mark.parametrize("fmt", kvgen.FORMATS)
+def test_one_block_call_matches_two_phases(fmt):
+    """Sequences of at most four 512-token partitions with one-partition runs are each one
+    workgroup's walk (4 waves; 8 for the Turbo formats), so kvd_decode_attn_paged takes the
+    unsplit path (the waves merge in LDS; no workspace, no reduce launch).  Its output agrees
+    with the two-phase path (partition triples, then the reduce kernel) to the format's operand
+    precision -- 1e-5 of the row for BF16 / FP8 (exact operands, P as a bf16 hi + lo pair); for
+    the codebook formats P' is rounded once to fp16 relative to each wave's reference, and the
+    paths give the waves different token ranges, so 2e-3 -- and both agree with the oracle."""
+    inp = _small(fmt, context=None, ctx_range=(1025, 2048), num_seqs=3)
+    ref = oracle.decode_attention(*oracle_args(inp))
+    gb = GpuBatch(inp, partition_size=512, partitions_per_wave=1)
+    fused = gb.run()
+    gb.out.fill_(float("nan"))
+    gb.run_phase1()
+    gb.kvd.reduce_partitions(*gb._args())
+    import torch
+    torch.cuda.synchronize()
+    two = gb.out.double().cpu().numpy()
+    assert np.isfinite(fused).all() and np.isfinite(two).all()
+    scale = np.abs(two).max(axis=-1, keepdims=True)
+    tol = 1e-5 if fmt in ("bf16", "fp8") else 2e-3
+    assert (np.abs(fused - two) <= tol * scale + 1e-7).all(), np.abs(fused - two).max()
+    assert_close(fused, ref, f"{fmt} one-block call")
+    assert_close(two, ref, f"{fmt} two-phase call")
+
+
 @pytest.mark.parametrize("run", [1, 3])
 @pytest.mark.parametrize("fmt", kvgen.FORMATS)
 def test_partials_match_oracle(fmt, run):
