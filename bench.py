@@ -1,7 +1,8 @@
 """Benchmark: paged decode attention on one MI355X, effective KV GB/s against HBM peak.
 
-One "step" is one full decode-attention call (kvd_decode_attn_paged: partition kernel + LSE
-reduce) over a synthetic batch already resident in HBM.  The default workload is the
+One "step" is one full decode-attention call (kvd_decode_attn_paged: partition kernel, then
+the LSE reduce unless every sequence is one workgroup's walk) over a synthetic batch already
+resident in HBM.  The default workload is the
 FP8-E4M3 cache at 32K context (16 sequences, 64 query / 8 KV heads, head_dim 128, 512-token
 partitions).  The K timed steps are timed with one HIP event pair each, on the stream the
 kernels run on, around the whole call.  No event sits between the two launches: a marker
@@ -52,8 +53,8 @@ def parse():
     # calls, 208-209 us from then on); the default warm-up reaches the steady state
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="c4",
-                    help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 m-bf16 m-t4 m-t3 m-t8 mq-fp8 mq8-fp8 mq-t4 mq-t3 "
-                         "mqa-fp8 mqa-bf16 mqa-t4 mqa-t8 (see kvgen.SPECS)")
+                    help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 s-t4 s-t3 m-bf16 m-t4 m-t3 m-t8 mq-fp8 "
+                         "mq8-fp8 mq-t4 mq-t3 mqa-fp8 mqa-bf16 mqa-t4 mqa-t8 (see kvgen.SPECS)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--partitions-per-wave", type=int, default=0,
                     help="launch tuning of the partition kernel (0 = the library's choice)")

@@ -103,6 +103,10 @@ SPECS: dict[str, Spec] = {
     "m-t3": Spec("turbo3-L32768", 8, 32, 8, 128, "turbo3", context=32768),
     "m-t8": Spec("turbo8-L32768", 8, 32, 8, 128, "turbo8", context=32768),
     "c5-t8": Spec("turbo8-L65536", 8, 32, 8, 128, "turbo8", context=65536),
+    # Short rotated-codebook contexts in a large batch: each sequence is one workgroup's walk,
+    # so a decode call is one partition launch with no reduce.
+    "s-t4": Spec("turbo4-L4096", 64, 32, 8, 128, "turbo4", context=4096),
+    "s-t3": Spec("turbo3-L4096", 64, 32, 8, 128, "turbo3", context=4096),
     # Chunks of queries (chunked prefill / multi-token decode) at 32K: n_q * group = 16 rows
     # per KV head fill one MFMA tile, so the cache is read once for all of them.
     "mq-fp8": Spec("fp8-e4m3-L32768-gqa8-q2", 16, 64, 8, 128, "fp8", context=32768,

@@ -164,6 +164,14 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     }
     const int64_t span = (int64_t)pl.P * ps;
     if (tokens > span) tokens = span;
+    // Runs that one workgroup covers with room to spare would leave some of its waves without
+    // pairs (Turbo 64 x 4K: 8 waves x 1024 tokens for a 4096-token context): the span is
+    // spread over the workgroup's waves instead, in whole page pairs and at least a partition.
+    const int64_t kw = kvd::waves_per_group(fmt);
+    if (d->partitions_per_wave == 0 && tokens * kw > span) {
+        const int64_t even = (span + kw * pair_tokens - 1) / (kw * pair_tokens) * pair_tokens;
+        if (even < tokens) tokens = even < ps ? ps : even;
+    }
     int64_t skew = 0;
     const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
     if (d->partitions_per_wave == 0 && !ragged && (fmt == KVD_BF16 || fmt == KVD_FP8_E4M3) &&
