@@ -107,6 +107,11 @@ SPECS: dict[str, Spec] = {
     # so a decode call is one partition launch with no reduce.
     "s-t4": Spec("turbo4-L4096", 64, 32, 8, 128, "turbo4", context=4096),
     "s-t3": Spec("turbo3-L4096", 64, 32, 8, 128, "turbo3", context=4096),
+    # Batches of 6 sequences at 32K (48 work units, which do not divide the device's workgroup
+    # slots): the run choice fills one round of workgroups with whole run blocks.
+    "b6-fp8": Spec("fp8-e4m3-L32768-b6", 6, 64, 8, 128, "fp8", context=32768),
+    "b6-bf16": Spec("bf16-L32768-b6", 6, 64, 8, 128, "bf16", context=32768),
+    "b6-t4": Spec("turbo4-L32768-b6", 6, 32, 8, 128, "turbo4", context=32768),
     # Chunks of queries (chunked prefill / multi-token decode) at 32K: n_q * group = 16 rows
     # per KV head fill one MFMA tile, so the cache is read once for all of them.
     "mq-fp8": Spec("fp8-e4m3-L32768-gqa8-q2", 16, 64, 8, 128, "fp8", context=32768,

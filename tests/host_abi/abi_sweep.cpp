@@ -265,7 +265,44 @@ kvd_dims valid_dims() {
     return d;
 }
 
+// The automatic run choice on uniform batches of 256-CU devices: the FP8 16 x 32K batch takes
+// runs of 2048 tokens, the XCD skew (64 tokens) and the early skew (64), 512 workgroups (two
+// per CU); batches of 6 sequences (48 units) fit one round of workgroups.
+void run_choice_cases() {
+    struct Case {
+        int fmt, seqs, hq, ctx;
+        int64_t run_tokens, skew, early, max_wgs;
+    };
+    const Case cases[] = {
+        {KVD_FP8_E4M3, 16, 64, 32768, 2048, 64, 64, 512},
+        {KVD_FP8_E4M3, 6, 64, 32768, 832, 32, 0, 512},
+        {KVD_TURBO4, 6, 32, 32768, 832, 0, 0, 256},
+        {KVD_TURBO4, 8, 32, 32768, 1024, 0, 0, 256},
+        {KVD_BF16, 6, 64, 32768, 1664, 0, 0, 256},
+        {KVD_TURBO4, 64, 32, 4096, 512, 0, 0, 512},
+    };
+    for (const Case& k : cases) {
+        kvd_dims* d = static_cast<kvd_dims*>(malloc(sizeof(kvd_dims)));
+        *d = valid_dims();
+        d->num_seqs = k.seqs;
+        d->num_q_heads = k.hq;
+        d->max_context_len = k.ctx;
+        d->num_pool_blocks = 1 << 20;
+        describe(*d, k.fmt, "run choice");
+        Call c = base_call(d, k.fmt);
+        c.ws_bytes = kvd_workspace_bytes(d);
+        stub::reset();
+        CHECK(call(kvd_decode_partitions, c) == KVD_OK);
+        const kvd::LaunchParams& p = stub::rec.lp;
+        CHECK(p.run_tokens == k.run_tokens && p.run_skew == k.skew && p.early_skew == k.early);
+        CHECK((int64_t)stub::rec.grid.x <= k.max_wgs);
+        check_decode_launch(*d, k.fmt, static_cast<const char*>(c.ws), c.ws_bytes, true, false);
+        free(d);
+    }
+}
+
 void fixed_cases() {
+    run_choice_cases();
     for (int s = -8; s <= 2; ++s) CHECK(kvd_status_str(s) != nullptr && kvd_status_str(s)[0]);
     snprintf(where, sizeof(where), "null dims");
     CHECK(kvd_workspace_bytes(nullptr) == 0);
