@@ -138,11 +138,14 @@ typedef struct kvd_dims {
                                     sequence; a workgroup's runs give one triple (results
                                     agree to rounding: the online softmax groups its sums by
                                     run and workgroup).
-                                    0: auto -- the page pairs of a batch of max_context_len
-                                    sequences split evenly over the device's resident
+                                    0: auto -- for a batch of max_context_len sequences,
+                                    each (sequence, KV head, unit) gets as many whole
+                                    workgroups as one round of the device's resident
+                                    wavefronts holds, its page pairs spread over their
                                     wavefronts (whole 32-token pairs, at least one partition,
                                     at most 4 partitions; a wavefront computing two query
-                                    tiles counts twice; single-query BF16 at head_dim 128
+                                    tiles counts twice; with a mean_context_len hint, the
+                                    batch's mean work over about 2.5 rounds; single-query BF16 at head_dim 128
                                     with at most 16 query heads per KV head uses a layout with
                                     one workgroup per CU and runs of up to 8 partitions when
                                     that covers the device in one round; BF16 / FP8 runs
