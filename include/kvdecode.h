@@ -142,8 +142,10 @@ typedef struct kvd_dims {
                                     each (sequence, KV head, unit) gets as many whole
                                     workgroups as one round of the device's resident
                                     wavefronts holds, its page pairs spread over their
-                                    wavefronts (whole 32-token pairs, at least one partition,
-                                    at most 4 partitions; a wavefront computing two query
+                                    wavefronts (whole 32-token pairs, a workgroup's runs at
+                                    least one partition, at most 4 partitions per run, one
+                                    workgroup per CU where two would get runs under 16
+                                    pairs; a wavefront computing two query
                                     tiles counts twice; with a mean_context_len hint, the
                                     batch's mean work over about 2.5 rounds; single-query BF16 at head_dim 128
                                     with at most 16 query heads per KV head uses a layout with

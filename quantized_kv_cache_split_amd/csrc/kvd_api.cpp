@@ -79,10 +79,11 @@ int device_cus() {
 // be covered in one round.  For a batch whose sequences were all max_context_len long the
 // automatic choice gives each sequence (and work unit) as many whole run blocks as one round
 // of workgroups holds, and spreads the sequence's page pairs over those blocks' waves (runs of
-// whole page pairs, at least one partition long).  Splitting the batch's pairs evenly over the
-// wave slots instead left a few workgroups for a second round whenever the units do not
-// divide the slots: 6 x 32K calls FP8 98.4 -> 80.6 us, Turbo4 84.5 -> 59.1, BF16 194.5 ->
-// 144.9 us with the whole-block rule; power-of-two batches get the same runs either way.  With
+// whole page pairs; a workgroup's runs cover at least one partition, its workspace slot).
+// Splitting the batch's pairs evenly over the wave slots instead left a few workgroups for a
+// second round whenever the units do not divide the slots: 6 x 32K calls FP8 98.4 -> 80.6
+// us, Turbo4 84.5 -> 59.1, BF16 194.5 -> 144.9 us with the whole-block rule; power-of-two
+// batches get the same runs either way.  With
 // a mean_context_len hint below max_context_len (a ragged batch) it splits the batch's mean
 // work over 2.5 rounds of the slots instead: sequences end at different times, and about 2.5
 // waves of work per slot let the dispatcher even them out (ragged 64 x U{1..32K} BF16 batch,
@@ -116,6 +117,12 @@ int device_cus() {
 // calls 190.1 -> 189.1 us and 192.6 -> 191.4 us; 16: 189.6 and 192.1; 47: 191.6 and 194.2;
 // 62: 193.4 and 196.2.
 constexpr int64_t run_skew_permille(bool wide) { return wide ? 70 : 31; }
+// Small uniform batches: runs shorter than a partition (a workgroup's runs still cover one)
+// fill the device where one-partition runs left most of it idle, and below this many pairs
+// per run one workgroup per CU beats two (calls at 32K, runs as chosen / one partition:
+// FP8 1 x 32K 24.2 / 30.8 us, 2 x 32K 34.6 us against 36.0 with two workgroups per CU and
+// half the run, Turbo4 1 x 32K 25.5 / 40.7 us, BF16 1 x 32K 35.3 / 37.6 us).
+constexpr int64_t kMinPairsTwoPerCu = 16;
 constexpr int64_t early_skew_permille = 31;
 struct RunChoice {
     int64_t run_tokens;   // narrowed to int32 once the caller has checked the token range
@@ -157,9 +164,19 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
                 // as many whole run blocks per sequence as one round of workgroups holds, the
                 // sequence spread over their waves
                 const int64_t kw = kvd::waves_per_group(fmt);
-                int64_t per_seq = slots / kw / units;
-                if (per_seq < 1) per_seq = 1;
-                rp = (pairs + per_seq * kw - 1) / (per_seq * kw);
+                auto whole_blocks = [&](int64_t sl) {
+                    int64_t per_seq = sl / kw / units;
+                    if (per_seq < 1) per_seq = 1;
+                    return (pairs + per_seq * kw - 1) / (per_seq * kw);
+                };
+                rp = whole_blocks(slots);
+                // two workgroups per CU pay off only with runs of at least kMinPairsTwoPerCu
+                // pairs; below that one per CU, with runs twice as long
+                if (rp < kMinPairsTwoPerCu && slots / kw == 2LL * device_cus())
+                    rp = whole_blocks(slots / 2);
+                // a block's kw runs cover at least one partition (its workspace slot)
+                const int64_t lo = (ps + kw * pair_tokens - 1) / (kw * pair_tokens);
+                return (rp < lo ? lo : rp) * pair_tokens;
             }
             return rp * pair_tokens < ps ? ps : rp * pair_tokens;
         };
@@ -180,11 +197,16 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
     if (tokens > span) tokens = span;
     // Runs that one workgroup covers with room to spare would leave some of its waves without
     // pairs (Turbo 64 x 4K: 8 waves x 1024 tokens for a 4096-token context): the span is
-    // spread over the workgroup's waves instead, in whole page pairs and at least a partition.
+    // spread over the workgroup's waves instead, in whole page pairs (at least a partition per
+    // workgroup; per run for ragged batches).
     const int64_t kw = kvd::waves_per_group(fmt);
     if (d->partitions_per_wave == 0 && tokens * kw > span) {
-        const int64_t even = (span + kw * pair_tokens - 1) / (kw * pair_tokens) * pair_tokens;
-        if (even < tokens) tokens = even < ps ? ps : even;
+        const bool rag = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;
+        const int64_t floor_tok =
+            rag ? ps : (ps + kw * pair_tokens - 1) / (kw * pair_tokens) * pair_tokens;
+        int64_t even = (span + kw * pair_tokens - 1) / (kw * pair_tokens) * pair_tokens;
+        if (even < floor_tok) even = floor_tok;
+        if (even < tokens) tokens = even;
     }
     int64_t skew = 0;
     const bool ragged = d->mean_context_len > 0 && d->mean_context_len < d->max_context_len;

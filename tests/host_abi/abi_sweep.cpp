@@ -184,7 +184,12 @@ void check_decode_launch(const kvd_dims& d, int fmt, const char* base, size_t ws
     if (p.P > 0) {
         CHECK(p.part_size > 0 && (int64_t)p.P * p.part_size >= d.max_context_len);
         CHECK((int64_t)(p.P - 1) * p.part_size < d.max_context_len);
-        CHECK(p.run_tokens >= p.part_size);
+        // a workgroup's runs cover at least one partition (its workspace slot); explicit
+        // partitions_per_wave and ragged batches: whole partitions
+        CHECK((int64_t)waves * p.run_tokens >= p.part_size && p.run_tokens > 0);
+        if (d.partitions_per_wave > 0 ||
+            (d.mean_context_len > 0 && d.mean_context_len < d.max_context_len))
+            CHECK(p.run_tokens >= p.part_size);
         CHECK(p.run_tokens <= (int64_t)p.P * p.part_size);
         CHECK(p.run_tokens == p.part_size || p.run_tokens % 32 == 0);
         CHECK((int64_t)p.P * p.part_size + (int64_t)waves * p.run_tokens <= INT32_MAX);
@@ -267,7 +272,8 @@ kvd_dims valid_dims() {
 
 // The automatic run choice on uniform batches of 256-CU devices: the FP8 16 x 32K batch takes
 // runs of 2048 tokens, the XCD skew (64 tokens) and the early skew (64), 512 workgroups (two
-// per CU); batches of 6 sequences (48 units) fit one round of workgroups.
+// per CU); batches of 6 sequences (48 units) fit one round of workgroups; batches of 1 or 2
+// sequences take runs shorter than a partition and one workgroup per CU.
 void run_choice_cases() {
     struct Case {
         int fmt, seqs, hq, ctx;
@@ -280,6 +286,11 @@ void run_choice_cases() {
         {KVD_TURBO4, 8, 32, 32768, 1024, 0, 0, 256},
         {KVD_BF16, 6, 64, 32768, 1664, 0, 0, 256},
         {KVD_TURBO4, 64, 32, 4096, 512, 0, 0, 512},
+        {KVD_FP8_E4M3, 1, 64, 32768, 256, 0, 0, 256},
+        {KVD_FP8_E4M3, 2, 64, 32768, 512, 0, 0, 256},
+        {KVD_FP8_E4M3, 4, 64, 32768, 512, 0, 0, 512},
+        {KVD_TURBO4, 1, 32, 32768, 128, 0, 0, 256},
+        {KVD_BF16, 1, 64, 32768, 256, 0, 0, 256},
     };
     for (const Case& k : cases) {
         kvd_dims* d = static_cast<kvd_dims*>(malloc(sizeof(kvd_dims)));
