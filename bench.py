@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--workload", default="c4",
                     help="c1 c2 c3 c4 c5-t4 c5-t3 c5-t8 s-t4 s-t3 b6-fp8 b6-bf16 b6-t4 b1-fp8 "
                          "b1-t4 m-bf16 m-t4 m-t3 m-t8 mq-fp8 mq8-fp8 mq-t4 mq-t3 mqa-fp8 mqa-bf16 "
-                         "mqa-t4 mqa-t8 "
+                         "mqa-t4 mqa-t8 b64-fp8 "
                          "(see kvgen.SPECS)")
     ap.add_argument("--partition-size", type=int, default=None)
     ap.add_argument("--partitions-per-wave", type=int, default=0,

@@ -115,6 +115,8 @@ SPECS: dict[str, Spec] = {
     # One sequence at 32K (8 work units): runs shorter than a partition fill the device.
     "b1-fp8": Spec("fp8-e4m3-L32768-b1", 1, 64, 8, 128, "fp8", context=32768),
     "b1-t4": Spec("turbo4-L32768-b1", 1, 32, 8, 128, "turbo4", context=32768),
+    # A large batch (64 sequences at 32K, 512 units): runs capped at 8 partitions.
+    "b64-fp8": Spec("fp8-e4m3-L32768-b64", 64, 64, 8, 128, "fp8", context=32768),
     # Chunks of queries (chunked prefill / multi-token decode) at 32K: n_q * group = 16 rows
     # per KV head fill one MFMA tile, so the cache is read once for all of them.
     "mq-fp8": Spec("fp8-e4m3-L32768-gqa8-q2", 16, 64, 8, 128, "fp8", context=32768,

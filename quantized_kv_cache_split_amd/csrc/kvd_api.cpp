@@ -90,8 +90,10 @@ int device_cus() {
 // runs of 1 / 2 / 3 / 4 partitions, i.e. 5.2 / 2.6 / 1.8 / 1.5 rounds: 500.9 / 490.8 / 499.8 /
 // 508.0 us per partition launch on MI355X).  Where
 // the wide layout is built (one workgroup per CU) it is taken if runs of at most kMaxRunWide
-// partitions cover the chip in one round; otherwise runs are capped at kMaxRun partitions
-// (ragged batches, whose real work is smaller, do better with short runs).  Runs other than
+// partitions cover the chip in one round; otherwise runs are capped at kMaxRunUniform
+// partitions, or kMaxRun for ragged batches, whose real work is smaller and which do better
+// with short runs (uniform FP8 16 x 32K with 8 queries per sequence, runs of 4 / 8 / 16
+// partitions: 256.2 / 242.6 / 250.4 us per call).  Runs other than
 // one partition need partition boundaries on even pages (partition size a multiple of 32).  A
 // wave that computes two query tiles counts as two slots' work, so its runs are twice as long
 // (FP8 / BF16 16 x 32K with 64 query heads on one KV head, runs of 1 / 2 partitions: 52.4 /
@@ -190,7 +192,8 @@ RunChoice choose_run(const kvd_dims* d, const Plan& pl, int fmt) {
         }
         if (!wide) {
             tokens = run_for(false);
-            if (tokens > (int64_t)kvd::kMaxRun * ps) tokens = (int64_t)kvd::kMaxRun * ps;
+            const int64_t cap = (int64_t)(ragged ? kvd::kMaxRun : kvd::kMaxRunUniform) * ps;
+            if (tokens > cap) tokens = cap;
         }
     }
     const int64_t span = (int64_t)pl.P * ps;

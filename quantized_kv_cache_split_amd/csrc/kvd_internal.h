@@ -12,7 +12,8 @@ constexpr int kPageTokens = 16;     // tokens per page (block_size)
 constexpr int kAutoPartition = 512; // partition size of the automatic split
 constexpr int kAutoSplitMin = 1024; // automatic split only from this many attended tokens
 constexpr int kMaxGroup = 16;       // query heads one MFMA tile (one wave) handles
-constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice
+constexpr int kMaxRun = 4;          // cap on the automatic partitions-per-wave choice (ragged)
+constexpr int kMaxRunUniform = 8;   // ... for a batch of equal lengths
 // Wide layout of the partition kernel: one 4-wave workgroup per CU (one wave per SIMD; its LDS
 // area of 137 KB keeps a second workgroup off the CU), with runs of up to kMaxRunWide
 // partitions.  Built for

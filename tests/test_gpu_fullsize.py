@@ -72,7 +72,7 @@ def _check(inp, gpu, pairs, what):
 @pytest.mark.parametrize("name", ["c4", "m-bf16", "m-t4", "m-t3", "m-t8", "c2", "c5-t4", "c5-t3",
                                   "c5-t8", "mq-fp8", "mq8-fp8", "mq-t4", "mq-t3", "mqa-fp8", "mqa-bf16",
                                   "mqa-t4", "mqa-t8", "s-t4", "s-t3", "b6-fp8", "b6-bf16", "b6-t4",
-                                  "b1-fp8", "b1-t4"])
+                                  "b1-fp8", "b1-t4", "b64-fp8"])
 def test_full_size_sampled(name):
     inp = kvgen.make_inputs(kvgen.SPECS[name])
     gpu = _bench_like_run(inp)
